@@ -1,0 +1,18 @@
+"""Float64 CPU oracle of the DFlash draft-attention layer step.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package. The product (the HIP library and its Python binding) never imports it
+and shares no code with it.
+"""
+from .ref_fp64 import (  # noqa: F401
+    OracleCache,
+    attention,
+    crop,
+    layer_step,
+    linear,
+    rms_norm,
+    rope,
+    rope_inv_freq,
+    window_keep,
+)

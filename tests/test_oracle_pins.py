@@ -1,0 +1,394 @@
+"""Pins of the float64 oracle against what the pages and mathematics fix.
+
+The pages print no numeric worked example for this layer, so every pin here is
+a closed form, an invariant, a special case that reduces to an independent
+library routine, or brute force on tiny inputs in pure Python. Each is chosen so
+that a plausible slip in the oracle (a dropped gain or eps, a wrong sign, an
+interleaved instead of half-split RoPE pairing, a prefix instead of suffix of
+positions, ``h % nkv`` instead of ``h // g``, a causal mask, ``<=`` instead of
+``<`` in the band, a transposed weight) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workload import LayerConfig, Weights
+
+RNG = np.random.default_rng(1234)
+
+
+def tiny_cfg(**kw):
+    base = dict(name="tiny", batch=1, hidden=12, n_q_heads=4, n_kv_heads=2, head_dim=6,
+                block_size=3, dtype="fp32", cached_len=2, new_ctx=3, rope_theta=10000.0,
+                rms_eps=1e-6, sliding_window=0)
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+def rand_weights(cfg, rng, gain_lo=0.5, gain_hi=1.5):
+    H, nq, nkv, d = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    return Weights(w_q=rng.standard_normal((nq * d, H)) * 0.3,
+                   w_k=rng.standard_normal((nkv * d, H)) * 0.3,
+                   w_v=rng.standard_normal((nkv * d, H)) * 0.3,
+                   w_o=rng.standard_normal((H, nq * d)) * 0.3,
+                   q_norm=rng.uniform(gain_lo, gain_hi, d),
+                   k_norm=rng.uniform(gain_lo, gain_hi, d))
+
+
+def rand_inputs(cfg, rng, lens, news):
+    B, H, nkv, d, bs = len(lens), cfg.hidden, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    offs = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    X = rng.standard_normal((B * bs, H))
+    C = rng.standard_normal((int(offs[-1]), H))
+    cache = oracle.OracleCache.from_arrays(
+        [rng.standard_normal((nkv, L, d)) for L in lens],
+        [rng.standard_normal((nkv, L, d)) for L in lens])
+    pos = np.concatenate([np.arange(L, L + n + bs) for L, n in zip(lens, news)])
+    return X, C, offs, pos, cache
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_step(cfg, w, cache, X, C, offs, pos):
+    """The whole layer step in pure-Python loops and the math module only."""
+    H, nq, nkv, d, bs = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    g, half, W = nq // nkv, d // 2, cfg.sliding_window
+    B = len(offs) - 1
+    out = [[0.0] * H for _ in range(B * bs)]
+
+    def lin(x, wm, rows):
+        return [sum(x[c] * float(wm[r][c]) for c in range(len(x))) for r in rows]
+
+    def norm(v, gain):
+        ms = sum(t * t for t in v) / len(v)
+        return [v[i] / math.sqrt(ms + cfg.rms_eps) * float(gain[i]) for i in range(len(v))]
+
+    def rot(v, p):
+        o = list(v)
+        for t in range(half):
+            a = p * cfg.rope_theta ** (-2.0 * t / d)
+            o[t] = v[t] * math.cos(a) - v[t + half] * math.sin(a)
+            o[t + half] = v[t + half] * math.cos(a) + v[t] * math.sin(a)
+        return o
+
+    new_k, new_v = [], []
+    for b in range(B):
+        n = int(offs[b + 1] - offs[b])
+        base = int(offs[b]) + b * bs
+        rows_src = [list(map(float, C[int(offs[b]) + r])) for r in range(n)] + \
+                   [list(map(float, X[b * bs + i])) for i in range(bs)]
+        Kb = [[list(map(float, cache.k[b][j, t])) for t in range(cache.k[b].shape[1])] for j in range(nkv)]
+        Vb = [[list(map(float, cache.v[b][j, t])) for t in range(cache.v[b].shape[1])] for j in range(nkv)]
+        for r, x in enumerate(rows_src):
+            p = int(pos[base + r])
+            for j in range(nkv):
+                kk = lin(x, w.w_k, range(j * d, (j + 1) * d))
+                vv = lin(x, w.w_v, range(j * d, (j + 1) * d))
+                Kb[j].append(rot(norm(kk, w.k_norm), p))
+                Vb[j].append(vv)
+        T = len(Kb[0])
+        for i in range(bs):
+            x = list(map(float, X[b * bs + i]))
+            p = int(pos[base + n + i])
+            concat = []
+            for h in range(nq):
+                q = rot(norm(lin(x, w.w_q, range(h * d, (h + 1) * d)), w.q_norm), p)
+                j = h // g
+                qi = T - bs + i
+                vis = [t for t in range(T) if not W or abs(qi - t) < W]
+                s = [sum(q[c] * Kb[j][t][c] for c in range(d)) / math.sqrt(d) for t in vis]
+                mx = max(s)
+                e = [math.exp(v - mx) for v in s]
+                z = sum(e)
+                o = [sum(e[u] / z * Vb[j][t][c] for u, t in enumerate(vis)) for c in range(d)]
+                concat += o
+            out[b * bs + i] = lin(concat, w.w_o, range(H))
+        new_k.append(Kb)
+        new_v.append(Vb)
+    return np.array(out), new_k, new_v
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_layer_step_matches_pure_python_brute_force(window):
+    cfg = tiny_cfg(batch=2, sliding_window=window)
+    rng = np.random.default_rng(7 + window)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[2, 4], news=[3, 0])
+    out, new = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    ref, bk, bv = brute_step(cfg, w, cache, X, C, offs, pos)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-11)
+    for b in range(2):
+        np.testing.assert_allclose(new.k[b], np.array(bk[b]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(new.v[b], np.array(bv[b]), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- projection
+
+def test_linear_is_x_times_w_transposed():
+    x = RNG.standard_normal((3, 5))
+    w = RNG.standard_normal((4, 5))
+    ref = [[sum(x[i, c] * w[r, c] for c in range(5)) for r in range(4)] for i in range(3)]
+    np.testing.assert_allclose(oracle.linear(x, w), ref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_unit_rms_before_gain_closed_form():
+    x = RNG.standard_normal((50, 128)) * RNG.uniform(0.001, 10, (50, 1))
+    eps = 1e-6
+    y = oracle.rms_norm(x, np.ones(128), eps)
+    ms = np.mean(x * x, axis=-1)
+    rms_y = np.sqrt(np.mean(y * y, axis=-1))
+    np.testing.assert_allclose(rms_y, np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    # large inputs: RMS exactly 1 up to eps / (2 ms)
+    assert np.all(np.abs(rms_y - 1) <= eps / (2 * ms) * 1.01 + 1e-15)
+
+
+def test_rmsnorm_gain_eps_and_zero_vector():
+    x = np.array([3.0, -4.0, 0.0, 0.0])
+    gain = np.array([2.0, 0.5, 7.0, 1.0])
+    eps = 0.25
+    denom = math.sqrt((9 + 16) / 4 + 0.25)
+    np.testing.assert_allclose(oracle.rms_norm(x, gain, eps), [6 / denom, -2 / denom, 0, 0], rtol=1e-15)
+    assert np.all(oracle.rms_norm(np.zeros(8), np.ones(8), 1e-6) == 0)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_pairs_halves_with_standard_frequencies():
+    d, theta = 8, 1e6
+    for t in range(d // 2):
+        x = np.zeros((1, d))
+        x[0, t] = 1.0
+        p = 37
+        y = oracle.rope(x, [p], theta)[0]
+        a = p * theta ** (-2.0 * t / d)
+        expect = np.zeros(d)
+        expect[t] = math.cos(a)
+        expect[t + d // 2] = math.sin(a)   # x2' = x2 cos + x1 sin
+        np.testing.assert_allclose(y, expect, atol=1e-15)
+        x = np.zeros((1, d))
+        x[0, t + d // 2] = 1.0
+        y = oracle.rope(x, [p], theta)[0]
+        expect = np.zeros(d)
+        expect[t] = -math.sin(a)           # x1' = x1 cos - x2 sin
+        expect[t + d // 2] = math.cos(a)
+        np.testing.assert_allclose(y, expect, atol=1e-15)
+
+
+def test_rope_identity_norm_and_composition():
+    d = 64
+    x = RNG.standard_normal((5, d))
+    np.testing.assert_array_equal(oracle.rope(x, [0] * 5, 1e6), x)
+    y = oracle.rope(x, [1, 100, 5000, 32800, 131071], 1e6)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    m, n = 1234, 777
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, [m] * 5, 1e6), [n] * 5, 1e6),
+                               oracle.rope(x, [m + n] * 5, 1e6), atol=1e-11)
+
+
+def test_rope_fp32_angle_would_lose_precision_at_long_context():
+    """Why the GPU path reads a cos/sin table built in float64: an fp32 angle
+    ``pos * inv_freq`` at position 32800 errs by ~7e-4 rad, far beyond the
+    fp32 parity tolerance of 1e-4, while the fp64 angle is exact to ~1e-11."""
+    inv = oracle.rope_inv_freq(128, 1e6)
+    exact = 32800 * inv
+    f32 = (np.float32(32800) * inv.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(f32 - exact)) > 5e-4
+
+
+def test_scores_invariant_under_shift_of_all_positions():
+    """RoPE relative invariance through the whole step: shifting every window
+    position by the same amount (empty cache) leaves the output unchanged."""
+    cfg = tiny_cfg(head_dim=8, hidden=16)
+    rng = np.random.default_rng(3)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[0], news=[5])
+    out0, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    out1, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos + 991)
+    np.testing.assert_allclose(out0, out1, rtol=1e-10, atol=1e-12)
+    out2, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos * 2)  # not a shift: must differ
+    assert np.max(np.abs(out2 - out0)) > 1e-3
+
+
+# ---------------------------------------------------------------- suffix rule
+
+def test_queries_take_the_trailing_positions_of_the_window():
+    """With identical q and k projections and gains, block row i's query equals
+    its own key before RoPE; rotated at the same position (the suffix rule) the
+    score with its own key is the unrotated <q, q> / sqrt(d) exactly."""
+    cfg = tiny_cfg(n_q_heads=2, n_kv_heads=2, head_dim=8, hidden=16, block_size=4)
+    rng = np.random.default_rng(11)
+    w = rand_weights(cfg, rng)
+    w.w_k = w.w_q.copy()
+    w.k_norm = w.q_norm.copy()
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[0], news=[3])
+    pos = pos * 7 + 5  # distinct positions, so a wrong alignment shows
+    _, new = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    q_unrot = oracle.rms_norm(oracle.linear(X, w.w_q).reshape(4, 2, 8), w.q_norm, cfg.rms_eps)
+    K = new.k[0]  # [2, 7, 8]; block keys are rows 3..6
+    for i in range(4):
+        for h in range(2):
+            q_rot = oracle.rope(q_unrot[i, h][None], [pos[3 + i]], cfg.rope_theta)[0]
+            np.testing.assert_allclose(q_rot @ K[h, 3 + i], q_unrot[i, h] @ q_unrot[i, h], rtol=1e-12)
+            # the prefix alignment (position i instead of 3+i) would not match
+            q_bad = oracle.rope(q_unrot[i, h][None], [pos[i]], cfg.rope_theta)[0]
+            assert abs(q_bad @ K[h, 3 + i] - q_unrot[i, h] @ q_unrot[i, h]) > 1e-6
+
+
+# ---------------------------------------------------------------- GQA
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    cfg = tiny_cfg(n_q_heads=6, n_kv_heads=2, head_dim=4, hidden=8)
+    rng = np.random.default_rng(5)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[3], news=[2])
+    out, new = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    g, d = 3, 4
+    rep = lambda m: np.repeat(m.reshape(2, d, -1), g, axis=0).reshape(6 * d, -1)  # noqa: E731
+    mha_cfg = cfg.replace(n_kv_heads=6)
+    w_mha = Weights(w.w_q, rep(w.w_k), rep(w.w_v), w.w_o, w.q_norm, w.k_norm)
+    cache_mha = oracle.OracleCache.from_arrays([np.repeat(cache.k[0], g, axis=0)],
+                                               [np.repeat(cache.v[0], g, axis=0)])
+    out_mha, _ = oracle.layer_step(mha_cfg, w_mha, cache_mha, X, C, offs, pos)
+    np.testing.assert_allclose(out, out_mha, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_reduces_to_torch_sdpa_at_position_zero():
+    """Positions all 0 make RoPE the identity; with an empty cache the step is
+    plain non-causal SDPA over [context | block], which torch computes in fp64
+    on the CPU (with the KV heads repeated for GQA)."""
+    torch = pytest.importorskip("torch")
+    cfg = tiny_cfg(n_q_heads=4, n_kv_heads=2, head_dim=8, hidden=16, block_size=4)
+    rng = np.random.default_rng(9)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[0], news=[5])
+    pos = np.zeros_like(pos)
+    out, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    T = torch.from_numpy
+    q = T(oracle.rms_norm((X @ w.w_q.T).reshape(4, 4, 8), w.q_norm, 1e-6)).transpose(0, 1)
+    src = np.concatenate([C, X])
+    k = T(oracle.rms_norm((src @ w.w_k.T).reshape(9, 2, 8), w.k_norm, 1e-6)).transpose(0, 1)
+    v = T((src @ w.w_v.T).reshape(9, 2, 8)).transpose(0, 1)
+    k = k.repeat_interleave(2, dim=0)
+    v = v.repeat_interleave(2, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=False)[0]
+    ref = o.transpose(0, 1).reshape(4, 32).numpy() @ w.w_o.T
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_single_key_returns_its_value():
+    cfg = tiny_cfg(block_size=1)
+    rng = np.random.default_rng(2)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[0], news=[0])
+    out, new = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    v = new.v[0][:, 0, :]  # [nkv, d], the only key
+    o = np.concatenate([v[h // 2] for h in range(4)])
+    np.testing.assert_allclose(out[0], w.w_o @ o, rtol=1e-12)
+
+
+def test_zero_input_gives_uniform_weights():
+    """X = 0 and C = 0 make q = 0 (RMSNorm of zero is zero), so every visible
+    key gets the same weight and the output is o_proj of the mean value row."""
+    cfg = tiny_cfg()
+    rng = np.random.default_rng(4)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[4], news=[2])
+    out, new = oracle.layer_step(cfg, w, cache, np.zeros_like(X), np.zeros_like(C), offs, pos)
+    mean_v = new.v[0].mean(axis=1)  # [nkv, d]
+    o = np.concatenate([mean_v[h // 2] for h in range(4)])
+    for i in range(cfg.block_size):
+        np.testing.assert_allclose(out[i], w.w_o @ o, rtol=1e-12, atol=1e-14)
+
+
+def test_block_queries_are_not_causal():
+    """Permuting the block rows together with their positions permutes the
+    output rows: no query is masked from later block keys."""
+    cfg = tiny_cfg(block_size=4)
+    rng = np.random.default_rng(6)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[3], news=[2])
+    perm = np.array([3, 1, 0, 2])
+    out, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    pos_p = pos.copy()
+    pos_p[2:] = pos[2:][perm]
+    out_p, _ = oracle.layer_step(cfg, w, cache, X[perm], C, offs, pos_p)
+    np.testing.assert_allclose(out_p, out[perm], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- sliding window
+
+def test_window_at_least_the_keys_is_full_attention():
+    cfg = tiny_cfg()
+    rng = np.random.default_rng(8)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[5], news=[2])
+    full, _ = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    T = 5 + 2 + cfg.block_size
+    banded, _ = oracle.layer_step(cfg.replace(sliding_window=T), w, cache, X, C, offs, pos)
+    np.testing.assert_array_equal(full, banded)
+    narrower, _ = oracle.layer_step(cfg.replace(sliding_window=T - cfg.block_size), w, cache, X, C, offs, pos)
+    assert np.max(np.abs(narrower - full)) > 1e-6
+
+
+def test_window_one_sees_only_its_own_key():
+    """Strict band: W = 1 keeps only |Δ| = 0, the query's own block key."""
+    cfg = tiny_cfg(sliding_window=1)
+    rng = np.random.default_rng(10)
+    w = rand_weights(cfg, rng)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens=[4], news=[2])
+    out, new = oracle.layer_step(cfg, w, cache, X, C, offs, pos)
+    T = new.v[0].shape[1]
+    for i in range(cfg.block_size):
+        v = new.v[0][:, T - cfg.block_size + i, :]
+        o = np.concatenate([v[h // 2] for h in range(4)])
+        np.testing.assert_allclose(out[i], w.w_o @ o, rtol=1e-12)
+
+
+def test_window_keep_band_edges():
+    keep = oracle.window_keep(2, 10, 3)  # queries at key index 8, 9
+    assert keep[0].tolist() == [False] * 6 + [True] * 4   # |8 - t| < 3: t in 6..9
+    assert keep[1].tolist() == [False] * 7 + [True] * 3   # |9 - t| < 3: t in 7..9
+
+
+# ---------------------------------------------------------------- cache and crop
+
+def test_incremental_steps_with_crop_equal_one_shot():
+    """Step 1 (ctx1, block1), crop the block off (accepted count 0), step 2
+    (ctx2, block2) equals one step on (ctx1 ‖ ctx2, block2) from the same
+    starting cache: the cache holds exactly the accepted prefix."""
+    cfg = tiny_cfg(batch=1)
+    rng = np.random.default_rng(12)
+    w = rand_weights(cfg, rng)
+    X1, C1, _, _, cache = rand_inputs(cfg, rng, lens=[2], news=[3])
+    X2 = rng.standard_normal(X1.shape)
+    C2 = rng.standard_normal((4, cfg.hidden))
+    bs = cfg.block_size
+    _, c1 = oracle.layer_step(cfg, w, cache, X1, C1, [0, 3], np.arange(2, 2 + 3 + bs))
+    c1 = oracle.crop(c1, 0, 2 + 3)
+    out_inc, c2 = oracle.layer_step(cfg, w, c1, X2, C2, [0, 4], np.arange(5, 5 + 4 + bs))
+    out_one, c3 = oracle.layer_step(cfg, w, cache, X2, np.concatenate([C1, C2]), [0, 7],
+                                    np.arange(2, 2 + 7 + bs))
+    np.testing.assert_allclose(out_inc, out_one, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(c2.k[0], c3.k[0], rtol=1e-13, atol=1e-15)
+
+
+def test_crop_keeps_exact_prefix_and_rejects_growth():
+    rng = np.random.default_rng(13)
+    cache = oracle.OracleCache.from_arrays([rng.standard_normal((2, 9, 4))], [rng.standard_normal((2, 9, 4))])
+    c = oracle.crop(cache, 0, 5)
+    assert c.lengths == [5]
+    np.testing.assert_array_equal(c.k[0], cache.k[0][:, :5])
+    np.testing.assert_array_equal(c.v[0], cache.v[0][:, :5])
+    assert oracle.crop(cache, 0, 9).lengths == [9]
+    assert oracle.crop(cache, 0, 0).lengths == [0]
+    for bad in (10, -1):
+        with pytest.raises(ValueError):
+            oracle.crop(cache, 0, bad)
+    with pytest.raises(IndexError):
+        oracle.crop(cache, 1, 0)

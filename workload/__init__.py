@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs for the DFlash draft-attention layer step.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the layer's arithmetic. Both the oracle-side tests and the HIP
+side (tests, bench) take their inputs from here.
+"""
+from .configs import (  # noqa: F401
+    CONFIGS,
+    Case,
+    LayerConfig,
+    Weights,
+    make_case,
+    round_bf16,
+)
