@@ -1,0 +1,177 @@
+"""DFlash draft-model attention layer step on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/dflash.h`` (``libdflash.so``):
+it marshals torch tensors (device memory and streams only) into plain
+pointers. Every step of the layer runs in the library's HIP kernels; there is
+no Python or CPU fallback, and loading fails loudly without the built library.
+
+    layer = DFlashLayer(LayerShape(...), w_qkv, w_o, q_norm, k_norm)
+    cache = KVCache(batch, n_kv_heads, head_dim, capacity, dtype)
+    out = layer.step(hidden_states, target_hidden, ctx_offsets, positions, cache)
+    cache.crop(seq, new_len)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import DFlashError, check  # noqa: F401
+
+__all__ = ["DFlashLayer", "KVCache", "LayerShape", "DFlashError", "KERNEL_NAMES"]
+KERNEL_NAMES = _lib.KERNEL_NAMES
+
+_DTYPES = {torch.float32: _lib.DFLASH_F32, torch.bfloat16: _lib.DFLASH_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: torch.dtype = torch.bfloat16
+    rope_theta: float = 1e6
+    rms_eps: float = 1e-6
+    sliding_window: int = 0
+    max_position: int = 4096 * 32
+
+
+class KVCache:
+    """Draft KV cache of ``batch`` sequences in device memory.
+
+    ``k`` is ``[batch, n_kv, capacity, head_dim]``; ``v`` is stored transposed,
+    ``[batch, n_kv, head_dim, capacity]``. ``lengths`` is the host array of
+    valid rows that the library reads and updates."""
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        self.batch, self.n_kv_heads, self.head_dim, self.capacity = batch, n_kv_heads, head_dim, capacity
+        self.dtype = dtype
+        self.k = torch.empty((batch, n_kv_heads, capacity, head_dim), dtype=dtype, device=device)
+        self.v = torch.empty((batch, n_kv_heads, head_dim, capacity), dtype=dtype, device=device)
+        self._len = (C.c_int32 * max(batch, 1))()
+        self.lengths = np.ctypeslib.as_array(self._len)[:batch]
+        self.desc = _lib.KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(),
+                                     C.cast(self._len, C.POINTER(C.c_int32)), batch, capacity)
+
+    def set_lengths(self, lengths: Sequence[int]) -> None:
+        self.lengths[:] = np.asarray(lengths, dtype=np.int32)
+
+    def write_prefix(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Place rows ``[0, L)`` of sequence ``seq`` (``k``, ``v``: ``[n_kv, L, d]``)
+        and set its length to L."""
+        L = k.shape[1]
+        self.k[seq, :, :L].copy_(k)
+        self.v[seq, :, :, :L].copy_(v.transpose(1, 2))
+        self.lengths[seq] = L
+
+    def read(self, seq: int):
+        """Valid rows of sequence ``seq`` as ``(k, v)``, each ``[n_kv, len, d]``."""
+        L = int(self.lengths[seq])
+        return self.k[seq, :, :L], self.v[seq, :, :, :L].transpose(1, 2)
+
+    def crop(self, seq: int, new_len: int) -> None:
+        check(_lib.lib().dflash_cache_crop(C.byref(self.desc), int(seq), int(new_len)), "dflash_cache_crop")
+
+
+class DFlashLayer:
+    """One DFlash draft-attention layer over borrowed device weights.
+
+    ``w_qkv`` is ``[(nq + 2 nkv) d, H]`` (rows q heads, k heads, v heads),
+    ``w_o`` ``[H, nq d]``, ``q_norm``/``k_norm`` ``[d]``, all in ``shape.dtype``
+    on the current device."""
+
+    def __init__(self, shape: LayerShape, w_qkv: torch.Tensor, w_o: torch.Tensor,
+                 q_norm: torch.Tensor, k_norm: torch.Tensor):
+        self.shape = shape
+        self._weights = [t.contiguous() for t in (w_qkv, w_o, q_norm, k_norm)]
+        for t in self._weights:
+            if t.dtype != shape.dtype or not t.is_cuda:
+                raise ValueError("weights must be device tensors of the layer dtype")
+        cfg = _lib.Config(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                          shape.block_size, shape.sliding_window, shape.max_position,
+                          _DTYPES[shape.dtype], float(shape.rope_theta), float(shape.rms_eps))
+        w = _lib.Weights(*[t.data_ptr() for t in self._weights])
+        handle = C.c_void_p()
+        with torch.cuda.device(self._weights[0].device):
+            check(_lib.lib().dflash_layer_create(C.byref(cfg), C.byref(w), C.byref(handle)),
+                  "dflash_layer_create")
+        self._h = handle
+        self._ws: Optional[torch.Tensor] = None
+
+    # ------------------------------------------------------------------ api
+    def workspace_bytes(self, batch: int, total_ctx: int, total_keys: int = 0) -> int:
+        return int(_lib.lib().dflash_workspace_bytes(self._h, batch, total_ctx, total_keys))
+
+    def workspace(self, batch: int, total_ctx: int) -> torch.Tensor:
+        need = self.workspace_bytes(batch, total_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+        return self._ws
+
+    def step(self, hidden_states: torch.Tensor, target_hidden: Optional[torch.Tensor],
+             ctx_offsets, positions: torch.Tensor, cache: KVCache,
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+        s = self.shape
+        if len(ctx_offsets) != cache.batch + 1:
+            raise ValueError("ctx_offsets must have batch + 1 entries")
+        offs = (C.c_int32 * (cache.batch + 1))(*[int(o) for o in ctx_offsets])
+        if hidden_states.dtype != s.dtype or not hidden_states.is_contiguous():
+            raise ValueError("hidden_states must be contiguous in the layer dtype")
+        if positions.dtype != torch.int32 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 device tensor")
+        if target_hidden is not None and target_hidden.numel() == 0:
+            target_hidden = None
+        if target_hidden is not None and (target_hidden.dtype != s.dtype or not target_hidden.is_contiguous()):
+            raise ValueError("target_hidden must be contiguous in the layer dtype")
+        if out is None:
+            out = torch.empty((cache.batch * s.block_size, s.hidden), dtype=s.dtype,
+                              device=hidden_states.device)
+        if workspace is None:
+            workspace = self.workspace(cache.batch, int(ctx_offsets[-1]))
+        st = _lib.lib().dflash_attn_step(self._h, _ptr(hidden_states), _ptr(target_hidden), offs,
+                                         _ptr(positions), C.byref(cache.desc), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        check(st, "dflash_attn_step")
+        return out
+
+    def poll_error(self, stream=None) -> int:
+        return int(_lib.lib().dflash_layer_poll_error(self._h, _stream_handle(stream)))
+
+    def set_profiling(self, enable: bool) -> None:
+        check(_lib.lib().dflash_layer_set_profiling(self._h, int(bool(enable))), "set_profiling")
+
+    def kernel_times(self):
+        """``{kernel name: (total ms, launches)}`` since profiling was enabled."""
+        ms = (C.c_double * len(KERNEL_NAMES))()
+        cnt = (C.c_int64 * len(KERNEL_NAMES))()
+        check(_lib.lib().dflash_layer_kernel_times(self._h, ms, cnt), "kernel_times")
+        return {n: (ms[i], cnt[i]) for i, n in enumerate(KERNEL_NAMES)}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.lib().dflash_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

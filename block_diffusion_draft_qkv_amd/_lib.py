@@ -1,0 +1,97 @@
+"""ctypes mirror of include/dflash.h and the loader of libdflash.so.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library. Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+DFLASH_OK = 0
+DFLASH_ERR_ARG = 1
+DFLASH_ERR_SHAPE = 2
+DFLASH_ERR_CAPACITY = 3
+DFLASH_ERR_RANGE = 4
+DFLASH_ERR_UNSUPPORTED = 5
+DFLASH_ERR_HIP = 6
+DFLASH_ERR_WORKSPACE = 7
+DFLASH_F32 = 0
+DFLASH_BF16 = 1
+DFLASH_MAX_BATCH = 256
+KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o")
+
+# Every symbol include/dflash.h declares.
+EXPORTS = (
+    "dflash_layer_create", "dflash_layer_destroy", "dflash_workspace_bytes",
+    "dflash_attn_step", "dflash_cache_crop", "dflash_layer_poll_error",
+    "dflash_layer_set_profiling", "dflash_layer_kernel_times", "dflash_status_string",
+)
+
+
+class Config(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("block_size", C.c_int32), ("sliding_window", C.c_int32),
+                ("max_position", C.c_int32), ("dtype", C.c_int32), ("rope_theta", C.c_double),
+                ("rms_eps", C.c_double)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p)]
+
+
+class KVCacheDesc(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("len", C.POINTER(C.c_int32)),
+                ("batch", C.c_int32), ("capacity", C.c_int32)]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_diffusion_draft_qkv_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        h.dflash_layer_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(C.c_void_p)]
+        h.dflash_layer_create.restype = C.c_int
+        h.dflash_layer_destroy.argtypes = [C.c_void_p]
+        h.dflash_layer_destroy.restype = None
+        h.dflash_workspace_bytes.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64]
+        h.dflash_workspace_bytes.restype = C.c_size_t
+        h.dflash_attn_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32),
+                                       C.c_void_p, C.POINTER(KVCacheDesc), C.c_void_p, C.c_void_p,
+                                       C.c_size_t, C.c_void_p]
+        h.dflash_attn_step.restype = C.c_int
+        h.dflash_cache_crop.argtypes = [C.POINTER(KVCacheDesc), C.c_int32, C.c_int32]
+        h.dflash_cache_crop.restype = C.c_int
+        h.dflash_layer_poll_error.argtypes = [C.c_void_p, C.c_void_p]
+        h.dflash_layer_poll_error.restype = C.c_int
+        h.dflash_layer_set_profiling.argtypes = [C.c_void_p, C.c_int32]
+        h.dflash_layer_set_profiling.restype = C.c_int
+        h.dflash_layer_kernel_times.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        h.dflash_layer_kernel_times.restype = C.c_int
+        h.dflash_status_string.argtypes = [C.c_int]
+        h.dflash_status_string.restype = C.c_char_p
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dflash_status_string(int(status)).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != DFLASH_OK:
+        raise DFlashError(status, where)

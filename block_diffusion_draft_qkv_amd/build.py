@@ -1,0 +1,77 @@
+"""Build ``libdflash.so`` (the C-ABI library of include/dflash.h) for gfx950.
+
+Every HIP source under ``csrc/`` is compiled with hipcc for gfx950 only and
+linked into one shared library next to this file. Packed fp32 VALU ops are
+turned off for the device code (``-packed-fp32-ops``); the host pass of hipcc
+warns that it does not know that feature, which is harmless.
+
+Usage: ``python -m block_diffusion_draft_qkv_amd.build [--debug]``.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdflash.so")
+ARCH = "gfx950"
+SOURCES = ["gemm.hip", "norm_rope_append.hip", "attention.hip", "dflash.cpp"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the DFlash kernels)")
+
+
+def flags(debug: bool = False):
+    f = ["-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+    f += ["-O1", "-g"] if debug else ["-O3"]
+    return f
+
+
+def build(debug: bool = False, verbose: bool = False) -> str:
+    cc = hipcc()
+    out_dir = os.path.join(PKG, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *flags(debug), "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd.insert(1, "-xhip")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--debug", action="store_true")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(debug=a.debug, verbose=a.verbose))
+    sys.exit(0)

@@ -1,0 +1,379 @@
+// Host side of the C ABI declared in include/dflash.h: argument validation,
+// the RoPE table, workspace carving and the kernel sequence of one step.
+//
+// One step, all on the caller's stream:
+//   HK1 grouped GEMM   block rows -> q|k|v, context rows -> k|v (fp32 out)
+//   HK2 norm_rope      per-head RMSNorm + RoPE + Q pack + cache append
+//   HK3 attention      split-KV non-causal GQA over the cache
+//   HK4 merge          only when some (sequence, KV head) was split
+//   HK1 GEMM           o_proj
+// then the host lengths become T_b = L_b + n_b + bs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Pending {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+// Workspace regions of one step (byte offsets from the workspace base).
+struct Carve {
+  size_t qkv, ctxkv, qpack, obuf, part_o, part_ml, total;
+};
+
+}  // namespace
+
+struct dflash_layer {
+  dflash_config cfg;
+  dflash_weights w;
+  int device = 0;
+  int num_cus = 256;
+  float* cos_sin = nullptr;  // [max_pos][d/2] cos, then [max_pos][d/2] sin
+  int32_t* err = nullptr;
+  bool profiling = false;
+  std::vector<Pending> pending;
+  double ms[DFLASH_K_COUNT] = {};
+  int64_t count[DFLASH_K_COUNT] = {};
+};
+
+namespace {
+
+int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
+
+// Attention work-groups for N flat tiles: two per CU (the kernel's LDS budget
+// allows two resident), never more than there are tiles.
+int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
+  const int64_t cap = 2 * (int64_t)L->num_cus;
+  return std::max<int64_t>(1, std::min<int64_t>(cap, n_tiles));
+}
+
+Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
+  const dflash_config& c = L->cfg;
+  const int64_t d = c.head_dim, g = c.n_q_heads / c.n_kv_heads;
+  const int64_t mq = batch * c.block_size, es = elem_size(c);
+  const int64_t gmax = 2 * (int64_t)L->num_cus;
+  Carve w{};
+  size_t off = 0;
+  w.qkv = off;     off += align_up(mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
+  w.ctxkv = off;   off += align_up(std::max<int64_t>(total_ctx, 1) * 2 * c.n_kv_heads * d * 4);
+  w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es);
+  w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
+  w.part_o = off;  off += align_up(2 * gmax * kMaxQueryRows * d * 4);
+  w.part_ml = off; off += align_up(2 * gmax * kMaxQueryRows * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+int validate_config(const dflash_config* c) {
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->block_size <= 0 ||
+      c->max_position <= 0 || c->sliding_window < 0)
+    return DFLASH_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if (c->hidden % 64) return DFLASH_ERR_SHAPE;
+  if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) return DFLASH_ERR_ARG;
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if ((int64_t)c->block_size * (c->n_q_heads / c->n_kv_heads) > kMaxQueryRows)
+    return DFLASH_ERR_UNSUPPORTED;
+  return DFLASH_OK;
+}
+
+void record(dflash_layer* L, int kernel, hipEvent_t* start, hipStream_t s) {
+  if (!L->profiling) return;
+  hipEventCreate(start);
+  hipEventRecord(*start, s);
+  (void)kernel;
+}
+void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s) {
+  if (!L->profiling) return;
+  hipEvent_t stop;
+  hipEventCreate(&stop);
+  hipEventRecord(stop, s);
+  L->pending.push_back({kernel, start, stop});
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_ARG: return "invalid argument";
+    case DFLASH_ERR_SHAPE: return "inconsistent or non-divisible shape";
+    case DFLASH_ERR_CAPACITY: return "step would exceed the cache capacity";
+    case DFLASH_ERR_RANGE: return "value out of range (crop length or position)";
+    case DFLASH_ERR_UNSUPPORTED: return "configuration not supported by the kernels";
+    case DFLASH_ERR_HIP: return "HIP runtime error";
+    case DFLASH_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int dflash_layer_create(const dflash_config* cfg, const dflash_weights* weights,
+                        dflash_layer** out) {
+  if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
+  *out = nullptr;
+  if (!weights->w_qkv || !weights->w_o || !weights->q_norm || !weights->k_norm) return DFLASH_ERR_ARG;
+  const int st = validate_config(cfg);
+  if (st != DFLASH_OK) return st;
+
+  dflash_layer* L = new (std::nothrow) dflash_layer();
+  if (!L) return DFLASH_ERR_HIP;
+  L->cfg = *cfg;
+  L->w = *weights;
+  if (hipGetDevice(&L->device) != hipSuccess) { delete L; return DFLASH_ERR_HIP; }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
+    L->num_cus = cus;
+
+  // cos/sin of pos * theta^(-2t/d), angle and trig in float64, stored fp32.
+  const int half = cfg->head_dim / 2;
+  const size_t n = (size_t)cfg->max_position * half;
+  std::vector<float> table(2 * n);
+  std::vector<double> inv(half);
+  for (int t = 0; t < half; ++t) inv[t] = std::pow(cfg->rope_theta, -2.0 * t / cfg->head_dim);
+  for (int64_t p = 0; p < cfg->max_position; ++p)
+    for (int t = 0; t < half; ++t) {
+      const double ang = (double)p * inv[t];
+      table[(size_t)p * half + t] = (float)std::cos(ang);
+      table[n + (size_t)p * half + t] = (float)std::sin(ang);
+    }
+  if (hipMalloc(&L->cos_sin, 2 * n * sizeof(float)) != hipSuccess ||
+      hipMemcpy(L->cos_sin, table.data(), 2 * n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMalloc(&L->err, sizeof(int32_t)) != hipSuccess ||
+      hipMemset(L->err, 0, sizeof(int32_t)) != hipSuccess) {
+    if (L->cos_sin) hipFree(L->cos_sin);
+    if (L->err) hipFree(L->err);
+    delete L;
+    return DFLASH_ERR_HIP;
+  }
+  *out = L;
+  return DFLASH_OK;
+}
+
+void dflash_layer_destroy(dflash_layer* L) {
+  if (!L) return;
+  hipDeviceSynchronize();
+  for (auto& p : L->pending) {
+    hipEventDestroy(p.start);
+    hipEventDestroy(p.stop);
+  }
+  hipFree(L->cos_sin);
+  hipFree(L->err);
+  delete L;
+}
+
+size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t total_ctx,
+                              int64_t total_keys) {
+  if (!L || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0 || total_keys < 0) return 0;
+  return carve(L, batch, total_ctx).total;
+}
+
+int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* target_hidden,
+                     const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!L || !hidden_states || !ctx_offsets || !positions || !cache || !out) return DFLASH_ERR_ARG;
+  if (!cache->k || !cache->v || !cache->len) return DFLASH_ERR_ARG;
+  const dflash_config& c = L->cfg;
+  const int B = cache->batch;
+  if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
+  if (cache->capacity <= 0 || cache->capacity % kKeyTile) return DFLASH_ERR_SHAPE;
+  if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
+  const int bs = c.block_size, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int g = nq / nkv, R = bs * g;
+
+  SeqTable seq;
+  std::memset(&seq, 0, sizeof(seq));
+  seq.batch = B;
+  int64_t n_tiles = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = (int64_t)ctx_offsets[b + 1] - ctx_offsets[b];
+    if (n < 0) return DFLASH_ERR_SHAPE;
+    if (cache->len[b] < 0) return DFLASH_ERR_SHAPE;
+    const int64_t T = (int64_t)cache->len[b] + n + bs;
+    if (T > cache->capacity) return DFLASH_ERR_CAPACITY;
+    seq.len[b] = cache->len[b];
+    seq.ctx_off[b] = ctx_offsets[b];
+    int64_t first = 0;
+    if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
+    n_tiles += nkv * ((T + kKeyTile - 1) / kKeyTile - first / kKeyTile);
+  }
+  seq.ctx_off[B] = ctx_offsets[B];
+  const int64_t Mc = ctx_offsets[B];
+  if (Mc > 0 && !target_hidden) return DFLASH_ERR_ARG;
+  if (!workspace) return DFLASH_ERR_WORKSPACE;
+  const Carve wc = carve(L, B, Mc);
+  if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return DFLASH_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qkv = reinterpret_cast<float*>(ws + wc.qkv);
+  float* ctxkv = reinterpret_cast<float*>(ws + wc.ctxkv);
+  void* qpack = ws + wc.qpack;
+  void* obuf = ws + wc.obuf;
+  const int es = elem_size(c);
+  const int Mq = B * bs, H = c.hidden;
+  const int Nqkv = (nq + 2 * nkv) * d, Nkv = 2 * nkv * d;
+
+  // HK1: block q|k|v and context k|v in one launch.
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.nprob = 1;
+  ga.p[0] = {hidden_states, L->w.w_qkv, qkv, Mq, Nqkv, H, H, H, Nqkv,
+             (Nqkv + kGemmBN - 1) / kGemmBN, 0};
+  int tiles = ((Mq + kGemmBM - 1) / kGemmBM) * ga.p[0].tiles_n;
+  if (Mc > 0) {
+    const char* wkv = static_cast<const char*>(L->w.w_qkv) + (size_t)nq * d * H * es;
+    ga.p[1] = {target_hidden, wkv, ctxkv, (int32_t)Mc, Nkv, H, H, H, Nkv,
+               (Nkv + kGemmBN - 1) / kGemmBN, tiles};
+    ga.nprob = 2;
+    tiles += (int)((Mc + kGemmBM - 1) / kGemmBM) * ga.p[1].tiles_n;
+  }
+  hipEvent_t ev;
+  record(L, DFLASH_K_GEMM_QKV, &ev, s);
+  if (launch_gemm(c.dtype, true, ga, tiles, s) != hipSuccess) return DFLASH_ERR_HIP;
+  record_end(L, DFLASH_K_GEMM_QKV, ev, s);
+
+  // HK2
+  NormRopeArgs na;
+  na.qkv = qkv;
+  na.ctxkv = ctxkv;
+  na.positions = positions;
+  na.cos_sin = L->cos_sin;
+  na.q_norm = L->w.q_norm;
+  na.k_norm = L->w.k_norm;
+  na.qpack = qpack;
+  na.kc = cache->k;
+  na.vc = cache->v;
+  na.err = L->err;
+  na.nq = nq; na.nkv = nkv; na.bs = bs; na.cap = cache->capacity; na.max_pos = c.max_position;
+  na.eps = (float)c.rms_eps;
+  na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  na.seq = seq;
+  record(L, DFLASH_K_NORM_ROPE, &ev, s);
+  if (launch_norm_rope(c.dtype, d, na, B * nkv, s) != hipSuccess) return DFLASH_ERR_HIP;
+  record_end(L, DFLASH_K_NORM_ROPE, ev, s);
+
+  // HK3 (+ HK4)
+  AttnArgs aa;
+  aa.q = qpack;
+  aa.kc = cache->k;
+  aa.vc = cache->v;
+  aa.o = obuf;
+  aa.part_o = reinterpret_cast<float*>(ws + wc.part_o);
+  aa.part_ml = reinterpret_cast<float*>(ws + wc.part_ml);
+  aa.nq = nq; aa.nkv = nkv; aa.bs = bs; aa.R = R; aa.cap = cache->capacity;
+  aa.window = c.sliding_window;
+  aa.total_tiles = n_tiles;
+  aa.G = (int32_t)attn_groups(L, n_tiles);
+  aa.seq = seq;
+  record(L, DFLASH_K_ATTN, &ev, s);
+  if (launch_attn(c.dtype, d, aa, s) != hipSuccess) return DFLASH_ERR_HIP;
+  record_end(L, DFLASH_K_ATTN, ev, s);
+
+  // A merge is needed iff some pair straddles two work-group ranges.
+  bool split = false;
+  {
+    int64_t f = 0;
+    for (int b = 0; b < B && !split; ++b) {
+      const int64_t T = (int64_t)seq.len[b] + (seq.ctx_off[b + 1] - seq.ctx_off[b]) + bs;
+      int64_t first = 0;
+      if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
+      const int64_t cnt = (T + kKeyTile - 1) / kKeyTile - first / kKeyTile;
+      for (int j = 0; j < nkv && !split; ++j, f += cnt)
+        split = part_owner(f, n_tiles, aa.G) != part_owner(f + cnt - 1, n_tiles, aa.G);
+    }
+  }
+  if (split) {
+    const int rows_per_group = 256 / (d / 4);
+    record(L, DFLASH_K_MERGE, &ev, s);
+    if (launch_merge(c.dtype, d, aa, (R + rows_per_group - 1) / rows_per_group, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    record_end(L, DFLASH_K_MERGE, ev, s);
+  }
+
+  // HK1: o_proj
+  GemmArgs go;
+  std::memset(&go, 0, sizeof(go));
+  go.nprob = 1;
+  go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + kGemmBN - 1) / kGemmBN, 0};
+  record(L, DFLASH_K_GEMM_O, &ev, s);
+  if (launch_gemm(c.dtype, false, go, ((Mq + kGemmBM - 1) / kGemmBM) * go.p[0].tiles_n, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  record_end(L, DFLASH_K_GEMM_O, ev, s);
+
+  for (int b = 0; b < B; ++b) cache->len[b] += (ctx_offsets[b + 1] - ctx_offsets[b]) + bs;
+  return DFLASH_OK;
+}
+
+int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len) {
+  if (!cache || !cache->len || seq < 0 || seq >= cache->batch) return DFLASH_ERR_ARG;
+  if (new_len < 0 || new_len > cache->len[seq]) return DFLASH_ERR_RANGE;
+  cache->len[seq] = new_len;
+  return DFLASH_OK;
+}
+
+int dflash_layer_poll_error(dflash_layer* L, void* stream) {
+  if (!L) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t flag = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return DFLASH_ERR_HIP;
+  if (hipMemcpy(&flag, L->err, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_ERR_HIP;
+  if (flag) {
+    if (hipMemset(L->err, 0, sizeof(int32_t)) != hipSuccess) return DFLASH_ERR_HIP;
+    return DFLASH_ERR_RANGE;
+  }
+  return DFLASH_OK;
+}
+
+int dflash_layer_set_profiling(dflash_layer* L, int32_t enable) {
+  if (!L) return DFLASH_ERR_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return DFLASH_ERR_HIP;
+  for (auto& p : L->pending) {
+    hipEventDestroy(p.start);
+    hipEventDestroy(p.stop);
+  }
+  L->pending.clear();
+  std::fill(L->ms, L->ms + DFLASH_K_COUNT, 0.0);
+  std::fill(L->count, L->count + DFLASH_K_COUNT, 0);
+  L->profiling = enable != 0;
+  return DFLASH_OK;
+}
+
+int dflash_layer_kernel_times(dflash_layer* L, double* ms, int64_t* count) {
+  if (!L || !ms || !count) return DFLASH_ERR_ARG;
+  for (auto& p : L->pending) {
+    if (hipEventSynchronize(p.stop) != hipSuccess) return DFLASH_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.start, p.stop) != hipSuccess) return DFLASH_ERR_HIP;
+    L->ms[p.kernel] += t;
+    L->count[p.kernel] += 1;
+    hipEventDestroy(p.start);
+    hipEventDestroy(p.stop);
+  }
+  L->pending.clear();
+  for (int k = 0; k < DFLASH_K_COUNT; ++k) {
+    ms[k] = L->ms[k];
+    count[k] = L->count[k];
+  }
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dflash {
+
+// ---------------------------------------------------------------- projections
+// C[m][n] = sum_k A[m][k] * B[n][k]: both operands row-major with k contiguous
+// (an nn.Linear weight is B). Up to two independent problems per launch.
+struct GemmProblem {
+  const void* a;
+  const void* b;
+  void* c;
+  int32_t m, n, k;
+  int32_t lda, ldb, ldc;
+  int32_t tiles_n;     // ceil(n / BN)
+  int32_t tile_begin;  // first flat tile index of this problem in the launch
+};
+struct GemmArgs {
+  GemmProblem p[2];
+  int32_t nprob;
+};
+constexpr int kGemmBM = 64;
+constexpr int kGemmBN = 128;
+// dtype: 0 fp32, 1 bf16 (A, B element type). out_f32: C is fp32, else C has
+// the element type of A and B.
+hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles,
+                       hipStream_t stream);
+
+// ------------------------------------------------- norm + RoPE + append + Q
+struct NormRopeArgs {
+  const float* qkv;        // [B*bs][(nq + 2 nkv) d] block projections (fp32)
+  const float* ctxkv;      // [sum n_b][2 nkv d] context projections (fp32)
+  const int32_t* positions;
+  const float* cos_sin;    // cos [max_pos][d/2] then sin [max_pos][d/2]
+  const void* q_norm;
+  const void* k_norm;
+  void* qpack;             // [B*nkv][R][d]: R = bs*g rows ordered (i, hh)
+  void* kc;                // cache K [B][nkv][cap][d]
+  void* vc;                // cache V [B][nkv][d][cap]
+  int32_t* err;
+  int32_t nq, nkv, bs, cap, max_pos;
+  float eps, qscale;
+  SeqTable seq;
+};
+hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
+                            hipStream_t stream);
+
+// ------------------------------------------------------------------ attention
+// Flattened work: pairs (b, j) in b-major order, each owning the 64-key tiles
+// [lo_b, hi_b) of sequence b (lo_b > 0 only under a sliding window). Work-group
+// w takes flat tiles [floor(w N / G), floor((w+1) N / G)).
+struct AttnArgs {
+  const void* q;           // qpack
+  const void* kc;
+  const void* vc;
+  void* o;                 // [B*bs][nq d] attention output (pre o_proj)
+  float* part_o;           // [2G][64][d] un-normalised partial outputs
+  float* part_ml;          // [2G][64][2] running max (log2 domain) and sum
+  int32_t nq, nkv, bs, R, cap, window, G;
+  int64_t total_tiles;
+  SeqTable seq;
+};
+hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream);
+hipError_t launch_merge(int dtype, int head_dim, const AttnArgs& args, int merge_groups,
+                        hipStream_t stream);
+
+// Host-side mirror of the kernels' partition (used to size and skip launches).
+inline int64_t part_bound(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
+inline int64_t part_owner(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
+
+}  // namespace dflash

@@ -1,0 +1,200 @@
+/*
+ * dflash.h -- C ABI of the DFlash draft-model attention layer step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One call runs the layer that the pages call Qwen3DFlashAttention for a batch
+ * of sequences: the draft block (one anchor plus block_size-1 mask tokens) is
+ * projected to Q, K and V, the new target-context rows to K and V with the same
+ * weights; q and k are RMS-normalised per head, rotated with neox RoPE (keys at
+ * every position of the window [new context | block], queries at its trailing
+ * block_size positions), appended to the draft KV cache, and the block's
+ * queries attend non-causally (optionally inside a sliding-window band) over
+ * every cached key; o_proj maps the heads back to the hidden size.
+ *   - NeMo AutoModel page "draft_qwen3": Qwen3DFlashAttention, forward,
+ *     apply_rotary_pos_emb, _sliding_window_mask.
+ *   - vLLM page "qwen3_dflash": DFlashQwen3Attention.__init__ and forward
+ *     (fused qkv_proj with rows q|k|v, per-head q_norm/k_norm, neox RoPE,
+ *     o_proj, no bias).
+ *   - "DFlash源码导读（二）" (cf-1.com), sections 1-5: QK-RMSNorm, dual-stream
+ *     K/V concat, full-window RoPE, cache update and crop(start), non-causal
+ *     block attention.
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns a dflash_status (0 = DFLASH_OK). Nothing throws
+ *     across the ABI.
+ *   - All arguments are validated on the host before any work is enqueued; on
+ *     an error nothing is launched and no state (cache lengths, outputs)
+ *     changes.
+ *   - Device pointers are borrowed: the caller allocates and frees every buffer
+ *     passed in and keeps weights alive for the layer's lifetime. The library
+ *     allocates only its own cos/sin table and error flag (at create).
+ *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
+ *     NULL is the default stream) and the calls return without synchronising,
+ *     except dflash_layer_poll_error and dflash_layer_kernel_times.
+ *   - Element type of every activation, weight and cache buffer is the
+ *     config's dtype (fp32 or bf16); accumulation is fp32.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_ERR_ARG = 1,          /* null pointer, bad index, bad flag value           */
+    DFLASH_ERR_SHAPE = 2,        /* sizes inconsistent or not divisible as required   */
+    DFLASH_ERR_CAPACITY = 3,     /* a step would write past the cache capacity        */
+    DFLASH_ERR_RANGE = 4,        /* crop past the length; position outside the table  */
+    DFLASH_ERR_UNSUPPORTED = 5,  /* valid but not built (head_dim, batch, query rows) */
+    DFLASH_ERR_HIP = 6,          /* a HIP runtime call failed                         */
+    DFLASH_ERR_WORKSPACE = 7     /* workspace missing or smaller than required        */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Largest batch one step accepts (per-sequence lengths ride in the kernel
+ * arguments). */
+#define DFLASH_MAX_BATCH 256
+
+/* Layer shape and numerics. Limits checked by dflash_layer_create:
+ *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
+ *   block_size * (n_q_heads / n_kv_heads) <= 64 (the query rows that share one
+ *   KV head, packed into MFMA tiles); hidden % 64 == 0;
+ *   rope_theta > 0; rms_eps >= 0; sliding_window >= 0; max_position >= 1. */
+typedef struct {
+    int32_t hidden;          /* H                                                 */
+    int32_t n_q_heads;       /* nq                                                */
+    int32_t n_kv_heads;      /* nkv                                               */
+    int32_t head_dim;        /* d                                                 */
+    int32_t block_size;      /* bs: draft tokens per block (queries per sequence) */
+    int32_t sliding_window;  /* 0: full attention; W > 0: key t visible to block
+                                query i iff |(T - bs + i) - t| < W (strict band)  */
+    int32_t max_position;    /* positions must lie in [0, max_position)           */
+    int32_t dtype;           /* dflash_dtype                                      */
+    double rope_theta;       /* RoPE base; inv_freq[t] = theta^(-2t/d)            */
+    double rms_eps;          /* RMSNorm eps, added to the mean square             */
+} dflash_config;
+
+/* Weights, device memory, row-major in the config dtype (nn.Linear [out, in]). */
+typedef struct {
+    const void* w_qkv;   /* [(nq + 2*nkv) * d, H]: rows of all q heads, then all k
+                            heads, then all v heads (head h = rows h*d .. h*d+d-1) */
+    const void* w_o;     /* [H, nq * d]                                           */
+    const void* q_norm;  /* [d] RMSNorm gain of q                                 */
+    const void* k_norm;  /* [d] RMSNorm gain of k                                 */
+} dflash_weights;
+
+/* Draft KV cache of `batch` sequences, device memory owned by the caller.
+ *   k: [batch][n_kv][capacity][head_dim]   K rows, key-major
+ *   v: [batch][n_kv][head_dim][capacity]   V stored transposed (key index
+ *                                          contiguous), so that the P*V
+ *                                          contraction streams it directly
+ *   len: HOST array [batch], the valid rows of each sequence; it is the
+ *        authoritative length (kernels receive it by value).
+ * K holds post-norm, post-RoPE keys; V holds raw values. Rows at or past len
+ * are dead: never read into a result, never zeroed.
+ * capacity must be a positive multiple of 64. */
+typedef struct {
+    void* k;
+    void* v;
+    int32_t* len;
+    int32_t batch;
+    int32_t capacity;
+} dflash_kv_cache;
+
+typedef struct dflash_layer dflash_layer; /* opaque */
+
+/* Create a layer handle for `cfg` over borrowed `weights` (device pointers that
+ * must outlive the handle). Builds the RoPE cos/sin table on the host in
+ * float64 and uploads it as fp32 [max_position][d/2] cos then sin (the pages
+ * keep inv_freq in fp32 so that long positions do not dephase; the table keeps
+ * the angle exact before rounding). The current HIP device at create time is
+ * the layer's device.
+ * Errors: DFLASH_ERR_ARG (null), DFLASH_ERR_SHAPE / DFLASH_ERR_UNSUPPORTED
+ * (limits above), DFLASH_ERR_HIP (allocation or copy failed). */
+int dflash_layer_create(const dflash_config* cfg, const dflash_weights* weights,
+                        dflash_layer** out);
+
+/* Release the handle's own table and flag. Waits for the device to finish
+ * work that may still read them. NULL is a no-op. */
+void dflash_layer_destroy(dflash_layer* layer);
+
+/* Bytes of device workspace a step needs for `batch` sequences with
+ * `total_ctx` = sum of new context rows and `total_keys` = sum over sequences
+ * of the keys each attends over (T_b = len_b + n_b + block_size). A bound: any
+ * step with no larger batch, total_ctx and total_keys fits. 0 on bad input. */
+size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
+                              int64_t total_ctx, int64_t total_keys);
+
+/* One layer step for every sequence of `cache` (B = cache->batch).
+ *   hidden_states  device [B * bs, H]: the draft block of sequence b is rows
+ *                  b*bs .. b*bs+bs-1 (one anchor plus bs-1 mask embeddings).
+ *   target_hidden  device [sum n_b, H]: new context rows, sequence b owning
+ *                  rows ctx_offsets[b] .. ctx_offsets[b+1]-1; may be NULL when
+ *                  every n_b is 0.
+ *   ctx_offsets    HOST [B + 1], ctx_offsets[0] == 0, non-decreasing.
+ *   positions      device int32 [sum n_b + B * bs]: sequence b's window
+ *                  [new context | block] (n_b + bs entries) starts at
+ *                  ctx_offsets[b] + b*bs. Keys are rotated at their own
+ *                  position, queries at the block's positions (the window's
+ *                  suffix). Values outside [0, max_position) are clamped and
+ *                  latch DFLASH_ERR_RANGE for dflash_layer_poll_error.
+ *   cache          rows [len_b, len_b + n_b + bs) of each sequence receive the
+ *                  new context rows then the block rows; len_b then becomes
+ *                  T_b = len_b + n_b + bs.
+ *   out            device [B * bs, H]: o_proj of the attention output.
+ *   workspace      device scratch of at least dflash_workspace_bytes(...)
+ *                  bytes, 256-byte aligned; contents need no initialisation.
+ * Errors (nothing launched, nothing changed): DFLASH_ERR_ARG (null pointer,
+ * batch outside [1, DFLASH_MAX_BATCH]), DFLASH_ERR_SHAPE (bad offsets,
+ * negative len, capacity not a multiple of 64), DFLASH_ERR_CAPACITY (some
+ * T_b > capacity), DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP (launch failure;
+ * lengths are then left unchanged). */
+int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
+                     const void* target_hidden, const int32_t* ctx_offsets,
+                     const int32_t* positions, dflash_kv_cache* cache, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rewind sequence `seq` to its first `new_len` rows (the accepted prefix after
+ * verification; "DFlash源码导读（二）" section 4, crop(start)). Only the host
+ * length changes: no data moves, rows below new_len stay bit-identical.
+ * Host-only; safe to call while earlier steps are still in flight on a stream,
+ * because later steps read the length when they are enqueued.
+ * Errors: DFLASH_ERR_ARG (null cache or seq outside [0, batch)),
+ * DFLASH_ERR_RANGE (new_len outside [0, len[seq]]: crop never grows). */
+int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len);
+
+/* Synchronise `stream`, then return and clear the layer's sticky device-side
+ * error (DFLASH_ERR_RANGE if a position fell outside the table since the last
+ * poll), or DFLASH_OK. */
+int dflash_layer_poll_error(dflash_layer* layer, void* stream);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * kernel of a step. enable != 0 turns it on (and clears the totals). */
+int dflash_layer_set_profiling(dflash_layer* layer, int32_t enable);
+
+/* Synchronise on the recorded events and return, for each kernel of the step
+ * (indices DFLASH_K_*), the summed milliseconds and the number of launches
+ * since profiling was enabled. `ms` and `count` hold DFLASH_K_COUNT entries. */
+enum {
+    DFLASH_K_GEMM_QKV = 0,   /* grouped projection: block QKV and context KV     */
+    DFLASH_K_NORM_ROPE = 1,  /* per-head RMSNorm + RoPE + Q pack + cache append   */
+    DFLASH_K_ATTN = 2,       /* split-KV non-causal GQA attention                 */
+    DFLASH_K_MERGE = 3,      /* log-sum-exp merge of split partials               */
+    DFLASH_K_GEMM_O = 4,     /* o_proj                                            */
+    DFLASH_K_COUNT = 5
+};
+int dflash_layer_kernel_times(dflash_layer* layer, double* ms, int64_t* count);
+
+/* Static description of a status code. */
+const char* dflash_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

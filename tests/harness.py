@@ -1,0 +1,120 @@
+"""Shared helpers of the GPU tests: put a seeded case on the device through the
+binding, run the library, and compare with the oracle.
+
+Tolerances (against the float64 oracle):
+  fp32: max |err| <= 1e-4.
+  bf16: max |err| <= 2e-2 and rel-RMS err <= 1e-2.
+Cache indexing, lengths and untouched rows: bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from workload import Case
+
+CANARY_BF16 = 0x7FA5          # a NaN pattern: any read of a dead row poisons the result
+CANARY_F32 = 0x7FC0A5A5
+
+
+def torch_dtype(case: Case):
+    return torch.bfloat16 if case.cfg.dtype == "bf16" else torch.float32
+
+
+def dev(a, dtype, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dtype)
+
+
+def make_layer(case: Case):
+    from block_diffusion_draft_qkv_amd import DFlashLayer, LayerShape
+    cfg, w = case.cfg, case.weights
+    dt = torch_dtype(case)
+    shape = LayerShape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, dt,
+                       cfg.rope_theta, cfg.rms_eps, cfg.sliding_window, cfg.max_position)
+    return DFlashLayer(shape, dev(w.w_qkv, dt), dev(w.w_o, dt), dev(w.q_norm, dt), dev(w.k_norm, dt))
+
+
+def fill_canary(t: torch.Tensor):
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(CANARY_BF16)
+    else:
+        t.view(torch.int32).fill_(CANARY_F32)
+
+
+def make_cache(case: Case, capacity: int = None):
+    from block_diffusion_draft_qkv_amd import KVCache
+    cfg = case.cfg
+    dt = torch_dtype(case)
+    cap = capacity or case.capacity()
+    cache = KVCache(case.batch, cfg.n_kv_heads, cfg.head_dim, cap, dt)
+    fill_canary(cache.k)
+    fill_canary(cache.v)
+    for b in range(case.batch):
+        cache.write_prefix(b, dev(case.cache_k[b], dt), dev(case.cache_v[b], dt))
+    return cache
+
+
+def step_inputs(case: Case):
+    dt = torch_dtype(case)
+    hs = dev(case.hidden_states, dt)
+    th = dev(case.target_hidden, dt) if case.target_hidden.size else None
+    pos = torch.from_numpy(case.positions.astype(np.int32)).cuda()
+    return hs, th, pos
+
+
+def run_oracle(case: Case, cache: oracle.OracleCache = None, hidden=None, target=None, offsets=None,
+               positions=None):
+    if cache is None:
+        cache = oracle.OracleCache.from_arrays(case.cache_k, case.cache_v)
+    return oracle.layer_step(case.cfg, case.weights, cache,
+                             case.hidden_states if hidden is None else hidden,
+                             case.target_hidden if target is None else target,
+                             case.ctx_offsets if offsets is None else offsets,
+                             case.positions if positions is None else positions)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    den = float(np.sqrt(np.mean(ref * ref))) if ref.size else 1.0
+    rel_rms = float(np.sqrt(np.mean(err * err))) / den if ref.size and den > 0 else 0.0
+    return max_abs, rel_rms
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    max_abs, rel_rms = errors(got, ref)
+    if dtype == "fp32":
+        assert max_abs <= 1e-4, f"{what}: max abs {max_abs:.3e} > 1e-4"
+    else:
+        assert max_abs <= 2e-2 and rel_rms <= 1e-2, \
+            f"{what}: max abs {max_abs:.3e} (<= 2e-2), rel-RMS {rel_rms:.3e} (<= 1e-2)"
+    return max_abs, rel_rms
+
+
+def raw_bits(t: torch.Tensor) -> np.ndarray:
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).cpu().numpy()
+
+
+def check_cache_after_step(case: Case, cache, before_k, before_v, new_cache: oracle.OracleCache):
+    """New rows [L_b, T_b) match the oracle; rows < L_b and >= T_b are
+    bit-identical to what they were; lengths equal T_b exactly."""
+    L, T = case.cached_len, case.total_len
+    assert cache.lengths.tolist() == T.tolist()
+    k_bits, v_bits = raw_bits(cache.k), raw_bits(cache.v)
+    for b in range(case.batch):
+        lb, tb = int(L[b]), int(T[b])
+        np.testing.assert_array_equal(k_bits[b, :, :lb], before_k[b, :, :lb])
+        np.testing.assert_array_equal(k_bits[b, :, tb:], before_k[b, :, tb:])
+        np.testing.assert_array_equal(v_bits[b, :, :, :lb], before_v[b, :, :, :lb])
+        np.testing.assert_array_equal(v_bits[b, :, :, tb:], before_v[b, :, :, tb:])
+        k_new = to64(cache.k[b, :, lb:tb])
+        v_new = to64(cache.v[b, :, :, lb:tb].transpose(1, 2))
+        assert_close(k_new, new_cache.k[b][:, lb:tb], case.cfg.dtype, f"cache K seq {b}")
+        assert_close(v_new, new_cache.v[b][:, lb:tb], case.cfg.dtype, f"cache V seq {b}")
