@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft-attention layer step on one MI355X.
+
+Workload: a batched ragged decode round of the Qwen3-8B-shaped draft layer
+(hidden 4096, 32 Q / 8 KV heads, head_dim 128, block 16, bf16): B=32 sequences
+with cached context U{512..8192}, U{1..16} new context rows each, the step,
+then the crop of every sequence to its accepted prefix (accepted count
+U{0..16}). Inputs are synthetic and seeded (workload.make_case) and already
+resident in HBM when timing starts. Several copies of the KV cache rotate from
+step to step so the 256 MB Infinity Cache cannot serve a cache that the
+previous step just streamed.
+
+One "step" = the whole hot path: grouped QKV/context-KV GEMM, norm+RoPE+append,
+split-KV attention, merge, o_proj, and the crop. Between timed steps the
+lengths are rewound to the round's starting lengths (host-only) so that every
+step sees the same workload.
+
+Prints ONE JSON line. ``value`` is draft-block tokens/s (B*bs per step);
+``roofline`` covers the attention kernel (HBM-bound): algorithmic bytes per
+launch (K and V rows once, Q and O once) over its mean launch time measured
+with HIP events on the launch stream over the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft-block tokens/s + attention HBM GB/s (% of peak), B=32 ctx 512–8K"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_splitkv_c3_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", "attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C3", help="workload (C3 is the reported one)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=3, help="KV-cache copies rotated across steps")
+    ap.add_argument("--cpu-sample", type=int, default=32,
+                    help="sequences of the workload the oracle is timed on (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(case, n_seq: int, runs: int = 5):
+    """Time the float64 oracle on the first n_seq sequences of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    k = min(n_seq, case.batch)
+    bs = case.cfg.block_size
+    offs = case.ctx_offsets[:k + 1]
+    npos = int(offs[-1]) + k * bs
+    cache = oracle.OracleCache.from_arrays(case.cache_k[:k], case.cache_v[:k])
+    args = (case.cfg, case.weights, cache, case.hidden_states[:k * bs],
+            case.target_hidden[:int(offs[-1])], offs, case.positions[:npos])
+    times = []
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            oracle.layer_step(*args)
+            times.append(time.perf_counter() - t0)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    t = float(np.median(times))
+    return {"value": k * bs / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{k} of {case.batch} sequences of the same workload "
+                      f"({int(case.total_len[:k].sum())} keys), float64 numpy, median of "
+                      f"{len(times)} runs of {t:.2f}s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: the multi-GPU path of this layer is a design "
+              "(sequence/head sharding) that is not built; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import DFlashLayer, KVCache, LayerShape
+    from workload import make_case
+
+    case = make_case(a.config, seed=a.seed)
+    cfg = case.cfg
+    B, bs, H = case.batch, cfg.block_size, cfg.hidden
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    es = 2 if cfg.dtype == "bf16" else 4
+
+    def dev(x, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+    w = case.weights
+    layer = DFlashLayer(LayerShape(H, nq, nkv, d, bs, dt, cfg.rope_theta, cfg.rms_eps,
+                                   cfg.sliding_window, cfg.max_position),
+                        dev(w.w_qkv), dev(w.w_o), dev(w.q_norm), dev(w.k_norm))
+    cap = case.capacity()
+    caches = []
+    for i in range(a.copies):
+        c = KVCache(B, nkv, d, cap, dt)
+        if i == 0:
+            for b in range(B):
+                c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
+        else:
+            c.k.copy_(caches[0].k)
+            c.v.copy_(caches[0].v)
+            c.set_lengths(case.cached_len)
+        caches.append(c)
+    hs = dev(case.hidden_states)
+    th = dev(case.target_hidden) if case.target_hidden.size else None
+    pos = dev(case.positions, torch.int32)
+    offs = [int(o) for o in case.ctx_offsets]
+    out = torch.empty((B * bs, H), dtype=dt, device="cuda")
+    ws = layer.workspace(B, offs[-1])
+    L0 = case.cached_len.copy()
+    accepted = (case.cached_len + case.new_ctx + case.accept).tolist()
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        cache = caches[i % a.copies]
+        layer.step(hs, th, offs, pos, cache, out=out, workspace=ws)
+        for b in range(B):
+            cache.crop(b, accepted[b])
+        cache.set_lengths(L0)  # rewind for the next use of this copy (not part of the step)
+
+    for i in range(a.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    if layer.poll_error() != 0:
+        raise RuntimeError("position outside the RoPE table during warm-up")
+
+    layer.set_profiling(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        one_step(a.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = layer.kernel_times()
+    layer.set_profiling(False)
+
+    ms_per_step = elapsed * 1e3 / a.steps
+    tokens_per_s = B * bs / (elapsed / a.steps)
+
+    # Algorithmic bytes and flops of one step.
+    T = case.total_len.astype(np.int64)
+    keys = np.minimum(T, cfg.sliding_window + bs - 1) if cfg.sliding_window else T
+    attn_bytes = int(keys.sum()) * nkv * d * 2 * es + 2 * B * bs * nq * d * es
+    mc = int(offs[-1])
+    proj_flops = 2 * H * (B * bs * (nq + 2 * nkv) * d + mc * 2 * nkv * d + B * bs * nq * d)
+
+    def mean_us(name):
+        ms, n = kt[name]
+        return ms * 1e3 / n if n else 0.0
+
+    t_attn = mean_us("attn")
+    t_merge = mean_us("merge")
+    t_proj = mean_us("gemm_qkv") + mean_us("gemm_o")
+    achieved = attn_bytes / (t_attn * 1e-6) / 1e9
+    traffic = traffic_per_launch()
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: one draft-attention layer step + crop, B={B}, cached ctx "
+                         f"{cfg.cached_len}, new ctx {cfg.new_ctx}, block {bs}, H={H}, "
+                         f"{nq}/{nkv} heads, head_dim {d}, window {cfg.sliding_window or 'none'}"),
+            "batch": B, "block_size": bs, "total_keys": int(T.sum()), "new_ctx_rows": mc,
+            "seed": a.seed, "kv_cache_copies": a.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "attn_splitkv_kernel<bf16,128>",
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "mean_launch_us": round(t_attn, 2),
+        },
+        "attention_with_merge": {
+            "achieved_gbs": round(attn_bytes / ((t_attn + t_merge) * 1e-6) / 1e9, 1),
+            "merge_us": round(t_merge, 2),
+        },
+        "projections": {
+            "bound": "mfma", "flops_per_step": proj_flops,
+            "achieved_tflops": round(proj_flops / (t_proj * 1e-6) / 1e12, 1) if t_proj else None,
+            "peak_tflops": BF16_PEAK_TFLOPS,
+        },
+        "kernel_mean_us": {k: round(mean_us(k), 2) for k in kt},
+        "kernel_sum_us_per_step": round(sum(v[0] for v in kt.values()) * 1e3 / a.steps, 2),
+    }
+    if a.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_baseline(case, a.cpu_sample)
+    layer.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+# DFLASH_LIB may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libdflash.so")
 
 DFLASH_OK = 0
 DFLASH_ERR_ARG = 1

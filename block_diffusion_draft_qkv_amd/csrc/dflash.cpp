@@ -47,6 +47,7 @@ struct dflash_layer {
   int32_t* err = nullptr;
   bool profiling = false;
   std::vector<Pending> pending;
+  std::vector<hipEvent_t> event_pool;
   double ms[DFLASH_K_COUNT] = {};
   int64_t count[DFLASH_K_COUNT] = {};
 };
@@ -93,16 +94,24 @@ int validate_config(const dflash_config* c) {
   return DFLASH_OK;
 }
 
-void record(dflash_layer* L, int kernel, hipEvent_t* start, hipStream_t s) {
+hipEvent_t pooled_event(dflash_layer* L) {
+  if (!L->event_pool.empty()) {
+    hipEvent_t e = L->event_pool.back();
+    L->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  hipEventCreate(&e);
+  return e;
+}
+void record(dflash_layer* L, hipEvent_t* start, hipStream_t s) {
   if (!L->profiling) return;
-  hipEventCreate(start);
+  *start = pooled_event(L);
   hipEventRecord(*start, s);
-  (void)kernel;
 }
 void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s) {
   if (!L->profiling) return;
-  hipEvent_t stop;
-  hipEventCreate(&stop);
+  hipEvent_t stop = pooled_event(L);
   hipEventRecord(stop, s);
   L->pending.push_back({kernel, start, stop});
 }
@@ -174,6 +183,7 @@ void dflash_layer_destroy(dflash_layer* L) {
     hipEventDestroy(p.start);
     hipEventDestroy(p.stop);
   }
+  for (hipEvent_t e : L->event_pool) hipEventDestroy(e);
   hipFree(L->cos_sin);
   hipFree(L->err);
   delete L;
@@ -247,7 +257,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
     tiles += (int)((Mc + kGemmBM - 1) / kGemmBM) * ga.p[1].tiles_n;
   }
   hipEvent_t ev;
-  record(L, DFLASH_K_GEMM_QKV, &ev, s);
+  record(L, &ev, s);
   if (launch_gemm(c.dtype, true, ga, tiles, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_GEMM_QKV, ev, s);
 
@@ -267,7 +277,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   na.eps = (float)c.rms_eps;
   na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   na.seq = seq;
-  record(L, DFLASH_K_NORM_ROPE, &ev, s);
+  record(L, &ev, s);
   if (launch_norm_rope(c.dtype, d, na, B * nkv, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_NORM_ROPE, ev, s);
 
@@ -284,7 +294,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   aa.total_tiles = n_tiles;
   aa.G = (int32_t)attn_groups(L, n_tiles);
   aa.seq = seq;
-  record(L, DFLASH_K_ATTN, &ev, s);
+  record(L, &ev, s);
   if (launch_attn(c.dtype, d, aa, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_ATTN, ev, s);
 
@@ -303,7 +313,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   }
   if (split) {
     const int rows_per_group = 256 / (d / 4);
-    record(L, DFLASH_K_MERGE, &ev, s);
+    record(L, &ev, s);
     if (launch_merge(c.dtype, d, aa, (R + rows_per_group - 1) / rows_per_group, s) != hipSuccess)
       return DFLASH_ERR_HIP;
     record_end(L, DFLASH_K_MERGE, ev, s);
@@ -314,7 +324,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   std::memset(&go, 0, sizeof(go));
   go.nprob = 1;
   go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + kGemmBN - 1) / kGemmBN, 0};
-  record(L, DFLASH_K_GEMM_O, &ev, s);
+  record(L, &ev, s);
   if (launch_gemm(c.dtype, false, go, ((Mq + kGemmBM - 1) / kGemmBM) * go.p[0].tiles_n, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_GEMM_O, ev, s);
@@ -347,8 +357,8 @@ int dflash_layer_set_profiling(dflash_layer* L, int32_t enable) {
   if (!L) return DFLASH_ERR_ARG;
   if (hipDeviceSynchronize() != hipSuccess) return DFLASH_ERR_HIP;
   for (auto& p : L->pending) {
-    hipEventDestroy(p.start);
-    hipEventDestroy(p.stop);
+    L->event_pool.push_back(p.start);
+    L->event_pool.push_back(p.stop);
   }
   L->pending.clear();
   std::fill(L->ms, L->ms + DFLASH_K_COUNT, 0.0);
@@ -365,8 +375,8 @@ int dflash_layer_kernel_times(dflash_layer* L, double* ms, int64_t* count) {
     if (hipEventElapsedTime(&t, p.start, p.stop) != hipSuccess) return DFLASH_ERR_HIP;
     L->ms[p.kernel] += t;
     L->count[p.kernel] += 1;
-    hipEventDestroy(p.start);
-    hipEventDestroy(p.stop);
+    L->event_pool.push_back(p.start);
+    L->event_pool.push_back(p.stop);
   }
   L->pending.clear();
   for (int k = 0; k < DFLASH_K_COUNT; ++k) {
