@@ -3,7 +3,9 @@
 Every HIP source under ``csrc/`` is compiled with hipcc for gfx950 only and
 linked into one shared library next to this file. Packed fp32 VALU ops are
 turned off for the device code (``-packed-fp32-ops``); the host pass of hipcc
-warns that it does not know that feature, which is harmless.
+warns that it does not know that feature, which is harmless. MFMA results are
+kept in ordinary VGPRs (``-amdgpu-mfma-vgpr-form``) so that the online-softmax
+rescale of the accumulators needs no AGPR moves.
 
 Usage: ``python -m block_diffusion_draft_qkv_amd.build [--debug]``.
 """
@@ -35,6 +37,7 @@ def hipcc() -> str:
 def flags(debug: bool = False):
     f = ["-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wno-unused-command-line-argument"]
     f += ["-O1", "-g"] if debug else ["-O3"]
     return f

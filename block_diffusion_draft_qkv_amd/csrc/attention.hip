@@ -8,11 +8,24 @@
 // included, no causal mask), restricted under a window W to
 // |(T_b - bs + i) - t| < W; then o . V.
 //
-// Layout of the work. The bs*g query rows that share KV head j (row i*g + hh)
-// form one tile of up to 64 rows; wave w of the 256-thread work-group owns rows
-// 16w .. 16w+15. Keys stream in tiles of 64 through LDS, double-buffered, the
-// next tile's global loads in flight while the current one is used:
-//   S^T (keys x queries) = K . Q^T     on MFMA, K from LDS, Q held in VGPRs
+// Work split. The bs*g query rows that share KV head j (row i*g + hh) form one
+// tile of up to 64 rows; wave w of the 256-thread work-group owns rows
+// 16w .. 16w+15. Every (sequence b, KV head j) pair owns the key tiles
+// [lo_b, hi_b) (lo_b > 0 only under a sliding window); all tiles of all pairs
+// are flattened b-major and cut into G equal ranges, one per work-group, so
+// every work-group streams the same number of key tiles whatever the ragged
+// lengths. A range crosses pair boundaries; the part of a pair inside a range
+// is a segment. A segment that is a whole pair writes the output directly; a
+// pair cut by a range boundary leaves fp32 partials (un-normalised O, exponent
+// offset, sum) in slot 2w (the range's first segment) or 2w+1 (its last), which
+// HK4 merges.
+//
+// Pipeline. One continuous stream of LDS-DMA loads (gfx950
+// global_load_lds_dwordx4) runs through the whole range, crossing segment
+// boundaries without draining: each step brings one K tile, one V^T tile and,
+// when the step starts a segment, that pair's Q tile into an S-stage LDS ring
+// while the previous stage is used:
+//   S^T (keys x queries) = K . Q^T     on MFMA, K from LDS, Q in VGPRs
 //   online softmax in the log2 domain  (Q was pre-scaled by d^-1/2 log2 e)
 //   O^T (d x queries)   += V^T . P^T   on MFMA, V^T from LDS, P^T from VGPRs
 // The S^T accumulator gives every lane one query column and 4 keys per 16-key
@@ -21,13 +34,12 @@
 // plain row reads. For bf16 the key order inside a 32-key step is permuted
 // (block 2s row 4q+r <-> key 8q+r, block 2s+1 row 4q+r <-> key 8q+4+r) so a
 // lane's 8 P values are 8 consecutive keys, i.e. one 16-byte chunk of V^T.
-//
-// Split-KV: all (b, j, 64-key tile) items are flattened (b-major) and cut into
-// G equal ranges, one per work-group, so every work-group streams the same
-// number of key tiles whatever the ragged lengths. A work-group writes a pair
-// that lies wholly inside its range straight to the output; a pair cut by a
-// range boundary leaves fp32 partials (un-normalised O, running max, sum) in
-// slot 2w (the range's first segment) or 2w+1 (its last), which HK4 merges.
+// The exponent offset of a row is raised only when the row maximum passes it
+// by more than kRescaleSlack (log2 units), so O is rescaled rarely; the result
+// is exact for any offset because O and the sum share it.
+// Keys past T_b inside the last tile are masked out of the softmax; the append
+// kernel zero-fills V up to the next multiple of 64 keys, so those keys also
+// contribute exact zeros to P.V whatever the dead rows held.
 #include "kernels.h"
 
 namespace dflash {
@@ -35,47 +47,104 @@ namespace dflash {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.0f;
 
-// Sequence geometry shared by both kernels: per sequence, the first key tile
-// and the tile count; an exclusive prefix of the counts.
-struct SeqGeom {
-  int32_t lo[kMaxBatch];
-  int32_t cnt[kMaxBatch];
-  int64_t pre[kMaxBatch + 1];
+// Shapes of the attention kernel for element type T and head_dim D.
+template <typename T, int D> struct AttnShape {
+  static constexpr int KT = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // keys per tile
+  static constexpr int E = 16 / (int)sizeof(T);                      // elements per 16 B chunk
+  static constexpr int CPR = D * (int)sizeof(T) / 16;                // chunks per K or Q row
+  static constexpr int VCPR = KT * (int)sizeof(T) / 16;              // chunks per V^T row
+  static constexpr int NC = CPR / 4;                                 // reduction blocks over d
+  static constexpr int NKS = VCPR / 4;                               // reduction blocks over keys
+  static constexpr int KB = KT / 16;                                 // 16-key S^T blocks per tile
+  static constexpr int K_BYTES = KT * D * (int)sizeof(T);
+  static constexpr int TILE = 2 * K_BYTES;                           // K + V^T
+  static constexpr int KPW = K_BYTES / 4096, VPW = K_BYTES / 4096;   // 1 KB DMA blocks per wave
+  static constexpr int QROWS = 64 / CPR;                             // Q rows per 1 KB block
+  static constexpr int QPW = (kMaxQueryRows / QROWS + 3) / 4;        // Q DMA blocks per wave
+  static constexpr int QSLOT = QPW * 4 * 1024;
+  static constexpr int S = 3 * (TILE + QSLOT) <= 150 * 1024 ? 3 : 2; // ring depth
+  static constexpr int LDS = S * (TILE + QSLOT);
+  static constexpr int DB = D / 16;
+  static_assert(K_BYTES % 4096 == 0, "a tile must split into 1 KB blocks over 4 waves");
+  static_assert(sizeof(T) == 4 || KT % 32 == 0, "bf16 P packing pairs 16-key blocks");
 };
 
-__device__ inline void build_geom(const AttnArgs& a, SeqGeom& sg) {
-  const int B = a.seq.batch, tid = threadIdx.x;
-  for (int b = tid; b < kMaxBatch; b += blockDim.x) {
-    int lo = 0, cnt = 0;
-    if (b < B) {
-      const int T = a.seq.len[b] + (a.seq.ctx_off[b + 1] - a.seq.ctx_off[b]) + a.bs;
-      int first = 0;
-      if (a.window > 0) {
-        first = T - a.bs - a.window + 1;
-        if (first < 0) first = 0;
-      }
-      lo = first / kKeyTile;
-      cnt = (T + kKeyTile - 1) / kKeyTile - lo;
-    }
-    sg.lo[b] = lo;
-    sg.cnt[b] = cnt;
-    sg.pre[b + 1] = cnt;
+// Per-sequence key tiles [lo, lo + cnt) of the attention (uniform per wave).
+__device__ inline void seq_tiles(const AttnArgs& a, int b, int kt, int& lo, int& cnt) {
+  const int T = a.seq.len[b] + (a.seq.ctx_off[b + 1] - a.seq.ctx_off[b]) + a.bs;
+  int first = 0;
+  if (a.window > 0) {
+    first = T - a.bs - a.window + 1;
+    if (first < 0) first = 0;
   }
-  if (tid == 0) sg.pre[0] = 0;
-  __syncthreads();
-  // inclusive scan of pre[1..kMaxBatch] (Hillis-Steele)
-  for (int off = 1; off < kMaxBatch; off <<= 1) {
-    int64_t v = 0;
-    for (int b = tid; b < kMaxBatch; b += blockDim.x) {
-      if (b >= off) v = sg.pre[b + 1 - off];
-    }
-    __syncthreads();
-    for (int b = tid; b < kMaxBatch; b += blockDim.x) {
-      if (b >= off) sg.pre[b + 1] += v;
-    }
-    __syncthreads();
+  lo = first / kt;
+  cnt = (T + kt - 1) / kt - lo;
+}
+
+// Wave-level inclusive scan (64 lanes).
+__device__ inline int64_t wave_incl_scan(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
   }
+  return v;
+}
+
+// Exclusive prefix, over sequences, of the tile counts: pre[b] for one b,
+// computed by each wave in registers (lane l owns sequences 4l .. 4l+3).
+__device__ inline int64_t tiles_before(const AttnArgs& a, int kt, int b) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bb = 4 * lane + k;
+    if (bb < a.seq.batch && bb < b) {
+      int lo, cnt;
+      seq_tiles(a, bb, kt, lo, cnt);
+      s += cnt;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
+// The sequence b holding flat tile f (flat index = nkv * pre[b] + j * cnt_b +
+// tile offset), with pre[b]; every lane gets the same answer.
+__device__ inline int find_seq(const AttnArgs& a, int kt, int64_t f, int64_t& pre_b) {
+  const int lane = threadIdx.x & 63;
+  int cnt4[4];
+  int64_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bb = 4 * lane + k;
+    cnt4[k] = 0;
+    if (bb < a.seq.batch) {
+      int lo;
+      seq_tiles(a, bb, kt, lo, cnt4[k]);
+    }
+    tot += cnt4[k];
+  }
+  const int64_t incl = wave_incl_scan(tot);
+  int64_t run = incl - tot;
+  int hit_b = -1;
+  int64_t hit_pre = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (hit_b < 0 && cnt4[k] > 0 && a.nkv * run <= f && f < a.nkv * (run + cnt4[k])) {
+      hit_b = 4 * lane + k;
+      hit_pre = run;
+    }
+    run += cnt4[k];
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(hit_b >= 0);
+  const int src = (int)__builtin_ctzll(m);
+  pre_b = __shfl(hit_pre, src, 64);
+  return __shfl(hit_b, src, 64);
 }
 
 __device__ inline int64_t bound_of(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
@@ -88,33 +157,77 @@ template <> __device__ inline int key_of<__bf16>(int kb, int m) {
 }
 template <> __device__ inline int key_of<float>(int kb, int m) { return 16 * kb + m; }
 
-// LDS chunk swizzle of a K tile row: keeps the 8 rows read by one ds_read_b128
-// phase on 8 distinct chunks.
-template <typename T> __device__ inline int kswz(int row);
-template <> __device__ inline int kswz<__bf16>(int row) { return (row & 3) | ((row >> 1) & 4); }
-template <> __device__ inline int kswz<float>(int row) { return row & 7; }
-
-// Zero the elements of a 16-byte chunk whose key index (first + e) is >= end.
-template <typename T> __device__ inline u32x4 mask_tail(u32x4 v, int first, int end);
-template <> __device__ inline u32x4 mask_tail<float>(u32x4 v, int first, int end) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (first + e >= end) v[e] = 0u;
-  return v;
+// LDS chunk swizzles. A ds_read_b128 of an MFMA operand reads 16 rows (lane %
+// 16) at one logical chunk; the chunk is stored at logical ^ swz(row), chosen
+// so those 16 reads hit distinct 16-byte bank groups whether the hardware
+// serves 8 or 16 lanes per pass. For K the 16 rows are key_of(kb, 0..15) and
+// the swizzle depends only on the lane; V^T and Q reads take 16 consecutive
+// rows, and their swizzle depends only on the row's low four bits.
+template <typename T, int CPR> __device__ inline int kswz(int row) {
+  if constexpr (sizeof(T) == 4) return row & 15;
+  else if constexpr (CPR == 16) return (row & 3) | ((row >> 1) & 12);
+  else return (((row >> 1) & 1) | ((row >> 2) & 6)) ^ ((row & 1) << 2);
 }
-template <> __device__ inline u32x4 mask_tail<__bf16>(u32x4 v, int first, int end) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t keep = 0u;
-    if (first + 2 * w < end) keep |= 0x0000FFFFu;
-    if (first + 2 * w + 1 < end) keep |= 0xFFFF0000u;
-    v[w] &= keep;
-  }
-  return v;
+template <int CPR> __device__ inline int rswz(int row) {
+  if constexpr (CPR >= 16) return row & 15;
+  else if constexpr (CPR == 8) return (row & 7) ^ ((row >> 3) & 1);
+  else return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
-template <typename T> __device__ inline u32x4 pack_p(const float* p0, const float* p1);
-template <> __device__ inline u32x4 pack_p<__bf16>(const float* p0, const float* p1) {
+// One 16-byte-per-lane LDS-DMA load: each lane fetches sbase + voff and the
+// wave's 64 chunks land at LDS bytes lds .. lds + 1023 (lane l at 16 l). It is
+// issued as inline assembly so that the compiler's own wait counting never
+// drains the ring on it (its waits can then only be more conservative, never
+// short); completion is awaited explicitly with vm_wait.
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Work-group barrier without the memory fence of __syncthreads (which would
+// drain every outstanding load): the waits it needs are issued explicitly, and
+// the empty asm statements keep the compiler from moving LDS accesses across.
+__device__ inline void block_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]); N is one of the
+// three DMA group sizes a step can leave in flight.
+template <int KVW, int QW> __device__ inline void vm_wait(int n) {
+#define DFLASH_VMWAIT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
+  if (n == KVW + QW) DFLASH_VMWAIT(KVW + QW);
+  else if (n == KVW) DFLASH_VMWAIT(KVW);
+  else DFLASH_VMWAIT(0);
+#undef DFLASH_VMWAIT
+}
+
+// Max / sum over the four lanes that hold one query row (l, l^16, l^32, l^48).
+__device__ inline float max4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline u32x4 pack_p_bf16(const f32x4& p0, const f32x4& p1) {
   bf16x8 v;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -124,117 +237,192 @@ template <> __device__ inline u32x4 pack_p<__bf16>(const float* p0, const float*
   return __builtin_bit_cast(u32x4, v);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void attn_splitkv_kernel(AttnArgs a) {
-  constexpr int E = Elem<T>::kPerChunk;
-  constexpr int CPR = D * (int)sizeof(T) / 16;         // chunks per K row
-  constexpr int VCPR = kKeyTile * (int)sizeof(T) / 16; // chunks per V^T row
-  constexpr int NC = CPR / 4;                          // reduction blocks over d
-  constexpr int K_CH = kKeyTile * CPR, V_CH = D * VCPR;
-  constexpr int KPT = K_CH / 256, VPT = V_CH / 256;
-  constexpr int DB = D / 16;
-  static_assert(K_CH % 256 == 0 && V_CH % 256 == 0, "tile must split over 256 threads");
-  __shared__ u32x4 lds[2][K_CH + V_CH];
-  __shared__ SeqGeom sg;
+__device__ inline u32x4 lds_read16(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)byte_addr;
+}
 
-  build_geom(a, sg);
+// Position in the flattened work: pair (b, j), key tile, the pair's tiles.
+struct Cursor {
+  int b, j, tile, lo, hi;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
+  using Sh = AttnShape<T, D>;
+  constexpr int KT = Sh::KT, E = Sh::E, CPR = Sh::CPR, VCPR = Sh::VCPR, NC = Sh::NC, NKS = Sh::NKS;
+  constexpr int KB = Sh::KB, DB = Sh::DB, S = Sh::S, TILE = Sh::TILE, K_BYTES = Sh::K_BYTES;
+  constexpr int KPW = Sh::KPW, VPW = Sh::VPW, QPW = Sh::QPW, QSLOT = Sh::QSLOT;
+  constexpr int KVW = KPW + VPW;
+  __shared__ u32x4 lds[Sh::LDS / 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int nkv = a.nkv, g = a.nq / nkv, R = a.R;
   const int64_t N = a.total_tiles, G = a.G, w = blockIdx.x;
   const int64_t f0 = bound_of(w, N, G), f1 = bound_of(w + 1, N, G);
+  const int total = (int)(f1 - f0);
   const bool active = wave * 16 < R;
   const int qrow = wave * 16 + r16;
   const bool qvalid = qrow < R;
-  const T* __restrict__ Qp = static_cast<const T*>(a.q);
-  const T* __restrict__ Kc = static_cast<const T*>(a.kc);
-  const T* __restrict__ Vc = static_cast<const T*>(a.vc);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  const uint32_t qlds0 = lds0 + S * TILE;
+  const char* Kc = static_cast<const char*>(a.kc);
+  const char* Vc = static_cast<const char*>(a.vc);
+  const char* Qp = static_cast<const char*>(a.q);
 
-  int64_t f = f0;
-  bool first_seg = true;
-  while (f < f1) {
-    // locate the pair holding flat tile f
-    int lo = 0, hi = a.seq.batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)nkv * sg.pre[mid] <= f) lo = mid; else hi = mid;
+  // Per-lane byte offsets, fixed for the whole kernel.
+  // LDS reads: K operand of block kb, chunk c = koff[c] + kb_off(kb); V^T
+  // operand of d-block db, key chunk ks = voff[ks] + db_off(db); Q row chunks.
+  uint32_t koff[NC], voff[NKS], qoff[NC];
+  {
+    const int krow = key_of<T>(0, r16), ksw = kswz<T, CPR>(krow);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) koff[c] = (uint32_t)(krow * CPR + ((4 * c + q) ^ ksw)) * 16u;
+    const int vsw = rswz<VCPR>(r16);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) voff[ks] = (uint32_t)(r16 * VCPR + ((4 * ks + q) ^ vsw)) * 16u + K_BYTES;
+    const int qsw = rswz<CPR>(qrow);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qoff[c] = (uint32_t)(qrow * CPR + ((4 * c + q) ^ qsw)) * 16u;
+  }
+  // DMA sources relative to a tile's (or Q tile's) first row: 1 KB block i of
+  // this wave; each lane fetches the chunk that belongs at its swizzled LDS
+  // position.
+  uint32_t kdma[KPW], vdma[VPW], qdma[QPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int blk = i * 4 + wave_u, row = blk * (64 / CPR) + lane / CPR;
+    const int c = (lane % CPR) ^ kswz<T, CPR>(row);
+    kdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int blk = i * 4 + wave_u, row = blk * (64 / VCPR) + lane / VCPR;
+    const int c = (lane % VCPR) ^ rswz<VCPR>(row);
+    vdma[i] = (uint32_t)(row * a.cap + c * E) * (uint32_t)sizeof(T);
+  }
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int blk = i * 4 + wave_u, row = blk * (64 / CPR) + lane / CPR;
+    const int c = (lane % CPR) ^ rswz<CPR>(row);
+    qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
+  }
+
+  // Both cursors start at flat tile f0.
+  Cursor ic;
+  {
+    int64_t pre_b;
+    ic.b = __builtin_amdgcn_readfirstlane(find_seq(a, KT, f0, pre_b));
+    pre_b = ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pre_b >> 32)) << 32) |
+            __builtin_amdgcn_readfirstlane((uint32_t)pre_b);
+    int lo, cnt;
+    seq_tiles(a, ic.b, KT, lo, cnt);
+    const int64_t off = f0 - (int64_t)nkv * pre_b;
+    ic.j = (int)(off / cnt);
+    ic.tile = lo + (int)(off % cnt);
+    ic.lo = lo;
+    ic.hi = lo + cnt;
+  }
+  Cursor cc = ic;
+  auto advance = [&](Cursor& c) {
+    if (++c.tile == c.hi) {
+      if (++c.j == nkv) {
+        c.j = 0;
+        ++c.b;
+        int lo, cnt;
+        seq_tiles(a, c.b, KT, lo, cnt);
+        c.lo = lo;
+        c.hi = lo + cnt;
+      }
+      c.tile = c.lo;
     }
-    const int b = lo;
-    const int cnt = sg.cnt[b];
-    const int64_t base_b = (int64_t)nkv * sg.pre[b];
-    const int j = (int)((f - base_b) / cnt);
-    const int tin = (int)((f - base_b) % cnt);
-    const int64_t pair_end = base_b + (int64_t)(j + 1) * cnt;
-    const int64_t seg_end = f1 < pair_end ? f1 : pair_end;
-    const int ntiles = (int)(seg_end - f);
-    const bool full = tin == 0 && seg_end == pair_end;
-    const int slot = 2 * (int)w + (first_seg ? 0 : 1);
-    const int tile0 = sg.lo[b] + tin;
+  };
 
-    const int Tb = a.seq.len[b] + (a.seq.ctx_off[b + 1] - a.seq.ctx_off[b]) + a.bs;
-    const size_t pair = (size_t)b * nkv + j;
-    const T* Kpair = Kc + pair * (size_t)a.cap * D;
-    const T* Vpair = Vc + pair * (size_t)D * a.cap;
-    const int qpos = Tb - a.bs + (qvalid ? qrow / g : 0);
+  // Issue step n (its tile is at cursor ic; the Q tile too if a segment starts
+  // there) and return the number of DMA blocks this wave issued for it.
+  int iseg = 0;
+  auto issue = [&](int n) -> int {
+    const size_t pair = (size_t)ic.b * nkv + ic.j;
+    int blocks = KVW;
+    if (n == 0 || ic.tile == ic.lo) {
+      const uint32_t qs = qlds0 + (uint32_t)(iseg % S) * QSLOT;
+      const void* qsrc = uniform_ptr(Qp + pair * R * D * sizeof(T));
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) lds_dma16(qdma[i], qsrc, qs + (uint32_t)(i * 4 + wave_u) * 1024u);
+      ++iseg;
+      blocks += QPW;
+    }
+    const uint32_t sl = lds0 + (uint32_t)(n % S) * TILE;
+    const void* kt = uniform_ptr(Kc + (pair * a.cap + (size_t)ic.tile * KT) * D * sizeof(T));
+    const void* vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)ic.tile * KT) * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) lds_dma16(kdma[i], kt, sl + (uint32_t)(i * 4 + wave_u) * 1024u);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) lds_dma16(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * 4 + wave_u) * 1024u);
+    advance(ic);
+    return blocks;
+  };
 
-    u32x4 qf[NC];
+  // Prologue: steps 0 .. S-2 in flight. `pending` holds the DMA blocks of the
+  // steps issued after the one the loop waits for next.
+  int sizes[S - 1];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qf[c] = qvalid ? ldg16(Qp + (pair * R + qrow) * D + (size_t)(4 * c + q) * E) : u32x4{0, 0, 0, 0};
+  for (int n = 0; n < S - 1; ++n) sizes[n] = n < total ? issue(n) : 0;
+  int pending = S >= 3 ? sizes[S - 2] : 0;
 
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 acc[DB];
+  u32x4 qf[NC];
+  int cseg = 0;
+  int seg_start_flat = 0;       // step index where the current segment began
+  bool seg_from_lo = false;     // the segment starts at the pair's first tile
+  int tb = 0, qpos = 0;
 
-    u32x4 rk[KPT], rv[VPT];
-    auto load_regs = [&](int tile) {
-      const int t0 = tile * kKeyTile;
+  for (int it = 0; it < total; ++it) {
+    vm_wait<KVW, QPW>(pending);
+    block_barrier();
+    int next = 0;
+    if (it + S - 1 < total) next = issue(it + S - 1);
+    pending = S >= 3 ? next : 0;
+
+    const bool seg_begin = it == 0 || cc.tile == cc.lo;
+    const bool seg_end = it + 1 == total || cc.tile + 1 == cc.hi;
+    if (seg_begin) {
+      seg_start_flat = it;
+      seg_from_lo = cc.tile == cc.lo;
+      tb = a.seq.len[cc.b] + (a.seq.ctx_off[cc.b + 1] - a.seq.ctx_off[cc.b]) + a.bs;
+      qpos = tb - a.bs + (qvalid ? qrow / g : 0);
+      if (active) {
+        const uint32_t qs = qlds0 + (uint32_t)(cseg % S) * QSLOT;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int id = tid + 256 * i, row = id / CPR, c = id % CPR;
-        rk[i] = ldg16(Kpair + (size_t)(t0 + row) * D + c * E);
+        for (int c = 0; c < NC; ++c) qf[c] = qvalid ? lds_read16(qs + qoff[c]) : u32x4{0, 0, 0, 0};
       }
+      ++cseg;
+      m_run = kNegInf;
+      l_run = 0.f;
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int id = tid + 256 * i, row = id / VCPR, c = id % VCPR;
-        rv[i] = ldg16(Vpair + (size_t)row * a.cap + t0 + c * E);
-      }
-    };
-    auto store_lds = [&](int buf, int tile) {
-      const int t0 = tile * kKeyTile;
-      const bool tail = t0 + kKeyTile > Tb;
+      for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (active) {
+      const uint32_t sl = lds0 + (uint32_t)(it % S) * TILE;
+      const int t0 = cc.tile * KT;
+      f32x4 s[KB];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int id = tid + 256 * i, row = id / CPR, c = id % CPR;
-        lds[buf][row * CPR + (c ^ kswz<T>(row))] = rk[i];
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int id = tid + 256 * i, row = id / VCPR, c = id % VCPR;
-        const u32x4 v = tail ? mask_tail<T>(rv[i], t0 + c * E, Tb) : rv[i];
-        lds[buf][K_CH + row * VCPR + (c ^ (row & 7))] = v;
-      }
-    };
-    auto compute = [&](int buf, int tile) {
-      const int t0 = tile * kKeyTile;
-      f32x4 s[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int krow = key_of<T>(kb, r16);
+        const uint32_t kbo = (uint32_t)(key_of<T>(kb, 0) * CPR * 16);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          Mfma<T>::chunk(s[kb], lds[buf][krow * CPR + ((4 * c + q) ^ kswz<T>(krow))], qf[c]);
+        for (int c = 0; c < NC; ++c) Mfma<T>::chunk(s[kb], lds_read16(sl + koff[c] + kbo), qf[c]);
       }
-      if (t0 + kKeyTile > Tb || a.window > 0) {
+      if (t0 + KT > tb || a.window > 0) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = t0 + key_of<T>(kb, 4 * q + r);
-            bool ok = key < Tb;
+            bool ok = key < tb;
             if (a.window > 0) {
               const int dlt = qpos - key;
               ok = ok && (dlt < a.window) && (-dlt < a.window);
@@ -244,90 +432,77 @@ __global__ __launch_bounds__(256, 2) void attn_splitkv_kernel(AttnArgs a) {
       }
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
+        mx = fmaxf(fmaxf(fmaxf(mx, s[kb][0]), fmaxf(s[kb][1], s[kb][2])), s[kb][3]);
+      mx = max4(mx);
+      // Raise the exponent offset only when this row's maximum passed it by
+      // more than the slack; the (rare) rescale is wave-uniform.
+      const bool raise = mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      float p[4][4];
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      f32x4 p[KB];
       float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           p[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
           psum += p[kb][r];
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      l_run += psum;
       if constexpr (sizeof(T) == 2) {
-        u32x4 pf[2];
-        pf[0] = pack_p<T>(p[0], p[1]);
-        pf[1] = pack_p<T>(p[2], p[3]);
+        u32x4 pf[NKS];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int vrow = db * 16 + r16;
+        for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack_p_bf16(p[2 * ks], p[2 * ks + 1]);
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            Mfma<T>::chunk(acc[db], lds[buf][K_CH + vrow * VCPR + ((4 * ks + q) ^ (vrow & 7))], pf[ks]);
-        }
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            Mfma<T>::chunk(acc[db], lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16)), pf[ks]);
       } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int vrow = db * 16 + r16;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const u32x4 pb = u32x4{__float_as_uint(p[kb][0]), __float_as_uint(p[kb][1]),
-                                   __float_as_uint(p[kb][2]), __float_as_uint(p[kb][3])};
-            Mfma<T>::chunk(acc[db], lds[buf][K_CH + vrow * VCPR + ((4 * kb + q) ^ (vrow & 7))], pb);
-          }
-        }
+          for (int ks = 0; ks < NKS; ++ks)
+            Mfma<T>::chunk(acc[db], lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16)),
+                           __builtin_bit_cast(u32x4, p[ks]));
       }
-    };
 
-    load_regs(tile0);
-    store_lds(0, tile0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1;
-      const bool more = it + 1 < ntiles;
-      if (more) load_regs(tile0 + it + 1);
-      if (active) compute(cur, tile0 + it);
-      if (more) store_lds(cur ^ 1, tile0 + it + 1);
-      __syncthreads();
-    }
-
-    if (active) {
-      float lt = l_run + shfl_xor(l_run, 16);
-      lt += shfl_xor(lt, 32);
-      if (qvalid) {
-        if (full) {
-          const float inv = 1.0f / lt;
-          const int i = qrow / g, hh = qrow % g;
-          T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.bs + i) * a.nq + (size_t)(j * g + hh)) * D;
+      if (seg_end) {
+        const float lt = sum4(l_run);
+        const bool full = seg_from_lo && cc.tile + 1 == cc.hi;
+        if (qvalid) {
+          if (full) {
+            const float inv = 1.0f / lt;
+            const int i = qrow / g, hh = qrow % g;
+            T* orow = static_cast<T*>(a.o) +
+                      ((size_t)(cc.b * a.bs + i) * a.nq + (size_t)(cc.j * g + hh)) * D;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) orow[db * 16 + 4 * q + r] = Elem<T>::from_f32(acc[db][r] * inv);
-        } else {
-          float* po = a.part_o + ((size_t)slot * kMaxQueryRows + qrow) * D;
+              for (int r = 0; r < 4; ++r) orow[db * 16 + 4 * q + r] = Elem<T>::from_f32(acc[db][r] * inv);
+          } else {
+            const int slot = 2 * (int)w + (seg_start_flat == 0 ? 0 : 1);
+            float* po = a.part_o + ((size_t)slot * kMaxQueryRows + qrow) * D;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * q) = acc[db];
-          if (q == 0) {
-            float* pm = a.part_ml + ((size_t)slot * kMaxQueryRows + qrow) * 2;
-            pm[0] = m_run;
-            pm[1] = lt;
+            for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * q) = acc[db];
+            if (q == 0) {
+              float* pm = a.part_ml + ((size_t)slot * kMaxQueryRows + qrow) * 2;
+              pm[0] = m_run;
+              pm[1] = lt;
+            }
           }
         }
       }
     }
-    f = seg_end;
-    first_seg = false;
+    advance(cc);
   }
 }
 
@@ -335,13 +510,13 @@ __global__ __launch_bounds__(256, 2) void attn_splitkv_kernel(AttnArgs a) {
 // work-group return at once.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rows_per_group) {
-  __shared__ SeqGeom sg;
-  build_geom(a, sg);
+  using Sh = AttnShape<T, D>;
   const int nkv = a.nkv, g = a.nq / nkv;
   const int b = blockIdx.x / nkv, j = blockIdx.x % nkv;
   const int64_t N = a.total_tiles, G = a.G;
-  const int cnt = sg.cnt[b];
-  const int64_t s_p = (int64_t)nkv * sg.pre[b] + (int64_t)j * cnt, e_p = s_p + cnt;
+  int lo, cnt;
+  seq_tiles(a, b, Sh::KT, lo, cnt);
+  const int64_t s_p = (int64_t)nkv * tiles_before(a, Sh::KT, b) + (int64_t)j * cnt, e_p = s_p + cnt;
   const int64_t w_first = owner_of(s_p, N, G), w_last = owner_of(e_p - 1, N, G);
   if (w_first == w_last) return;
 
@@ -372,7 +547,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rows_pe
   for (int r = 0; r < 4; ++r) orow[d4 + r] = Elem<T>::from_f32(num[r] * inv);
 }
 
+template <typename T, int D> int wgs_per_cu() { return (160 * 1024) / AttnShape<T, D>::LDS; }
+
 }  // namespace
+
+int attn_wgs_per_cu(int dtype, int head_dim) {
+  if (dtype == 1) return head_dim == 128 ? wgs_per_cu<__bf16, 128>() : wgs_per_cu<__bf16, 64>();
+  return head_dim == 128 ? wgs_per_cu<float, 128>() : wgs_per_cu<float, 64>();
+}
+
+int attn_key_tile(int dtype, int head_dim) {
+  if (dtype == 1) return head_dim == 128 ? AttnShape<__bf16, 128>::KT : AttnShape<__bf16, 64>::KT;
+  return head_dim == 128 ? AttnShape<float, 128>::KT : AttnShape<float, 64>::KT;
+}
 
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream) {
   if (args.G <= 0) return hipSuccess;

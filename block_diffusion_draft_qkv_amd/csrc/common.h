@@ -26,7 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxBatch = 256;
-constexpr int kKeyTile = 64;       // keys per attention tile
+constexpr int kKeyTile = 64;       // cache capacity granule; V is zero-padded to it
 constexpr int kMaxQueryRows = 64;  // block_size * (n_q / n_kv) rows per KV head
 
 // Per-sequence lengths of one step, passed to kernels by value.

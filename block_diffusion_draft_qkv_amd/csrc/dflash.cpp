@@ -56,10 +56,10 @@ namespace {
 
 int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
-// Attention work-groups for N flat tiles: two per CU (the kernel's LDS budget
-// allows two resident), never more than there are tiles.
+// Attention work-groups for N flat tiles: as many as the CUs hold at once
+// (the kernel's LDS ring bounds that), never more than there are tiles.
 int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
-  const int64_t cap = 2 * (int64_t)L->num_cus;
+  const int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
   return std::max<int64_t>(1, std::min<int64_t>(cap, n_tiles));
 }
 
@@ -67,12 +67,13 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   const dflash_config& c = L->cfg;
   const int64_t d = c.head_dim, g = c.n_q_heads / c.n_kv_heads;
   const int64_t mq = batch * c.block_size, es = elem_size(c);
-  const int64_t gmax = 2 * (int64_t)L->num_cus;
+  const int64_t gmax = (int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim);
   Carve w{};
   size_t off = 0;
   w.qkv = off;     off += align_up(mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
   w.ctxkv = off;   off += align_up(std::max<int64_t>(total_ctx, 1) * 2 * c.n_kv_heads * d * 4);
-  w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es);
+  // The attention kernel fetches whole 64-row query tiles: slack past the end.
+  w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es + kMaxQueryRows * d * 4);
   w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
   w.part_o = off;  off += align_up(2 * gmax * kMaxQueryRows * d * 4);
   w.part_ml = off; off += align_up(2 * gmax * kMaxQueryRows * 2 * 4);
@@ -208,6 +209,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   const int bs = c.block_size, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int g = nq / nkv, R = bs * g;
 
+  const int64_t kt = attn_key_tile(c.dtype, d);
   SeqTable seq;
   std::memset(&seq, 0, sizeof(seq));
   seq.batch = B;
@@ -222,7 +224,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
     seq.ctx_off[b] = ctx_offsets[b];
     int64_t first = 0;
     if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
-    n_tiles += nkv * ((T + kKeyTile - 1) / kKeyTile - first / kKeyTile);
+    n_tiles += nkv * ((T + kt - 1) / kt - first / kt);
   }
   seq.ctx_off[B] = ctx_offsets[B];
   const int64_t Mc = ctx_offsets[B];
@@ -306,7 +308,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
       const int64_t T = (int64_t)seq.len[b] + (seq.ctx_off[b + 1] - seq.ctx_off[b]) + bs;
       int64_t first = 0;
       if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
-      const int64_t cnt = (T + kKeyTile - 1) / kKeyTile - first / kKeyTile;
+      const int64_t cnt = (T + kt - 1) / kt - first / kt;
       for (int j = 0; j < nkv && !split; ++j, f += cnt)
         split = part_owner(f, n_tiles, aa.G) != part_owner(f + cnt - 1, n_tiles, aa.G);
     }

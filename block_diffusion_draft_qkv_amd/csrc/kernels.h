@@ -66,6 +66,10 @@ struct AttnArgs {
   SeqTable seq;
 };
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream);
+// Attention work-groups one CU holds at once (bounded by the kernel's LDS ring)
+// and the keys per attention tile.
+int attn_wgs_per_cu(int dtype, int head_dim);
+int attn_key_tile(int dtype, int head_dim);
 hipError_t launch_merge(int dtype, int head_dim, const AttnArgs& args, int merge_groups,
                         hipStream_t stream);
 

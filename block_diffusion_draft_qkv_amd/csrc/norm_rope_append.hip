@@ -7,7 +7,8 @@
 //     cache K row L_b + r ("DFlash源码导读（二）" sections 1-4: k_norm before
 //     RoPE, keys over the whole window, cache update);
 //   * stores the raw value rows transposed into cache V (column L_b + r), via
-//     an LDS tile so that global writes run along the key axis;
+//     an LDS tile so that global writes run along the key axis, and zeroes V
+//     columns T_b .. (T_b rounded up to 64) - 1;
 //   * normalises (q_norm) and rotates the g = nq/nkv query heads of KV head j
 //     for every block token i at the window's suffix position n_b + i (NeMo
 //     page "draft_qwen3", apply_rotary_pos_emb), scales them by
@@ -129,6 +130,16 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a) {
       vdst[(size_t)dd * a.cap + r0 + rr] = Elem<T>::from_f32(vt[dd][rr]);
     }
     __syncthreads();
+  }
+
+  // Zero V from T_b to the end of its 64-key tile: the attention kernel reads
+  // whole tiles and needs finite values past T_b (they meet zero weights).
+  T* vpad = static_cast<T*>(a.vc) + pair * D * a.cap;
+  const int Tb = L + nnew;
+  const int pad = (Tb + 63) / 64 * 64 - Tb;
+  for (int idx = tid; idx < D * pad; idx += 256) {
+    const int dd = idx / pad, k = idx % pad;
+    vpad[(size_t)dd * a.cap + Tb + k] = Elem<T>::from_f32(0.f);
   }
 }
 

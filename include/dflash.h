@@ -97,7 +97,7 @@ typedef struct {
  *   len: HOST array [batch], the valid rows of each sequence; it is the
  *        authoritative length (kernels receive it by value).
  * K holds post-norm, post-RoPE keys; V holds raw values. Rows at or past len
- * are dead: never read into a result, never zeroed.
+ * are dead: they never contribute to a result.
  * capacity must be a positive multiple of 64. */
 typedef struct {
     void* k;
@@ -146,7 +146,9 @@ size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
  *                  latch DFLASH_ERR_RANGE for dflash_layer_poll_error.
  *   cache          rows [len_b, len_b + n_b + bs) of each sequence receive the
  *                  new context rows then the block rows; len_b then becomes
- *                  T_b = len_b + n_b + bs.
+ *                  T_b = len_b + n_b + bs. V columns from T_b up to the next
+ *                  multiple of 64 (dead rows) are set to zero; nothing else
+ *                  in the cache is written.
  *   out            device [B * bs, H]: o_proj of the attention output.
  *   workspace      device scratch of at least dflash_workspace_bytes(...)
  *                  bytes, 256-byte aligned; contents need no initialisation.
