@@ -41,6 +41,7 @@
 // kernel zero-fills V up to the next multiple of 64 keys, so those keys also
 // contribute exact zeros to P.V whatever the dead rows held.
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace dflash {
 
@@ -162,55 +163,18 @@ template <> __device__ inline int key_of<float>(int kb, int m) { return 16 * kb 
 // so those 16 reads hit distinct 16-byte bank groups whether the hardware
 // serves 8 or 16 lanes per pass. For K the 16 rows are key_of(kb, 0..15) and
 // the swizzle depends only on the lane; V^T and Q reads take 16 consecutive
-// rows, and their swizzle depends only on the row's low four bits.
+// rows and use rswz (lds_dma.h).
 template <typename T, int CPR> __device__ inline int kswz(int row) {
   if constexpr (sizeof(T) == 4) return row & 15;
   else if constexpr (CPR == 16) return (row & 3) | ((row >> 1) & 12);
   else return (((row >> 1) & 1) | ((row >> 2) & 6)) ^ ((row & 1) << 2);
 }
-template <int CPR> __device__ inline int rswz(int row) {
-  if constexpr (CPR >= 16) return row & 15;
-  else if constexpr (CPR == 8) return (row & 7) ^ ((row >> 3) & 1);
-  else return ((row >> 1) ^ (row >> 2)) & 3;
-}
-
-// One 16-byte-per-lane LDS-DMA load: each lane fetches sbase + voff and the
-// wave's 64 chunks land at LDS bytes lds .. lds + 1023 (lane l at 16 l). It is
-// issued as inline assembly so that the compiler's own wait counting never
-// drains the ring on it (its waits can then only be more conservative, never
-// short); completion is awaited explicitly with vm_wait.
-__device__ inline const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(((uint64_t)hi << 32) | lo);
-}
-__device__ inline void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-
-// Work-group barrier without the memory fence of __syncthreads (which would
-// drain every outstanding load): the waits it needs are issued explicitly, and
-// the empty asm statements keep the compiler from moving LDS accesses across.
-__device__ inline void block_barrier() {
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left alone (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]); N is one of the
-// three DMA group sizes a step can leave in flight.
+// Wait until at most n DMA blocks are outstanding, n being one of the three
+// group sizes a step can leave in flight.
 template <int KVW, int QW> __device__ inline void vm_wait(int n) {
-#define DFLASH_VMWAIT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
   if (n == KVW + QW) DFLASH_VMWAIT(KVW + QW);
   else if (n == KVW) DFLASH_VMWAIT(KVW);
   else DFLASH_VMWAIT(0);
-#undef DFLASH_VMWAIT
 }
 
 // Max / sum over the four lanes that hold one query row (l, l^16, l^32, l^48).
@@ -237,10 +201,6 @@ __device__ inline u32x4 pack_p_bf16(const f32x4& p0, const f32x4& p1) {
   return __builtin_bit_cast(u32x4, v);
 }
 
-__device__ inline u32x4 lds_read16(uint32_t byte_addr) {
-  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)byte_addr;
-}
-
 // Position in the flattened work: pair (b, j), key tile, the pair's tiles.
 struct Cursor {
   int b, j, tile, lo, hi;
@@ -265,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
   const int qrow = wave * 16 + r16;
   const bool qvalid = qrow < R;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  const uint32_t lds0 = lds_base(lds);
   const uint32_t qlds0 = lds0 + S * TILE;
   const char* Kc = static_cast<const char*>(a.kc);
   const char* Vc = static_cast<const char*>(a.vc);

@@ -24,6 +24,7 @@ using namespace dflash;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxKSlices = 4;  // k splits of the projection GEMM for small M
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Pending {
@@ -70,8 +71,8 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   const int64_t gmax = (int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim);
   Carve w{};
   size_t off = 0;
-  w.qkv = off;     off += align_up(mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
-  w.ctxkv = off;   off += align_up(std::max<int64_t>(total_ctx, 1) * 2 * c.n_kv_heads * d * 4);
+  w.qkv = off;     off += align_up(kMaxKSlices * mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
+  w.ctxkv = off;   off += align_up(kMaxKSlices * std::max<int64_t>(total_ctx, 1) * 2 * c.n_kv_heads * d * 4);
   // The attention kernel fetches whole 64-row query tiles: slack past the end.
   w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es + kMaxQueryRows * d * 4);
   w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
@@ -79,6 +80,31 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   w.part_ml = off; off += align_up(2 * gmax * kMaxQueryRows * 2 * 4);
   w.total = off;
   return w;
+}
+
+// Tile shape of a projection launch (one or two problems of m x n outputs):
+// the largest tiles that still give about one work-group per CU; problems too
+// small for that use 64 x 64 tiles and, when fp32 partial sums are allowed,
+// split k so that the launch still covers the CUs.
+struct TileChoice {
+  int bm, bn, tiles, kslices;
+};
+TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, bool allow_split) {
+  static const int cand[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
+  const int target = L->num_cus * 3 / 4;
+  auto count = [&](int bm, int bn) {
+    int t = ((m0 + bm - 1) / bm) * ((n0 + bn - 1) / bn);
+    if (m1 > 0) t += ((m1 + bm - 1) / bm) * ((n1 + bn - 1) / bn);
+    return t;
+  };
+  for (const auto& c : cand) {
+    const int t = count(c[0], c[1]);
+    if (t >= target) return {c[0], c[1], t, 1};
+  }
+  const int t = count(64, 64);
+  int ks = 1;
+  if (allow_split) ks = std::min(kMaxKSlices, std::max(1, (L->num_cus + t - 1) / t));
+  return {64, 64, t, ks};
 }
 
 int validate_config(const dflash_config* c) {
@@ -245,28 +271,32 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   const int Nqkv = (nq + 2 * nkv) * d, Nkv = 2 * nkv * d;
 
   // HK1: block q|k|v and context k|v in one launch.
+  const TileChoice tq = choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.nprob = 1;
   ga.p[0] = {hidden_states, L->w.w_qkv, qkv, Mq, Nqkv, H, H, H, Nqkv,
-             (Nqkv + kGemmBN - 1) / kGemmBN, 0};
-  int tiles = ((Mq + kGemmBM - 1) / kGemmBM) * ga.p[0].tiles_n;
+             (Nqkv + tq.bn - 1) / tq.bn, 0, (int64_t)Mq * Nqkv};
   if (Mc > 0) {
     const char* wkv = static_cast<const char*>(L->w.w_qkv) + (size_t)nq * d * H * es;
     ga.p[1] = {target_hidden, wkv, ctxkv, (int32_t)Mc, Nkv, H, H, H, Nkv,
-               (Nkv + kGemmBN - 1) / kGemmBN, tiles};
+               (Nkv + tq.bn - 1) / tq.bn, ((Mq + tq.bm - 1) / tq.bm) * ga.p[0].tiles_n,
+               (int64_t)Mc * Nkv};
     ga.nprob = 2;
-    tiles += (int)((Mc + kGemmBM - 1) / kGemmBM) * ga.p[1].tiles_n;
   }
   hipEvent_t ev;
   record(L, &ev, s);
-  if (launch_gemm(c.dtype, true, ga, tiles, s) != hipSuccess) return DFLASH_ERR_HIP;
+  if (launch_gemm(c.dtype, true, ga, tq.tiles, tq.bm, tq.bn, tq.kslices, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_GEMM_QKV, ev, s);
 
   // HK2
   NormRopeArgs na;
   na.qkv = qkv;
   na.ctxkv = ctxkv;
+  na.qkv_slice = (int64_t)Mq * Nqkv;
+  na.ctx_slice = (int64_t)Mc * Nkv;
+  na.kslices = tq.kslices;
   na.positions = positions;
   na.cos_sin = L->cos_sin;
   na.q_norm = L->w.q_norm;
@@ -280,7 +310,9 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   na.seq = seq;
   record(L, &ev, s);
-  if (launch_norm_rope(c.dtype, d, na, B * nkv, s) != hipSuccess) return DFLASH_ERR_HIP;
+  int max_new = 0;
+  for (int b = 0; b < B; ++b) max_new = std::max(max_new, ctx_offsets[b + 1] - ctx_offsets[b] + bs);
+  if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_NORM_ROPE, ev, s);
 
   // HK3 (+ HK4)
@@ -322,13 +354,13 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   }
 
   // HK1: o_proj
+  const TileChoice to = choose_tiles(L, Mq, H, 0, 0, false);
   GemmArgs go;
   std::memset(&go, 0, sizeof(go));
   go.nprob = 1;
-  go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + kGemmBN - 1) / kGemmBN, 0};
+  go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + to.bn - 1) / to.bn, 0, 0};
   record(L, &ev, s);
-  if (launch_gemm(c.dtype, false, go, ((Mq + kGemmBM - 1) / kGemmBM) * go.p[0].tiles_n, s) != hipSuccess)
-    return DFLASH_ERR_HIP;
+  if (launch_gemm(c.dtype, false, go, to.tiles, to.bm, to.bn, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_GEMM_O, ev, s);
 
   for (int b = 0; b < B; ++b) cache->len[b] += (ctx_offsets[b + 1] - ctx_offsets[b]) + bs;

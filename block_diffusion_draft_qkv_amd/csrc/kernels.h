@@ -10,31 +10,35 @@ namespace dflash {
 
 // ---------------------------------------------------------------- projections
 // C[m][n] = sum_k A[m][k] * B[n][k]: both operands row-major with k contiguous
-// (an nn.Linear weight is B). Up to two independent problems per launch.
+// (an nn.Linear weight is B). Up to two independent problems per launch, one
+// BM x BN tile per work-group; gridDim.y splits k, slice s of a problem's fp32
+// partial sums going to c + s * slice_stride elements.
 struct GemmProblem {
   const void* a;
   const void* b;
   void* c;
   int32_t m, n, k;
   int32_t lda, ldb, ldc;
-  int32_t tiles_n;     // ceil(n / BN)
-  int32_t tile_begin;  // first flat tile index of this problem in the launch
+  int32_t tiles_n;       // ceil(n / BN)
+  int32_t tile_begin;    // first flat tile index of this problem in the launch
+  int64_t slice_stride;  // elements between k-slice outputs
 };
 struct GemmArgs {
   GemmProblem p[2];
   int32_t nprob;
 };
-constexpr int kGemmBM = 64;
-constexpr int kGemmBN = 128;
 // dtype: 0 fp32, 1 bf16 (A, B element type). out_f32: C is fp32, else C has
-// the element type of A and B.
-hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles,
-                       hipStream_t stream);
+// the element type of A and B (then kslices must be 1). (bm, bn) in
+// {64, 128}^2.
+hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles, int bm, int bn,
+                       int kslices, hipStream_t stream);
 
 // ------------------------------------------------- norm + RoPE + append + Q
 struct NormRopeArgs {
-  const float* qkv;        // [B*bs][(nq + 2 nkv) d] block projections (fp32)
-  const float* ctxkv;      // [sum n_b][2 nkv d] context projections (fp32)
+  const float* qkv;        // [kslices][B*bs][(nq + 2 nkv) d] block projections (fp32)
+  const float* ctxkv;      // [kslices][sum n_b][2 nkv d] context projections (fp32)
+  int64_t qkv_slice, ctx_slice;  // elements between k slices (summed on read)
+  int32_t kslices;
   const int32_t* positions;
   const float* cos_sin;    // cos [max_pos][d/2] then sin [max_pos][d/2]
   const void* q_norm;
@@ -47,8 +51,10 @@ struct NormRopeArgs {
   float eps, qscale;
   SeqTable seq;
 };
+// grid: B * n_kv (one column of work-groups per sequence and KV head);
+// max_new_rows: the largest n_b + bs of the batch.
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
-                            hipStream_t stream);
+                            int max_new_rows, hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
 // Flattened work: pairs (b, j) in b-major order, each owning the 64-key tiles

@@ -1,0 +1,44 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (same library, same step call), against the float64 oracle
+run over every output and every appended cache row.
+
+C1 tiny fp32 | C2 single bf16 | C3 ragged B=32 | C4 long 32K | C5 window 4096.
+After the step each sequence is cropped to its accepted prefix and the
+lengths and surviving rows are checked bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from harness import (assert_close, check_cache_after_step, make_cache, make_layer, raw_bits,
+                     run_oracle, step_inputs, to64)
+from workload import make_case
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_full_config_step_and_crop(name):
+    case = make_case(name, seed=0)
+    print(f"[{name}] batch {case.batch}, keys {int(case.total_len.sum())}", flush=True)
+    layer = make_layer(case)
+    cache = make_cache(case)
+    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    hs, th, pos = step_inputs(case)
+    out = layer.step(hs, th, case.ctx_offsets, pos, cache)
+    torch.cuda.synchronize()
+    assert layer.poll_error() == 0
+    ref, new = run_oracle(case)
+    max_abs, rel = assert_close(to64(out), ref, case.cfg.dtype, f"{name} out")
+    print(f"[{name}] out max abs {max_abs:.3e} rel-RMS {rel:.3e}", flush=True)
+    check_cache_after_step(case, cache, bk, bv, new)
+
+    # crop to the accepted prefix: lengths exact, rows below untouched
+    k_after, v_after = raw_bits(cache.k), raw_bits(cache.v)
+    accepted = case.cached_len + case.new_ctx + case.accept
+    for b in range(case.batch):
+        cache.crop(b, int(accepted[b]))
+    assert cache.lengths.tolist() == accepted.tolist()
+    np.testing.assert_array_equal(raw_bits(cache.k), k_after)
+    np.testing.assert_array_equal(raw_bits(cache.v), v_after)
+    layer.close()
