@@ -11,9 +11,9 @@ step to step so the 256 MB Infinity Cache cannot serve a cache that the
 previous step just streamed.
 
 One "step" = the whole hot path: grouped QKV/context-KV GEMM, norm+RoPE+append,
-split-KV attention, merge, o_proj, and the crop. Between timed steps the
-lengths are rewound to the round's starting lengths (host-only) so that every
-step sees the same workload.
+split-KV attention, the merge of split pairs, o_proj, and the
+crop. Between timed steps the lengths are rewound to the round's starting
+lengths (host-only) so that every step sees the same workload.
 
 Prints ONE JSON line. ``value`` is draft-block tokens/s (B*bs per step);
 ``roofline`` covers the attention kernel (HBM-bound): algorithmic bytes per

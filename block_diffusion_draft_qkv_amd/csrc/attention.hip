@@ -1,5 +1,5 @@
 // HK3: split-KV non-causal grouped-query attention of the draft block over the
-// draft KV cache, and HK4: log-sum-exp merge of split partials.
+// draft KV cache, and HK4: log-sum-exp merge of the pairs it split.
 //
 // What is computed (NeMo page "draft_qwen3": Qwen3DFlashAttention, scaling,
 // _sliding_window_mask; "DFlash源码导读（二）" section on non-causal block
@@ -17,8 +17,11 @@
 // lengths. A range crosses pair boundaries; the part of a pair inside a range
 // is a segment. A segment that is a whole pair writes the output directly; a
 // pair cut by a range boundary leaves fp32 partials (un-normalised O, exponent
-// offset, sum) in slot 2w (the range's first segment) or 2w+1 (its last), which
-// HK4 merges.
+// offset, sum) in slot 2w (the range's first segment) or 2w+1 (its last),
+// which HK4 merges. (Merging inside HK3 would need the partials coherent
+// across XCDs before the last part is counted in; those device-scope round
+// trips land on the slowest work-group's critical path and cost more than a
+// separate launch.)
 //
 // Pipeline. One continuous stream of LDS-DMA loads (gfx950
 // global_load_lds_dwordx4) runs through the whole range, crossing segment
@@ -84,70 +87,6 @@ __device__ inline void seq_tiles(const AttnArgs& a, int b, int kt, int& lo, int&
   cnt = (T + kt - 1) / kt - lo;
 }
 
-// Wave-level inclusive scan (64 lanes).
-__device__ inline int64_t wave_incl_scan(int64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-// Exclusive prefix, over sequences, of the tile counts: pre[b] for one b,
-// computed by each wave in registers (lane l owns sequences 4l .. 4l+3).
-__device__ inline int64_t tiles_before(const AttnArgs& a, int kt, int b) {
-  const int lane = threadIdx.x & 63;
-  int64_t s = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int bb = 4 * lane + k;
-    if (bb < a.seq.batch && bb < b) {
-      int lo, cnt;
-      seq_tiles(a, bb, kt, lo, cnt);
-      s += cnt;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-  return s;
-}
-
-// The sequence b holding flat tile f (flat index = nkv * pre[b] + j * cnt_b +
-// tile offset), with pre[b]; every lane gets the same answer.
-__device__ inline int find_seq(const AttnArgs& a, int kt, int64_t f, int64_t& pre_b) {
-  const int lane = threadIdx.x & 63;
-  int cnt4[4];
-  int64_t tot = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int bb = 4 * lane + k;
-    cnt4[k] = 0;
-    if (bb < a.seq.batch) {
-      int lo;
-      seq_tiles(a, bb, kt, lo, cnt4[k]);
-    }
-    tot += cnt4[k];
-  }
-  const int64_t incl = wave_incl_scan(tot);
-  int64_t run = incl - tot;
-  int hit_b = -1;
-  int64_t hit_pre = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (hit_b < 0 && cnt4[k] > 0 && a.nkv * run <= f && f < a.nkv * (run + cnt4[k])) {
-      hit_b = 4 * lane + k;
-      hit_pre = run;
-    }
-    run += cnt4[k];
-  }
-  const uint64_t m = __builtin_amdgcn_ballot_w64(hit_b >= 0);
-  const int src = (int)__builtin_ctzll(m);
-  pre_b = __shfl(hit_pre, src, 64);
-  return __shfl(hit_b, src, 64);
-}
-
 __device__ inline int64_t bound_of(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
 __device__ inline int64_t owner_of(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
 
@@ -201,10 +140,25 @@ __device__ inline u32x4 pack_p_bf16(const f32x4& p0, const f32x4& p1) {
   return __builtin_bit_cast(u32x4, v);
 }
 
+// Four consecutive outputs of one row as one 16-byte (fp32) or 8-byte (bf16) store.
+template <typename T> __device__ inline void store4(T* p, const f32x4& v);
+template <> __device__ inline void store4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <> __device__ inline void store4<__bf16>(__bf16* p, const f32x4& v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = (__bf16)v[r];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+
 // Position in the flattened work: pair (b, j), key tile, the pair's tiles.
 struct Cursor {
   int b, j, tile, lo, hi;
 };
+
+
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
@@ -269,18 +223,16 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
     qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
   }
 
-  // Both cursors start at flat tile f0.
+  // Both cursors start at flat tile f0, whose pair and tile the host worked out.
   Cursor ic;
   {
-    int64_t pre_b;
-    ic.b = __builtin_amdgcn_readfirstlane(find_seq(a, KT, f0, pre_b));
-    pre_b = ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pre_b >> 32)) << 32) |
-            __builtin_amdgcn_readfirstlane((uint32_t)pre_b);
+    const uint32_t st = a.start[w];
+    const int pair0 = (int)(st & 0xffffu);
+    ic.b = pair0 / nkv;
+    ic.j = pair0 % nkv;
+    ic.tile = (int)(st >> 16);
     int lo, cnt;
     seq_tiles(a, ic.b, KT, lo, cnt);
-    const int64_t off = f0 - (int64_t)nkv * pre_b;
-    ic.j = (int)(off / cnt);
-    ic.tile = lo + (int)(off % cnt);
     ic.lo = lo;
     ic.hi = lo + cnt;
   }
@@ -309,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
       const uint32_t qs = qlds0 + (uint32_t)(iseg % S) * QSLOT;
       const void* qsrc = uniform_ptr(Qp + pair * R * D * sizeof(T));
 #pragma unroll
-      for (int i = 0; i < QPW; ++i) lds_dma16(qdma[i], qsrc, qs + (uint32_t)(i * 4 + wave_u) * 1024u);
+      for (int i = 0; i < QPW; ++i) lds_dma16<true>(qdma[i], qsrc, qs + (uint32_t)(i * 4 + wave_u) * 1024u);
       ++iseg;
       blocks += QPW;
     }
@@ -317,9 +269,9 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
     const void* kt = uniform_ptr(Kc + (pair * a.cap + (size_t)ic.tile * KT) * D * sizeof(T));
     const void* vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)ic.tile * KT) * sizeof(T));
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) lds_dma16(kdma[i], kt, sl + (uint32_t)(i * 4 + wave_u) * 1024u);
+    for (int i = 0; i < KPW; ++i) lds_dma16<true>(kdma[i], kt, sl + (uint32_t)(i * 4 + wave_u) * 1024u);
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) lds_dma16(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * 4 + wave_u) * 1024u);
+    for (int i = 0; i < VPW; ++i) lds_dma16<true>(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * 4 + wave_u) * 1024u);
     advance(ic);
     return blocks;
   };
@@ -342,12 +294,14 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
   for (int it = 0; it < total; ++it) {
     vm_wait<KVW, QPW>(pending);
     block_barrier();
-    int next = 0;
-    if (it + S - 1 < total) next = issue(it + S - 1);
-    pending = S >= 3 ? next : 0;
-
     const bool seg_begin = it == 0 || cc.tile == cc.lo;
     const bool seg_end = it + 1 == total || cc.tile + 1 == cc.hi;
+    // A step that ends a segment stores its result before issuing the next
+    // DMA: the wait counter retires in issue order, so stores issued after a
+    // stage's loads would hold up the wait for that stage.
+    const bool more = it + S - 1 < total;
+    int next = 0;
+    if (more && !seg_end) next = issue(it + S - 1);
     if (seg_begin) {
       seg_start_flat = it;
       seg_from_lo = cc.tile == cc.lo;
@@ -445,9 +399,7 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
             T* orow = static_cast<T*>(a.o) +
                       ((size_t)(cc.b * a.bs + i) * a.nq + (size_t)(cc.j * g + hh)) * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) orow[db * 16 + 4 * q + r] = Elem<T>::from_f32(acc[db][r] * inv);
+            for (int db = 0; db < DB; ++db) store4<T>(orow + db * 16 + 4 * q, acc[db] * inv);
           } else {
             const int slot = 2 * (int)w + (seg_start_flat == 0 ? 0 : 1);
             float* po = a.part_o + ((size_t)slot * kMaxQueryRows + qrow) * D;
@@ -462,49 +414,63 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
         }
       }
     }
+    if (more && seg_end) next = issue(it + S - 1);
+    pending = S >= 3 ? next : 0;
     advance(cc);
   }
+
 }
 
-// HK4: one work-group per (pair, group of rows). Pairs processed whole by one
-// work-group return at once.
+// HK4: one work-group column per split pair (host list), one thread per four
+// outputs of a row. o = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with
+// M = max_p m_p, folded over the parts four at a time so that each group of
+// loads goes out together. Part 0 sits in slot first_slot, part p > 0 (the
+// work-group first + p, whose range starts inside the pair) in slot
+// 2 (first + p).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rows_per_group) {
-  using Sh = AttnShape<T, D>;
-  const int nkv = a.nkv, g = a.nq / nkv;
-  const int b = blockIdx.x / nkv, j = blockIdx.x % nkv;
-  const int64_t N = a.total_tiles, G = a.G;
-  int lo, cnt;
-  seq_tiles(a, b, Sh::KT, lo, cnt);
-  const int64_t s_p = (int64_t)nkv * tiles_before(a, Sh::KT, b) + (int64_t)j * cnt, e_p = s_p + cnt;
-  const int64_t w_first = owner_of(s_p, N, G), w_last = owner_of(e_p - 1, N, G);
-  if (w_first == w_last) return;
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  constexpr int TPR = D / 4, RPG = 256 / TPR;
+  const int e = blockIdx.x;
+  const int pair = a.pair[e], s0 = a.first_slot[e], np = a.nparts[e];
+  const int row = blockIdx.y * RPG + (int)threadIdx.x / TPR;
+  if (row >= a.R) return;
+  const int d4 = ((int)threadIdx.x % TPR) * 4;
+  auto slot = [&](int p) { return p == 0 ? s0 : (s0 & ~1) + 2 * p; };
 
-  constexpr int TPR = D / 4;  // threads per row, 4 values each
-  const int tid = threadIdx.x;
-  const int row = blockIdx.y * rows_per_group + tid / TPR;
-  const int d4 = (tid % TPR) * 4;
-  if (tid / TPR >= rows_per_group || row >= a.R) return;
-
-  auto slot_of = [&](int64_t wg) {
-    return (int)(2 * wg + ((wg == w_first && s_p != bound_of(wg, N, G)) ? 1 : 0));
-  };
-  float M = kNegInf;
-  for (int64_t wg = w_first; wg <= w_last; ++wg)
-    M = fmaxf(M, a.part_ml[((size_t)slot_of(wg) * kMaxQueryRows + row) * 2]);
-  float den = 0.f;
+  float M = kNegInf, den = 0.f;
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t wg = w_first; wg <= w_last; ++wg) {
-    const size_t sr = (size_t)slot_of(wg) * kMaxQueryRows + row;
-    const float wgt = __builtin_amdgcn_exp2f(a.part_ml[sr * 2] - M);
-    den += wgt * a.part_ml[sr * 2 + 1];
-    num += wgt * *reinterpret_cast<const f32x4*>(a.part_o + sr * D + d4);
+  for (int p0 = 0; p0 < np; p0 += 4) {
+    float m[4], l[4];
+    f32x4 o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m[k] = kNegInf;
+      l[k] = 0.f;
+      o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p0 + k < np) {
+        const size_t sr = (size_t)slot(p0 + k) * kMaxQueryRows + row;
+        m[k] = a.part_ml[sr * 2];
+        l[k] = a.part_ml[sr * 2 + 1];
+        o[k] = *reinterpret_cast<const f32x4*>(a.part_o + sr * D + d4);
+      }
+    }
+    const float Mn = fmaxf(fmaxf(M, fmaxf(m[0], m[1])), fmaxf(m[2], m[3]));
+    const float Mu = Mn == kNegInf ? 0.f : Mn;  // rows no key reached yet
+    const float sc = __builtin_amdgcn_exp2f(M - Mu);
+    den *= sc;
+    num *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float wk = __builtin_amdgcn_exp2f(m[k] - Mu);
+      den += wk * l[k];
+      num += wk * o[k];
+    }
+    M = Mn;
   }
-  const float inv = 1.0f / den;
+  const int g = a.nq / a.nkv, b = pair / a.nkv, j = pair % a.nkv;
   const int i = row / g, hh = row % g;
   T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.bs + i) * a.nq + (size_t)(j * g + hh)) * D;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) orow[d4 + r] = Elem<T>::from_f32(num[r] * inv);
+  store4<T>(orow + d4, num * (1.0f / den));
 }
 
 template <typename T, int D> int wgs_per_cu() { return (160 * 1024) / AttnShape<T, D>::LDS; }
@@ -538,20 +504,20 @@ hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_merge(int dtype, int head_dim, const AttnArgs& args, int merge_groups,
-                        hipStream_t stream) {
+hipError_t launch_merge(int dtype, int head_dim, const MergeArgs& args, hipStream_t stream) {
+  if (args.n_split <= 0) return hipSuccess;
   const int rows_per_group = 256 / (head_dim / 4);
-  const dim3 grid(args.seq.batch * args.nkv, merge_groups), block(256);
+  const dim3 grid(args.n_split, (args.R + rows_per_group - 1) / rows_per_group), block(256);
   if (dtype == 1) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((attn_merge_kernel<__bf16, 128>), grid, block, 0, stream, args, rows_per_group);
+      hipLaunchKernelGGL((attn_merge_kernel<__bf16, 128>), grid, block, 0, stream, args);
     else
-      hipLaunchKernelGGL((attn_merge_kernel<__bf16, 64>), grid, block, 0, stream, args, rows_per_group);
+      hipLaunchKernelGGL((attn_merge_kernel<__bf16, 64>), grid, block, 0, stream, args);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((attn_merge_kernel<float, 128>), grid, block, 0, stream, args, rows_per_group);
+      hipLaunchKernelGGL((attn_merge_kernel<float, 128>), grid, block, 0, stream, args);
     else
-      hipLaunchKernelGGL((attn_merge_kernel<float, 64>), grid, block, 0, stream, args, rows_per_group);
+      hipLaunchKernelGGL((attn_merge_kernel<float, 64>), grid, block, 0, stream, args);
   }
   return hipGetLastError();
 }

@@ -5,7 +5,7 @@
 //   HK1 grouped GEMM   block rows -> q|k|v, context rows -> k|v (fp32 out)
 //   HK2 norm_rope      per-head RMSNorm + RoPE + Q pack + cache append
 //   HK3 attention      split-KV non-causal GQA over the cache
-//   HK4 merge          only when some (sequence, KV head) was split
+//   HK4 merge          the pairs HK3 split over several work-groups
 //   HK1 GEMM           o_proj
 // then the host lengths become T_b = L_b + n_b + bs.
 #include <hip/hip_runtime.h>
@@ -60,7 +60,8 @@ int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 // Attention work-groups for N flat tiles: as many as the CUs hold at once
 // (the kernel's LDS ring bounds that), never more than there are tiles.
 int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
-  const int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
+  int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
+  cap = std::min<int64_t>(cap, kMaxGroups);
   return std::max<int64_t>(1, std::min<int64_t>(cap, n_tiles));
 }
 
@@ -68,7 +69,8 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   const dflash_config& c = L->cfg;
   const int64_t d = c.head_dim, g = c.n_q_heads / c.n_kv_heads;
   const int64_t mq = batch * c.block_size, es = elem_size(c);
-  const int64_t gmax = (int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim);
+  const int64_t gmax =
+      std::min<int64_t>((int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim), kMaxGroups);
   Carve w{};
   size_t off = 0;
   w.qkv = off;     off += align_up(kMaxKSlices * mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
@@ -112,6 +114,7 @@ int validate_config(const dflash_config* c) {
       c->max_position <= 0 || c->sliding_window < 0)
     return DFLASH_ERR_SHAPE;
   if (c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if (c->n_kv_heads > kMaxKvHeads) return DFLASH_ERR_UNSUPPORTED;
   if (c->hidden % 64) return DFLASH_ERR_SHAPE;
   if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) return DFLASH_ERR_ARG;
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_ARG;
@@ -231,6 +234,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   const int B = cache->batch;
   if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
   if (cache->capacity <= 0 || cache->capacity % kKeyTile) return DFLASH_ERR_SHAPE;
+  if (cache->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
   if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
   const int bs = c.block_size, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int g = nq / nkv, R = bs * g;
@@ -240,6 +244,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   std::memset(&seq, 0, sizeof(seq));
   seq.batch = B;
   int64_t n_tiles = 0;
+  int32_t tile_lo[kMaxBatch], tile_cnt[kMaxBatch];  // each sequence's attention key tiles
   for (int b = 0; b < B; ++b) {
     const int64_t n = (int64_t)ctx_offsets[b + 1] - ctx_offsets[b];
     if (n < 0) return DFLASH_ERR_SHAPE;
@@ -250,7 +255,9 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
     seq.ctx_off[b] = ctx_offsets[b];
     int64_t first = 0;
     if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
-    n_tiles += nkv * ((T + kt - 1) / kt - first / kt);
+    tile_lo[b] = (int32_t)(first / kt);
+    tile_cnt[b] = (int32_t)((T + kt - 1) / kt - first / kt);
+    n_tiles += (int64_t)nkv * tile_cnt[b];
   }
   seq.ctx_off[B] = ctx_offsets[B];
   const int64_t Mc = ctx_offsets[B];
@@ -328,28 +335,47 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   aa.total_tiles = n_tiles;
   aa.G = (int32_t)attn_groups(L, n_tiles);
   aa.seq = seq;
+  // Each work-group's first (pair, tile): walk the pairs in flat order.
+  {
+    int64_t f = 0;
+    int w = 0;
+    for (int b = 0; b < B && w < aa.G; ++b)
+      for (int j = 0; j < nkv && w < aa.G; ++j) {
+        const int64_t end = f + tile_cnt[b];
+        for (int64_t fw; w < aa.G && (fw = part_bound(w, n_tiles, aa.G)) < end; ++w)
+          aa.start[w] = (uint32_t)(b * nkv + j) | ((uint32_t)(tile_lo[b] + (fw - f)) << 16);
+        f = end;
+      }
+  }
   record(L, &ev, s);
   if (launch_attn(c.dtype, d, aa, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_ATTN, ev, s);
 
-  // A merge is needed iff some pair straddles two work-group ranges.
-  bool split = false;
+  // HK4 over the pairs that straddle a range boundary.
+  MergeArgs ma;
+  ma.part_o = aa.part_o;
+  ma.part_ml = aa.part_ml;
+  ma.o = obuf;
+  ma.nq = nq; ma.nkv = nkv; ma.bs = bs; ma.R = R;
+  ma.n_split = 0;
   {
     int64_t f = 0;
-    for (int b = 0; b < B && !split; ++b) {
-      const int64_t T = (int64_t)seq.len[b] + (seq.ctx_off[b + 1] - seq.ctx_off[b]) + bs;
-      int64_t first = 0;
-      if (c.sliding_window > 0) first = std::max<int64_t>(0, T - bs - c.sliding_window + 1);
-      const int64_t cnt = (T + kt - 1) / kt - first / kt;
-      for (int j = 0; j < nkv && !split; ++j, f += cnt)
-        split = part_owner(f, n_tiles, aa.G) != part_owner(f + cnt - 1, n_tiles, aa.G);
-    }
+    for (int b = 0; b < B; ++b)
+      for (int j = 0; j < nkv; ++j) {
+        const int64_t e = f + tile_cnt[b];
+        const int64_t w0 = part_owner(f, n_tiles, aa.G), w1 = part_owner(e - 1, n_tiles, aa.G);
+        if (w0 != w1) {
+          ma.pair[ma.n_split] = b * nkv + j;
+          ma.first_slot[ma.n_split] = (int16_t)(2 * w0 + (f != part_bound(w0, n_tiles, aa.G) ? 1 : 0));
+          ma.nparts[ma.n_split] = (int16_t)(w1 - w0 + 1);
+          ++ma.n_split;
+        }
+        f = e;
+      }
   }
-  if (split) {
-    const int rows_per_group = 256 / (d / 4);
+  if (ma.n_split > 0) {
     record(L, &ev, s);
-    if (launch_merge(c.dtype, d, aa, (R + rows_per_group - 1) / rows_per_group, s) != hipSuccess)
-      return DFLASH_ERR_HIP;
+    if (launch_merge(c.dtype, d, ma, s) != hipSuccess) return DFLASH_ERR_HIP;
     record_end(L, DFLASH_K_MERGE, ev, s);
   }
 

@@ -70,14 +70,28 @@ struct AttnArgs {
   int32_t nq, nkv, bs, R, cap, window, G;
   int64_t total_tiles;
   SeqTable seq;
+  // Start of work-group w's range: pair b * nkv + j in bits 0..15, absolute key
+  // tile in bits 16..31 (filled by the host, which knows every length).
+  uint32_t start[kMaxGroups];
 };
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream);
 // Attention work-groups one CU holds at once (bounded by the kernel's LDS ring)
 // and the keys per attention tile.
 int attn_wgs_per_cu(int dtype, int head_dim);
 int attn_key_tile(int dtype, int head_dim);
-hipError_t launch_merge(int dtype, int head_dim, const AttnArgs& args, int merge_groups,
-                        hipStream_t stream);
+
+// Pairs that the attention split over several work-group ranges (at most
+// G - 1: each contains a range boundary), merged by HK4.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  void* o;
+  int32_t nq, nkv, bs, R, n_split;
+  int32_t pair[kMaxGroups];        // b * nkv + j
+  int16_t first_slot[kMaxGroups];  // slot of the pair's first part
+  int16_t nparts[kMaxGroups];      // parts (work-group ranges) of the pair
+};
+hipError_t launch_merge(int dtype, int head_dim, const MergeArgs& args, hipStream_t stream);
 
 // Host-side mirror of the kernels' partition (used to size and skip launches).
 inline int64_t part_bound(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }

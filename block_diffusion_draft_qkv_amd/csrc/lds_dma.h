@@ -21,11 +21,22 @@ __device__ inline const void* uniform_ptr(const void* p) {
 // drains a ring on it (its waits can then only be more conservative, never
 // short); completion is awaited explicitly with an s_waitcnt vmcnt. The
 // s_nop gives the M0 write the wait state an LDS-DMA load needs after it.
+// kStream sets the non-temporal cache policy: for data read exactly once (the
+// KV cache in attention) it streams measurably faster from HBM than the
+// default policy, which is kept for operands that other work-groups re-read
+// through L2 (GEMM weights and activations).
+template <bool kStream = false>
 __device__ inline void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) leaving expcnt and lgkmcnt alone (gfx9 encoding:

@@ -62,7 +62,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_MAX_BATCH 256
 
 /* Layer shape and numerics. Limits checked by dflash_layer_create:
- *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
+ *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0; n_kv_heads <= 256;
  *   block_size * (n_q_heads / n_kv_heads) <= 64 (the query rows that share one
  *   KV head, packed into MFMA tiles); hidden % 64 == 0;
  *   rope_theta > 0; rms_eps >= 0; sliding_window >= 0; max_position >= 1. */
@@ -98,7 +98,7 @@ typedef struct {
  *        authoritative length (kernels receive it by value).
  * K holds post-norm, post-RoPE keys; V holds raw values. Rows at or past len
  * are dead: they never contribute to a result.
- * capacity must be a positive multiple of 64. */
+ * capacity must be a positive multiple of 64, at most 2^21 rows. */
 typedef struct {
     void* k;
     void* v;
@@ -154,7 +154,7 @@ size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
  *                  bytes, 256-byte aligned; contents need no initialisation.
  * Errors (nothing launched, nothing changed): DFLASH_ERR_ARG (null pointer,
  * batch outside [1, DFLASH_MAX_BATCH]), DFLASH_ERR_SHAPE (bad offsets,
- * negative len, capacity not a multiple of 64), DFLASH_ERR_CAPACITY (some
+ * negative len, capacity not a multiple of 64 or above 2^21), DFLASH_ERR_CAPACITY (some
  * T_b > capacity), DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP (launch failure;
  * lengths are then left unchanged). */
 int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
