@@ -9,7 +9,7 @@
 // |(T_b - bs + i) - t| < W; then o . V.
 //
 // Work split. The bs*g query rows that share KV head j (row i*g + hh) form one
-// tile of up to 64 rows; wave w of the 256-thread work-group owns rows
+// tile of up to 64 rows; consumer wave w (0-3) of the work-group owns rows
 // 16w .. 16w+15. Every (sequence b, KV head j) pair owns the key tiles
 // [lo_b, hi_b) (lo_b > 0 only under a sliding window); all tiles of all pairs
 // are flattened b-major and cut into G equal ranges, one per work-group, so
@@ -27,7 +27,10 @@
 // global_load_lds_dwordx4) runs through the whole range, crossing segment
 // boundaries without draining: each step brings one K tile, one V^T tile and,
 // when the step starts a segment, that pair's Q tile into an S-stage LDS ring
-// while the previous stage is used:
+// while the previous stage is used. Two producer waves do nothing but issue
+// these loads and wait for them, so a load queue that is full (the normal
+// state when HBM is the bottleneck) stalls only them; the four consumer waves
+// compute:
 //   S^T (keys x queries) = K . Q^T     on MFMA, K from LDS, Q in VGPRs
 //   online softmax in the log2 domain  (Q was pre-scaled by d^-1/2 log2 e)
 //   O^T (d x queries)   += V^T . P^T   on MFMA, V^T from LDS, P^T from VGPRs
@@ -53,6 +56,12 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;
 
+// Wave roles of the 384-thread attention work-group: waves 0-3 compute (16
+// query rows each), waves 4-5 only issue and await the LDS-DMA loads.
+constexpr int kConsumerWaves = 4;
+constexpr int kProducerWaves = 2;
+constexpr int kAttnThreads = 64 * (kConsumerWaves + kProducerWaves);
+
 // Shapes of the attention kernel for element type T and head_dim D.
 template <typename T, int D> struct AttnShape {
   static constexpr int KT = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // keys per tile
@@ -64,15 +73,18 @@ template <typename T, int D> struct AttnShape {
   static constexpr int KB = KT / 16;                                 // 16-key S^T blocks per tile
   static constexpr int K_BYTES = KT * D * (int)sizeof(T);
   static constexpr int TILE = 2 * K_BYTES;                           // K + V^T
-  static constexpr int KPW = K_BYTES / 4096, VPW = K_BYTES / 4096;   // 1 KB DMA blocks per wave
-  static constexpr int QROWS = 64 / CPR;                             // Q rows per 1 KB block
-  static constexpr int QPW = (kMaxQueryRows / QROWS + 3) / 4;        // Q DMA blocks per wave
-  static constexpr int QSLOT = QPW * 4 * 1024;
+  static constexpr int Q_BYTES = kMaxQueryRows * D * (int)sizeof(T);
+  // 1 KB DMA blocks per producer wave: of a K tile (and of a V^T tile), of a Q tile.
+  static constexpr int KPP = K_BYTES / 1024 / kProducerWaves;
+  static constexpr int QPP = Q_BYTES / 1024 / kProducerWaves;
+  static constexpr int QSLOT = Q_BYTES;
   static constexpr int S = 3 * (TILE + QSLOT) <= 150 * 1024 ? 3 : 2; // ring depth
   static constexpr int LDS = S * (TILE + QSLOT);
   static constexpr int DB = D / 16;
-  static_assert(K_BYTES % 4096 == 0, "a tile must split into 1 KB blocks over 4 waves");
+  static_assert(K_BYTES % (1024 * kProducerWaves) == 0, "a K tile splits into 1 KB blocks per producer");
+  static_assert(Q_BYTES % (1024 * kProducerWaves) == 0, "a Q tile splits into 1 KB blocks per producer");
   static_assert(sizeof(T) == 4 || KT % 32 == 0, "bf16 P packing pairs 16-key blocks");
+  static_assert(2 * (S - 1) * KPP + (S - 1) * QPP <= 63, "outstanding DMA blocks must fit vmcnt");
 };
 
 // Per-sequence key tiles [lo, lo + cnt) of the attention (uniform per wave).
@@ -89,6 +101,15 @@ __device__ inline void seq_tiles(const AttnArgs& a, int b, int kt, int& lo, int&
 
 __device__ inline int64_t bound_of(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
 __device__ inline int64_t owner_of(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
+
+// Range handled by work-group `bid`. Work-groups are dealt to the 8 XCDs
+// round-robin (bid % 8); giving each XCD a contiguous block of ranges spreads
+// every KV head and sequence over all XCDs instead of pinning XCD x to the
+// ranges x, x+8, ..., which measured up to 5 % slower on some XCDs.
+__device__ inline int range_of_block(int bid, int G) {
+  const int x = bid % 8, per = G / 8, extra = G % 8;
+  return x * per + (x < extra ? x : extra) + bid / 8;
+}
 
 // Which key each lane's S^T accumulator row stands for (see the file comment).
 template <typename T> __device__ inline int key_of(int kb, int m);
@@ -161,82 +182,35 @@ struct Cursor {
 
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs a) {
   using Sh = AttnShape<T, D>;
   constexpr int KT = Sh::KT, E = Sh::E, CPR = Sh::CPR, VCPR = Sh::VCPR, NC = Sh::NC, NKS = Sh::NKS;
   constexpr int KB = Sh::KB, DB = Sh::DB, S = Sh::S, TILE = Sh::TILE, K_BYTES = Sh::K_BYTES;
-  constexpr int KPW = Sh::KPW, VPW = Sh::VPW, QPW = Sh::QPW, QSLOT = Sh::QSLOT;
-  constexpr int KVW = KPW + VPW;
+  constexpr int KPP = Sh::KPP, QPP = Sh::QPP, QSLOT = Sh::QSLOT;
   __shared__ u32x4 lds[Sh::LDS / 16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
-  const int nkv = a.nkv, g = a.nq / nkv, R = a.R;
-  const int64_t N = a.total_tiles, G = a.G, w = blockIdx.x;
-  const int64_t f0 = bound_of(w, N, G), f1 = bound_of(w + 1, N, G);
-  const int total = (int)(f1 - f0);
-  const bool active = wave * 16 < R;
-  const int qrow = wave * 16 + r16;
-  const bool qvalid = qrow < R;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nkv = a.nkv, R = a.R;
+  const int64_t N = a.total_tiles, G = a.G, w = range_of_block(blockIdx.x, (int)G);
+  const int total = (int)(bound_of(w + 1, N, G) - bound_of(w, N, G));
   const uint32_t lds0 = lds_base(lds);
   const uint32_t qlds0 = lds0 + S * TILE;
-  const char* Kc = static_cast<const char*>(a.kc);
-  const char* Vc = static_cast<const char*>(a.vc);
-  const char* Qp = static_cast<const char*>(a.q);
 
-  // Per-lane byte offsets, fixed for the whole kernel.
-  // LDS reads: K operand of block kb, chunk c = koff[c] + kb_off(kb); V^T
-  // operand of d-block db, key chunk ks = voff[ks] + db_off(db); Q row chunks.
-  uint32_t koff[NC], voff[NKS], qoff[NC];
-  {
-    const int krow = key_of<T>(0, r16), ksw = kswz<T, CPR>(krow);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) koff[c] = (uint32_t)(krow * CPR + ((4 * c + q) ^ ksw)) * 16u;
-    const int vsw = rswz<VCPR>(r16);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) voff[ks] = (uint32_t)(r16 * VCPR + ((4 * ks + q) ^ vsw)) * 16u + K_BYTES;
-    const int qsw = rswz<CPR>(qrow);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qoff[c] = (uint32_t)(qrow * CPR + ((4 * c + q) ^ qsw)) * 16u;
-  }
-  // DMA sources relative to a tile's (or Q tile's) first row: 1 KB block i of
-  // this wave; each lane fetches the chunk that belongs at its swizzled LDS
-  // position.
-  uint32_t kdma[KPW], vdma[VPW], qdma[QPW];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int blk = i * 4 + wave_u, row = blk * (64 / CPR) + lane / CPR;
-    const int c = (lane % CPR) ^ kswz<T, CPR>(row);
-    kdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
-  }
-#pragma unroll
-  for (int i = 0; i < VPW; ++i) {
-    const int blk = i * 4 + wave_u, row = blk * (64 / VCPR) + lane / VCPR;
-    const int c = (lane % VCPR) ^ rswz<VCPR>(row);
-    vdma[i] = (uint32_t)(row * a.cap + c * E) * (uint32_t)sizeof(T);
-  }
-#pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    const int blk = i * 4 + wave_u, row = blk * (64 / CPR) + lane / CPR;
-    const int c = (lane % CPR) ^ rswz<CPR>(row);
-    qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
-  }
-
-  // Both cursors start at flat tile f0, whose pair and tile the host worked out.
-  Cursor ic;
+  // Producers and consumers walk the same flattened tiles from flat tile f0,
+  // whose pair and tile the host worked out.
+  Cursor cur;
   {
     const uint32_t st = a.start[w];
     const int pair0 = (int)(st & 0xffffu);
-    ic.b = pair0 / nkv;
-    ic.j = pair0 % nkv;
-    ic.tile = (int)(st >> 16);
+    cur.b = pair0 / nkv;
+    cur.j = pair0 % nkv;
+    cur.tile = (int)(st >> 16);
     int lo, cnt;
-    seq_tiles(a, ic.b, KT, lo, cnt);
-    ic.lo = lo;
-    ic.hi = lo + cnt;
+    seq_tiles(a, cur.b, KT, lo, cnt);
+    cur.lo = lo;
+    cur.hi = lo + cnt;
   }
-  Cursor cc = ic;
   auto advance = [&](Cursor& c) {
     if (++c.tile == c.hi) {
       if (++c.j == nkv) {
@@ -251,37 +225,102 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
     }
   };
 
-  // Issue step n (its tile is at cursor ic; the Q tile too if a segment starts
-  // there) and return the number of DMA blocks this wave issued for it.
-  int iseg = 0;
-  auto issue = [&](int n) -> int {
-    const size_t pair = (size_t)ic.b * nkv + ic.j;
-    int blocks = KVW;
-    if (n == 0 || ic.tile == ic.lo) {
-      const uint32_t qs = qlds0 + (uint32_t)(iseg % S) * QSLOT;
-      const void* qsrc = uniform_ptr(Qp + pair * R * D * sizeof(T));
+  // Step n lives in ring stage n % S. Barrier n (one per step) is passed once
+  // stage n has landed (the producers wait for it first) and the consumers
+  // have finished step n - 1, whose stage the producers refill right after it.
+  if (wave >= kConsumerWaves) {
+    // ---------------------------------------------------------- producers
+    const int pw = wave - kConsumerWaves;
+    const char* Kc = static_cast<const char*>(a.kc);
+    const char* Vc = static_cast<const char*>(a.vc);
+    const char* Qp = static_cast<const char*>(a.q);
+    // Source offsets (relative to the tile's first row) of this wave's 1 KB
+    // blocks i * kProducerWaves + pw; each lane fetches the chunk that belongs
+    // at its swizzled LDS position.
+    uint32_t kdma[KPP], vdma[KPP], qdma[QPP];
 #pragma unroll
-      for (int i = 0; i < QPW; ++i) lds_dma16<true>(qdma[i], qsrc, qs + (uint32_t)(i * 4 + wave_u) * 1024u);
-      ++iseg;
-      blocks += QPW;
+    for (int i = 0; i < KPP; ++i) {
+      const int blk = i * kProducerWaves + pw, row = blk * (64 / CPR) + lane / CPR;
+      const int c = (lane % CPR) ^ kswz<T, CPR>(row);
+      kdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
     }
-    const uint32_t sl = lds0 + (uint32_t)(n % S) * TILE;
-    const void* kt = uniform_ptr(Kc + (pair * a.cap + (size_t)ic.tile * KT) * D * sizeof(T));
-    const void* vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)ic.tile * KT) * sizeof(T));
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) lds_dma16<true>(kdma[i], kt, sl + (uint32_t)(i * 4 + wave_u) * 1024u);
+    for (int i = 0; i < KPP; ++i) {
+      const int blk = i * kProducerWaves + pw, row = blk * (64 / VCPR) + lane / VCPR;
+      const int c = (lane % VCPR) ^ rswz<VCPR>(row);
+      vdma[i] = (uint32_t)(row * a.cap + c * E) * (uint32_t)sizeof(T);
+    }
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) lds_dma16<true>(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * 4 + wave_u) * 1024u);
-    advance(ic);
-    return blocks;
-  };
+    for (int i = 0; i < QPP; ++i) {
+      const int blk = i * kProducerWaves + pw, row = blk * (64 / CPR) + lane / CPR;
+      const int c = (lane % CPR) ^ rswz<CPR>(row);
+      qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
+    }
+    // Issue step n (its tile is at the cursor; the Q tile too if a segment
+    // starts there) and return the number of DMA blocks this wave issued.
+    int iseg = 0;
+    auto issue = [&](int n) -> int {
+      const size_t pair = (size_t)cur.b * nkv + cur.j;
+      int blocks = 2 * KPP;
+      if (n == 0 || cur.tile == cur.lo) {
+        const uint32_t qs = qlds0 + (uint32_t)(iseg % S) * QSLOT;
+        const void* qsrc = uniform_ptr(Qp + pair * R * D * sizeof(T));
+#pragma unroll
+        for (int i = 0; i < QPP; ++i)
+          lds_dma16<true>(qdma[i], qsrc, qs + (uint32_t)(i * kProducerWaves + pw) * 1024u);
+        ++iseg;
+        blocks += QPP;
+      }
+      const uint32_t sl = lds0 + (uint32_t)(n % S) * TILE;
+      const void* kt = uniform_ptr(Kc + (pair * a.cap + (size_t)cur.tile * KT) * D * sizeof(T));
+      const void* vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)cur.tile * KT) * sizeof(T));
+#pragma unroll
+      for (int i = 0; i < KPP; ++i)
+        lds_dma16<true>(kdma[i], kt, sl + (uint32_t)(i * kProducerWaves + pw) * 1024u);
+#pragma unroll
+      for (int i = 0; i < KPP; ++i)
+        lds_dma16<true>(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * kProducerWaves + pw) * 1024u);
+      advance(cur);
+      return blocks;
+    };
+    // Steps 0 .. S-2 go out before the first barrier; `pending` is the number
+    // of blocks issued after the step the next wait is for.
+    int sizes[S - 1];
+#pragma unroll
+    for (int n = 0; n < S - 1; ++n) sizes[n] = n < total ? issue(n) : 0;
+    int pending = S >= 3 ? sizes[S - 2] : 0;
+    for (int it = 0; it < total; ++it) {
+      vm_wait<2 * KPP, QPP>(pending);
+      block_barrier();
+      int next = 0;
+      if (it + S - 1 < total) next = issue(it + S - 1);
+      pending = S >= 3 ? next : 0;
+    }
+    return;
+  }
 
-  // Prologue: steps 0 .. S-2 in flight. `pending` holds the DMA blocks of the
-  // steps issued after the one the loop waits for next.
-  int sizes[S - 1];
+  // ------------------------------------------------------------ consumers
+  const int q = lane >> 4, r16 = lane & 15;
+  const int g = a.nq / nkv;
+  const bool active = wave * 16 < R;
+  const int qrow = wave * 16 + r16;
+  const bool qvalid = qrow < R;
+
+  // Per-lane LDS byte offsets, fixed for the whole kernel: K operand of block
+  // kb, chunk c = koff[c] + kb_off(kb); V^T operand of d-block db, key chunk
+  // ks = voff[ks] + db_off(db); Q row chunks.
+  uint32_t koff[NC], voff[NKS], qoff[NC];
+  {
+    const int krow = key_of<T>(0, r16), ksw = kswz<T, CPR>(krow);
 #pragma unroll
-  for (int n = 0; n < S - 1; ++n) sizes[n] = n < total ? issue(n) : 0;
-  int pending = S >= 3 ? sizes[S - 2] : 0;
+    for (int c = 0; c < NC; ++c) koff[c] = (uint32_t)(krow * CPR + ((4 * c + q) ^ ksw)) * 16u;
+    const int vsw = rswz<VCPR>(r16);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) voff[ks] = (uint32_t)(r16 * VCPR + ((4 * ks + q) ^ vsw)) * 16u + K_BYTES;
+    const int qsw = rswz<CPR>(qrow);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qoff[c] = (uint32_t)(qrow * CPR + ((4 * c + q) ^ qsw)) * 16u;
+  }
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 acc[DB];
@@ -292,20 +331,13 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
   int tb = 0, qpos = 0;
 
   for (int it = 0; it < total; ++it) {
-    vm_wait<KVW, QPW>(pending);
     block_barrier();
-    const bool seg_begin = it == 0 || cc.tile == cc.lo;
-    const bool seg_end = it + 1 == total || cc.tile + 1 == cc.hi;
-    // A step that ends a segment stores its result before issuing the next
-    // DMA: the wait counter retires in issue order, so stores issued after a
-    // stage's loads would hold up the wait for that stage.
-    const bool more = it + S - 1 < total;
-    int next = 0;
-    if (more && !seg_end) next = issue(it + S - 1);
+    const bool seg_begin = it == 0 || cur.tile == cur.lo;
+    const bool seg_end = it + 1 == total || cur.tile + 1 == cur.hi;
     if (seg_begin) {
       seg_start_flat = it;
-      seg_from_lo = cc.tile == cc.lo;
-      tb = a.seq.len[cc.b] + (a.seq.ctx_off[cc.b + 1] - a.seq.ctx_off[cc.b]) + a.bs;
+      seg_from_lo = cur.tile == cur.lo;
+      tb = a.seq.len[cur.b] + (a.seq.ctx_off[cur.b + 1] - a.seq.ctx_off[cur.b]) + a.bs;
       qpos = tb - a.bs + (qvalid ? qrow / g : 0);
       if (active) {
         const uint32_t qs = qlds0 + (uint32_t)(cseg % S) * QSLOT;
@@ -321,27 +353,44 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
 
     if (active) {
       const uint32_t sl = lds0 + (uint32_t)(it % S) * TILE;
-      const int t0 = cc.tile * KT;
+      const int t0 = cur.tile * KT;
+      // Every K fragment of the tile is read before the first MFMA, and the
+      // MFMAs cycle over the KB independent accumulators, so LDS latency is
+      // paid once per tile rather than once per MFMA.
+      u32x4 kf[KB][NC];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          kf[kb][c] = lds_read16(sl + koff[c] + (uint32_t)(key_of<T>(kb, 0) * CPR * 16));
       f32x4 s[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t kbo = (uint32_t)(key_of<T>(kb, 0) * CPR * 16);
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) Mfma<T>::chunk(s[kb], lds_read16(sl + koff[c] + kbo), qf[c]);
-      }
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Mfma<T>::chunk(s[kb], kf[kb][c], qf[c]);
+      // The V^T fragments are read now and land while the softmax runs.
+      u32x4 vf[DB][NKS];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          vf[db][ks] = lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16));
       if (t0 + KT > tb || a.window > 0) {
+        // Key t survives if t < T_b and, under a window W, -W < qpos - t < W,
+        // i.e. 0 <= qpos - t + W - 1 <= 2W - 2 as one unsigned compare (the
+        // host passes W < capacity, so nothing wraps; without a window the
+        // limit admits every key).
+        const uint32_t wlim = a.window > 0 ? (uint32_t)(2 * a.window - 2) : 0xffffffffu;
+        const uint32_t wbias = a.window > 0 ? (uint32_t)(a.window - 1) : 0u;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = t0 + key_of<T>(kb, 4 * q + r);
-            bool ok = key < tb;
-            if (a.window > 0) {
-              const int dlt = qpos - key;
-              ok = ok && (dlt < a.window) && (-dlt < a.window);
-            }
-            if (!ok) s[kb][r] = kNegInf;
+            const bool ok = (key < tb) & ((uint32_t)(qpos - key) + wbias <= wlim);
+            s[kb][r] = ok ? s[kb][r] : kNegInf;
           }
       }
       float mx = kNegInf;
@@ -376,28 +425,26 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack_p_bf16(p[2 * ks], p[2 * ks + 1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            Mfma<T>::chunk(acc[db], lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16)), pf[ks]);
+          for (int db = 0; db < DB; ++db) Mfma<T>::chunk(acc[db], vf[db][ks], pf[ks]);
       } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            Mfma<T>::chunk(acc[db], lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16)),
-                           __builtin_bit_cast(u32x4, p[ks]));
+          for (int db = 0; db < DB; ++db)
+            Mfma<T>::chunk(acc[db], vf[db][ks], __builtin_bit_cast(u32x4, p[ks]));
       }
 
       if (seg_end) {
         const float lt = sum4(l_run);
-        const bool full = seg_from_lo && cc.tile + 1 == cc.hi;
+        const bool full = seg_from_lo && cur.tile + 1 == cur.hi;
         if (qvalid) {
           if (full) {
             const float inv = 1.0f / lt;
             const int i = qrow / g, hh = qrow % g;
             T* orow = static_cast<T*>(a.o) +
-                      ((size_t)(cc.b * a.bs + i) * a.nq + (size_t)(cc.j * g + hh)) * D;
+                      ((size_t)(cur.b * a.bs + i) * a.nq + (size_t)(cur.j * g + hh)) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) store4<T>(orow + db * 16 + 4 * q, acc[db] * inv);
           } else {
@@ -414,11 +461,8 @@ __global__ __launch_bounds__(256, 1) void attn_splitkv_kernel(AttnArgs a) {
         }
       }
     }
-    if (more && seg_end) next = issue(it + S - 1);
-    pending = S >= 3 ? next : 0;
-    advance(cc);
+    advance(cur);
   }
-
 }
 
 // HK4: one work-group column per split pair (host list), one thread per four
@@ -489,7 +533,7 @@ int attn_key_tile(int dtype, int head_dim) {
 
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream) {
   if (args.G <= 0) return hipSuccess;
-  const dim3 grid(args.G), block(256);
+  const dim3 grid(args.G), block(kAttnThreads);
   if (dtype == 1) {
     if (head_dim == 128)
       hipLaunchKernelGGL((attn_splitkv_kernel<__bf16, 128>), grid, block, 0, stream, args);

@@ -331,7 +331,8 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   aa.part_o = reinterpret_cast<float*>(ws + wc.part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + wc.part_ml);
   aa.nq = nq; aa.nkv = nkv; aa.bs = bs; aa.R = R; aa.cap = cache->capacity;
-  aa.window = c.sliding_window;
+  // A window at least the capacity keeps every key (|query - key| < T_b <= capacity).
+  aa.window = c.sliding_window >= cache->capacity ? 0 : c.sliding_window;
   aa.total_tiles = n_tiles;
   aa.G = (int32_t)attn_groups(L, n_tiles);
   aa.seq = seq;
