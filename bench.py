@@ -17,8 +17,9 @@ lengths (host-only) so that every step sees the same workload.
 
 Prints ONE JSON line. ``value`` is draft-block tokens/s (B*bs per step);
 ``roofline`` covers the attention kernel (HBM-bound): algorithmic bytes per
-launch (K and V rows once, Q and O once) over its mean launch time measured
-with HIP events on the launch stream over the timed region.
+launch (K and V rows once, Q and O once) over its mean launch time, measured
+with HIP events on the launch stream in a second pass of the same K steps
+(events are kept out of the timed region that gives ``value``).
 """
 from __future__ import annotations
 
@@ -181,13 +182,20 @@ def main():
     if layer.poll_error() != 0:
         raise RuntimeError("position outside the RoPE table during warm-up")
 
-    layer.set_profiling(True)
+    # Timed region: K steps with nothing but the steps themselves enqueued.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
         one_step(a.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # Per-kernel durations: the same K steps again with HIP events recorded
+    # around every launch on the launch stream (kept out of the timed region).
+    layer.set_profiling(True)
+    for i in range(a.steps):
+        one_step(a.warmup + a.steps + i)
+    torch.cuda.synchronize()
     kt = layer.kernel_times()
     layer.set_profiling(False)
 
