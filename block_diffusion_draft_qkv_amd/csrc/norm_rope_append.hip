@@ -1,7 +1,8 @@
 // HK2: per-head RMSNorm, RoPE, query packing and KV-cache append.
 //
-// Grid: one column per (sequence b, KV head j); along y, slices of 16 (d=128)
-// or 32 (d=64) rows, then the value tiles. For its pair the column
+// Grid: one column per (sequence b, KV head j); along y, first the value
+// tiles (dispatched first: they take longest), then slices of 16 (d=128) or
+// 32 (d=64) key/query rows. For its pair the column
 //   * takes the new key rows of the window [context (n_b rows) | block (bs)]
 //     from the fp32 projections (summing the GEMM's k slices), RMS-normalises each over head_dim with the
 //     k_norm gain, rotates it at its own window position and stores it as
@@ -35,14 +36,18 @@ __device__ inline float head_sum(float v) {
   return v;
 }
 
+// Row slots per wave: a key/query work-group takes 4 * kNormSlots * (128 / D)
+// rows, all of whose loads go out before any is used.
+constexpr int kNormSlots = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, int yk) {
+__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, int yv) {
   constexpr int HALF = D / 2;            // lanes per row
   constexpr int RPW = 64 / HALF;         // rows per wave slot
-  constexpr int SLOTS = 4;               // row slots per wave, loads hoisted over all of them
+  constexpr int SLOTS = kNormSlots;
   constexpr int WG_ROWS = 4 * SLOTS * RPW;
   constexpr int VT = 64;                 // value rows per transpose tile
-  __shared__ float vt[D][VT + 1];
+  __shared__ T vt[D][VT + 2];            // values in the cache type (padding spreads banks)
 
   const int nkv = a.nkv, nq = a.nq, bs = a.bs, g = nq / nkv;
   const int b = blockIdx.x / nkv, j = blockIdx.x % nkv;
@@ -54,36 +59,51 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   const size_t ld_blk = (size_t)(nq + 2 * nkv) * D, ld_ctx = (size_t)2 * nkv * D;
   const size_t pair = (size_t)b * nkv + j;
 
-  if ((int)blockIdx.y < yk) {
+  if ((int)blockIdx.y >= yv) {
     // Rows of this work-group: jobs [0, nnew) are key rows (context then
     // block), [nnew, nnew + R) are query rows (i, hh) = divmod(job - nnew, g).
-    const int base = blockIdx.y * WG_ROWS + wave * SLOTS * RPW + sub;
-    if (blockIdx.y * WG_ROWS >= nnew + R) return;
+    const int yk = (int)blockIdx.y - yv;
+    const int base = yk * WG_ROWS + wave * SLOTS * RPW + sub;
+    if (yk * WG_ROWS >= nnew + R) return;
     float x1[SLOTS], x2[SLOTS];
     int pidx[SLOTS], kind[SLOTS];  // kind: 0 none, 1 key, 2 query
+    const float* src[SLOTS];
+    int64_t stride[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int r = base + s * RPW;
-      const float* src = a.qkv;  // any valid address for idle slots
+      src[s] = a.qkv;  // any valid address for idle slots
+      stride[s] = a.qkv_slice;
       kind[s] = 0;
       pidx[s] = pos_off;
       if (r < nnew) {
         kind[s] = 1;
-        src = r < n ? a.ctxkv + (size_t)(c0 + r) * ld_ctx + (size_t)j * D
-                    : a.qkv + (size_t)(b * bs + r - n) * ld_blk + (size_t)(nq + j) * D;
+        if (r < n) {
+          src[s] = a.ctxkv + (size_t)(c0 + r) * ld_ctx + (size_t)j * D;
+          stride[s] = a.ctx_slice;
+        } else {
+          src[s] = a.qkv + (size_t)(b * bs + r - n) * ld_blk + (size_t)(nq + j) * D;
+        }
         pidx[s] = pos_off + r;
       } else if (r - nnew < R) {
         kind[s] = 2;
         const int i = (r - nnew) / g, hh = (r - nnew) % g;
-        src = a.qkv + (size_t)(b * bs + i) * ld_blk + (size_t)(j * g + hh) * D;
+        src[s] = a.qkv + (size_t)(b * bs + i) * ld_blk + (size_t)(j * g + hh) * D;
         pidx[s] = pos_off + n + i;  // queries sit at the window's suffix
       }
-      const int64_t stride = kind[s] == 1 && r < n ? a.ctx_slice : a.qkv_slice;
-      x1[s] = 0.f;
-      x2[s] = 0.f;
-      for (int sl = 0; sl < a.kslices; ++sl) {
-        x1[s] += src[sl * stride + t];
-        x2[s] += src[sl * stride + t + HALF];
+    }
+    // Every slot's first k slice goes out before any is used; further slices
+    // (small-M projections split k) are added afterwards.
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      x1[s] = src[s][t];
+      x2[s] = src[s][t + HALF];
+    }
+    for (int sl = 1; sl < a.kslices; ++sl) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        x1[s] += src[s][sl * stride[s] + t];
+        x2[s] += src[s][sl * stride[s] + t + HALF];
       }
     }
     int p[SLOTS];
@@ -133,27 +153,54 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   // contiguous) through LDS; the first tile's work-group also zeroes V from
   // T_b to the end of its 64-key tile, which the attention kernel reads whole
   // and needs finite there (those keys meet zero weights).
-  const int r0 = ((int)blockIdx.y - yk) * VT;
+  const int r0 = (int)blockIdx.y * VT;
   if (r0 >= nnew) return;
   const int nr = nnew - r0 < VT ? nnew - r0 : VT;
-  for (int rb = wave * RPW + sub; rb < nr; rb += 4 * RPW) {
-    const int rr = r0 + rb;
-    const float* src = rr < n ? a.ctxkv + (size_t)(c0 + rr) * ld_ctx + (size_t)(nkv + j) * D
-                              : a.qkv + (size_t)(b * bs + rr - n) * ld_blk + (size_t)(nq + nkv + j) * D;
-    const int64_t stride = rr < n ? a.ctx_slice : a.qkv_slice;
-    float v1 = 0.f, v2 = 0.f;
-    for (int sl = 0; sl < a.kslices; ++sl) {
-      v1 += src[sl * stride + t];
-      v2 += src[sl * stride + t + HALF];
+  // Each wave takes rows wave*RPW + sub + k*4*RPW; all of a lane's loads go
+  // out before the first LDS write.
+  constexpr int VROWS = VT / (4 * RPW);
+  const float* vsrc[VROWS];
+  int64_t vstride[VROWS];
+  float v1[VROWS], v2[VROWS];
+#pragma unroll
+  for (int k = 0; k < VROWS; ++k) {
+    const int rb = wave * RPW + sub + k * 4 * RPW, rr = r0 + rb;
+    vsrc[k] = a.qkv;  // any valid address for rows past the tile
+    vstride[k] = a.qkv_slice;
+    if (rb < nr) {
+      if (rr < n) {
+        vsrc[k] = a.ctxkv + (size_t)(c0 + rr) * ld_ctx + (size_t)(nkv + j) * D;
+        vstride[k] = a.ctx_slice;
+      } else {
+        vsrc[k] = a.qkv + (size_t)(b * bs + rr - n) * ld_blk + (size_t)(nq + nkv + j) * D;
+      }
     }
-    vt[t][rb] = v1;
-    vt[t + HALF][rb] = v2;
+  }
+#pragma unroll
+  for (int k = 0; k < VROWS; ++k) {
+    v1[k] = vsrc[k][t];
+    v2[k] = vsrc[k][t + HALF];
+  }
+  for (int sl = 1; sl < a.kslices; ++sl) {
+#pragma unroll
+    for (int k = 0; k < VROWS; ++k) {
+      v1[k] += vsrc[k][sl * vstride[k] + t];
+      v2[k] += vsrc[k][sl * vstride[k] + t + HALF];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < VROWS; ++k) {
+    const int rb = wave * RPW + sub + k * 4 * RPW;
+    if (rb < nr) {
+      vt[t][rb] = Elem<T>::from_f32(v1[k]);
+      vt[t + HALF][rb] = Elem<T>::from_f32(v2[k]);
+    }
   }
   __syncthreads();
   T* vdst = static_cast<T*>(a.vc) + pair * D * a.cap + L;
   for (int idx = tid; idx < D * nr; idx += 256) {
     const int dd = idx / nr, rr = idx % nr;
-    vdst[(size_t)dd * a.cap + r0 + rr] = Elem<T>::from_f32(vt[dd][rr]);
+    vdst[(size_t)dd * a.cap + r0 + rr] = vt[dd][rr];
   }
   if (r0 == 0) {
     T* vpad = static_cast<T*>(a.vc) + pair * D * a.cap;
@@ -171,21 +218,21 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
                             int max_new_rows, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const int wg_rows = 4 * 4 * (128 / head_dim);
+  const int wg_rows = 4 * kNormSlots * (128 / head_dim);
   const int R = args.bs * (args.nq / args.nkv);
   const int yk = (max_new_rows + R + wg_rows - 1) / wg_rows;
   const int yv = (max_new_rows + 63) / 64;
-  const dim3 g(grid, yk + yv), blk(256);
+  const dim3 g(grid, yv + yk), blk(256);
   if (dtype == 1) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 128>), g, blk, 0, stream, args, yk);
+      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 128>), g, blk, 0, stream, args, yv);
     else
-      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 64>), g, blk, 0, stream, args, yk);
+      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 64>), g, blk, 0, stream, args, yv);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), g, blk, 0, stream, args, yk);
+      hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), g, blk, 0, stream, args, yv);
     else
-      hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), g, blk, 0, stream, args, yk);
+      hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), g, blk, 0, stream, args, yv);
   }
   return hipGetLastError();
 }
