@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=3, help="KV-cache copies rotated across steps")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="sequences of the workload the oracle is timed on (0: skip)")
+    ap.add_argument("--append-mode", default="auto", choices=("auto", "fused", "separate"),
+                    help="where q/k norm + RoPE + cache append run (projection epilogue or own kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -147,6 +149,7 @@ def main():
     layer = DFlashLayer(LayerShape(H, nq, nkv, d, bs, dt, cfg.rope_theta, cfg.rms_eps,
                                    cfg.sliding_window, cfg.max_position),
                         dev(w.w_qkv), dev(w.w_o), dev(w.q_norm), dev(w.k_norm))
+    layer.set_append_mode(a.append_mode)
     cap = case.capacity()
     caches = []
     for i in range(a.copies):
@@ -237,7 +240,7 @@ def main():
                          f"{cfg.cached_len}, new ctx {cfg.new_ctx}, block {bs}, H={H}, "
                          f"{nq}/{nkv} heads, head_dim {d}, window {cfg.sliding_window or 'none'}"),
             "batch": B, "block_size": bs, "total_keys": int(T.sum()), "new_ctx_rows": mc,
-            "seed": a.seed, "kv_cache_copies": a.copies,
+            "seed": a.seed, "kv_cache_copies": a.copies, "append_mode": a.append_mode,
         },
         "roofline": {
             "bound": "hbm",

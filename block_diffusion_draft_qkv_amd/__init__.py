@@ -155,6 +155,11 @@ class DFlashLayer:
     def poll_error(self, stream=None) -> int:
         return int(_lib.lib().dflash_layer_poll_error(self._h, _stream_handle(stream)))
 
+    def set_append_mode(self, mode: str) -> None:
+        """Where q/k are normalised and rotated and the cache rows appended:
+        ``"auto"`` (default), ``"fused"`` (projection epilogue) or ``"separate"``."""
+        check(_lib.lib().dflash_layer_set_append_mode(self._h, _lib.APPEND_MODES[mode]), "set_append_mode")
+
     def set_profiling(self, enable: bool) -> None:
         check(_lib.lib().dflash_layer_set_profiling(self._h, int(bool(enable))), "set_profiling")
 

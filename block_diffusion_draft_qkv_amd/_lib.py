@@ -23,6 +23,7 @@ DFLASH_ERR_WORKSPACE = 7
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
 DFLASH_MAX_BATCH = 256
+APPEND_MODES = {"auto": 0, "fused": 1, "separate": 2}
 KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o")
 
 # Every symbol include/dflash.h declares.
@@ -30,6 +31,7 @@ EXPORTS = (
     "dflash_layer_create", "dflash_layer_destroy", "dflash_workspace_bytes",
     "dflash_attn_step", "dflash_cache_crop", "dflash_layer_poll_error",
     "dflash_layer_set_profiling", "dflash_layer_kernel_times", "dflash_status_string",
+    "dflash_layer_set_append_mode",
 )
 
 
@@ -80,6 +82,8 @@ def lib() -> C.CDLL:
         h.dflash_cache_crop.restype = C.c_int
         h.dflash_layer_poll_error.argtypes = [C.c_void_p, C.c_void_p]
         h.dflash_layer_poll_error.restype = C.c_int
+        h.dflash_layer_set_append_mode.argtypes = [C.c_void_p, C.c_int32]
+        h.dflash_layer_set_append_mode.restype = C.c_int
         h.dflash_layer_set_profiling.argtypes = [C.c_void_p, C.c_int32]
         h.dflash_layer_set_profiling.restype = C.c_int
         h.dflash_layer_kernel_times.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]

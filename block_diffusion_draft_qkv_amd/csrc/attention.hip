@@ -43,9 +43,9 @@
 // The exponent offset of a row is raised only when the row maximum passes it
 // by more than kRescaleSlack (log2 units), so O is rescaled rarely; the result
 // is exact for any offset because O and the sum share it.
-// Keys past T_b inside the last tile are masked out of the softmax; the append
-// kernel zero-fills V up to the next multiple of 64 keys, so those keys also
-// contribute exact zeros to P.V whatever the dead rows held.
+// Keys past T_b inside the last tile are masked out of the softmax, and their
+// V elements are zeroed in registers, so those keys contribute exact zeros to
+// P.V whatever the dead rows of the cache hold.
 #include "kernels.h"
 #include "lds_dma.h"
 
@@ -149,6 +149,21 @@ __device__ inline float sum4(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Bit mask keeping the first n (< elements per chunk) elements of a 16-byte chunk.
+template <typename T> __device__ inline u32x4 keep_mask(int n);
+template <> __device__ inline u32x4 keep_mask<__bf16>(int n) {
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m[w] = (2 * w < n ? 0x0000ffffu : 0u) | (2 * w + 1 < n ? 0xffff0000u : 0u);
+  return m;
+}
+template <> __device__ inline u32x4 keep_mask<float>(int n) {
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m[w] = w < n ? 0xffffffffu : 0u;
+  return m;
 }
 
 __device__ inline u32x4 pack_p_bf16(const f32x4& p0, const f32x4& p1) {
@@ -377,6 +392,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
           vf[db][ks] = lds_read16(sl + voff[ks] + (uint32_t)(db * 16 * VCPR * 16));
+      if (t0 + KT > tb) {
+        // Keys at or past T_b get zero weight, but the cache there may hold
+        // anything (not even a number): zero those V elements so that 0 * V
+        // stays 0. Chunk 4ks + q of a V^T row holds keys (4ks + q) * E ...
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int nvalid = tb - (t0 + (4 * ks + q) * E);
+          if (nvalid < E) {
+            const u32x4 keep = keep_mask<T>(nvalid);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vf[db][ks] &= keep;
+          }
+        }
+      }
       if (t0 + KT > tb || a.window > 0) {
         // Key t survives if t < T_b and, under a window W, -W < qpos - t < W,
         // i.e. 0 <= qpos - t + W - 1 <= 2W - 2 as one unsigned compare (the

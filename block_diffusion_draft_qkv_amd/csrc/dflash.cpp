@@ -2,7 +2,8 @@
 // the RoPE table, workspace carving and the kernel sequence of one step.
 //
 // One step, all on the caller's stream:
-//   HK1 grouped GEMM   block rows -> q|k|v, context rows -> k|v (fp32 out)
+//   HK1 grouped GEMM   block rows -> q|k|v, context rows -> k|v; with enough
+//                      tiles its epilogue also does HK2's work, else fp32 out
 //   HK2 norm_rope      per-head RMSNorm + RoPE + Q pack + cache append
 //   HK3 attention      split-KV non-causal GQA over the cache
 //   HK4 merge          the pairs HK3 split over several work-groups
@@ -47,6 +48,7 @@ struct dflash_layer {
   float* cos_sin = nullptr;  // [max_pos][d/2] cos, then [max_pos][d/2] sin
   int32_t* err = nullptr;
   bool profiling = false;
+  int append_mode = DFLASH_APPEND_AUTO;
   std::vector<Pending> pending;
   std::vector<hipEvent_t> event_pool;
   double ms[DFLASH_K_COUNT] = {};
@@ -277,8 +279,15 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   const int Mq = B * bs, H = c.hidden;
   const int Nqkv = (nq + 2 * nkv) * d, Nkv = 2 * nkv * d;
 
-  // HK1: block q|k|v and context k|v in one launch.
-  const TileChoice tq = choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
+  // HK1: block q|k|v and context k|v in one launch; with the append fused into
+  // its epilogue (one head per tile, no k split) it also does HK2's work.
+  const int nt64 = ((Mq + 63) / 64) * (Nqkv / d) + (int)((Mc + 63) / 64) * (Nkv / d);
+  const int nt128 = ((Mq + 127) / 128) * (Nqkv / d) + (int)((Mc + 127) / 128) * (Nkv / d);
+  const int target = L->num_cus * 3 / 4;
+  const bool fused = L->append_mode == DFLASH_APPEND_FUSED ||
+                     (L->append_mode == DFLASH_APPEND_AUTO && nt64 >= target);
+  const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, nt128 >= target ? nt128 : nt64, 1}
+                              : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.nprob = 1;
@@ -291,13 +300,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
                (int64_t)Mc * Nkv};
     ga.nprob = 2;
   }
-  hipEvent_t ev;
-  record(L, &ev, s);
-  if (launch_gemm(c.dtype, true, ga, tq.tiles, tq.bm, tq.bn, tq.kslices, s) != hipSuccess)
-    return DFLASH_ERR_HIP;
-  record_end(L, DFLASH_K_GEMM_QKV, ev, s);
-
-  // HK2
+  // HK2 (or the fused epilogue)
   NormRopeArgs na;
   na.qkv = qkv;
   na.ctxkv = ctxkv;
@@ -316,11 +319,21 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   na.eps = (float)c.rms_eps;
   na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   na.seq = seq;
+  hipEvent_t ev;
   record(L, &ev, s);
-  int max_new = 0;
-  for (int b = 0; b < B; ++b) max_new = std::max(max_new, ctx_offsets[b + 1] - ctx_offsets[b] + bs);
-  if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, s) != hipSuccess) return DFLASH_ERR_HIP;
-  record_end(L, DFLASH_K_NORM_ROPE, ev, s);
+  if (fused) {
+    if (launch_gemm_append(c.dtype, d, ga, na, tq.tiles, tq.bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+    record_end(L, DFLASH_K_GEMM_QKV, ev, s);
+  } else {
+    if (launch_gemm(c.dtype, true, ga, tq.tiles, tq.bm, tq.bn, tq.kslices, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    record_end(L, DFLASH_K_GEMM_QKV, ev, s);
+    record(L, &ev, s);
+    int max_new = 0;
+    for (int b = 0; b < B; ++b) max_new = std::max(max_new, ctx_offsets[b + 1] - ctx_offsets[b] + bs);
+    if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, s) != hipSuccess) return DFLASH_ERR_HIP;
+    record_end(L, DFLASH_K_NORM_ROPE, ev, s);
+  }
 
   // HK3 (+ HK4)
   AttnArgs aa;
@@ -411,6 +424,12 @@ int dflash_layer_poll_error(dflash_layer* L, void* stream) {
     if (hipMemset(L->err, 0, sizeof(int32_t)) != hipSuccess) return DFLASH_ERR_HIP;
     return DFLASH_ERR_RANGE;
   }
+  return DFLASH_OK;
+}
+
+int dflash_layer_set_append_mode(dflash_layer* L, int32_t mode) {
+  if (!L || mode < DFLASH_APPEND_AUTO || mode > DFLASH_APPEND_SEPARATE) return DFLASH_ERR_ARG;
+  L->append_mode = mode;
   return DFLASH_OK;
 }
 

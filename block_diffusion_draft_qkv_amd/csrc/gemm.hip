@@ -17,6 +17,8 @@
 // so results store as 16-byte (fp32) or 8-byte (bf16) runs. An optional split
 // of k over gridDim.y writes fp32 partial sums;
 // their consumer adds the slices (slice s of a problem at C + s * slice_stride).
+#include <type_traits>
+
 #include "kernels.h"
 #include "lds_dma.h"
 
@@ -68,28 +70,37 @@ template <int PER, int S> __device__ inline void stage_wait(int n) {
   DFLASH_VMWAIT(0);
 }
 
-template <typename T, typename OutT, int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
+// The tile of one work-group: which problem, where, and which k steps.
+struct TileJob {
+  GemmProblem P;
+  bool second;
+  int m0, n0, k_first, nk;
+};
+template <int BM, int BN> __device__ inline TileJob tile_job(const GemmArgs& args) {
+  TileJob t;
+  int tile = blockIdx.x;
+  t.second = args.nprob > 1 && tile >= args.p[1].tile_begin;
+  t.P = t.second ? args.p[1] : args.p[0];
+  tile -= t.P.tile_begin;
+  t.m0 = (tile / t.P.tiles_n) * BM;
+  t.n0 = (tile % t.P.tiles_n) * BN;
+  return t;
+}
+
+// Main loop shared by the plain and the appending GEMM. Producers return
+// false after `extra` more barriers (those of the caller's epilogue);
+// consumers return true with their sub-tile in acc.
+template <typename T, int BM, int BN>
+__device__ __forceinline__ bool gemm_core(const TileJob& J, uint32_t lds0, int extra,
+                                          f32x4 (&acc)[GemmShape<BM, BN>::NI][GemmShape<BM, BN>::MI]) {
   using Sh = GemmShape<BM, BN>;
   constexpr int S = Sh::S, STAGE = Sh::STAGE, A_BYTES = Sh::A_BYTES;
   constexpr int APP = Sh::APP, BPP = Sh::BPP, PER = Sh::PER;
   constexpr int WM = Sh::WM, WN = Sh::WN, MI = Sh::MI, NI = Sh::NI;
-  __shared__ u32x4 lds[S * STAGE / 16];
-
-  int tile = blockIdx.x;
-  const bool second = args.nprob > 1 && tile >= args.p[1].tile_begin;
-  const GemmProblem P = second ? args.p[1] : args.p[0];
-  tile -= P.tile_begin;
-  const int m0 = (tile / P.tiles_n) * BM;
-  const int n0 = (tile % P.tiles_n) * BN;
-  const int ksl = gridDim.y;                       // k slices
-  const int nk_all = P.k / (8 * (16 / (int)sizeof(T)));  // 128-byte k steps
-  const int k_first = (int)(((int64_t)nk_all * blockIdx.y) / ksl);
-  const int nk = (int)(((int64_t)nk_all * (blockIdx.y + 1)) / ksl) - k_first;
-
+  const GemmProblem& P = J.P;
+  const int m0 = J.m0, n0 = J.n0, k_first = J.k_first, nk = J.nk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t lds0 = lds_base(lds);
 
   // Step s lives in ring stage s % S. Barrier s is passed once stage s has
   // landed (the producers wait for it first) and the consumers have read every
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
       block_barrier();
       if (it + S - 1 < nk) issue(it + S - 1);
     }
-    return;
+    for (int e = 0; e < extra; ++e) block_barrier();
+    return false;
   }
 
   // ------------------------------------------------------------ consumers
@@ -156,8 +168,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
       brd[kb] = (uint32_t)((wn * WN + r16) * 8 + ((4 * kb + q) ^ sw)) * 16u + A_BYTES;
     }
   }
-
-  f32x4 acc[NI][MI];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -198,19 +208,261 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
     __builtin_amdgcn_sched_barrier(0);
   }
   if (nk > 0) mma(h1);
+  return true;
+}
 
+template <typename T, typename OutT, int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
+  using Sh = GemmShape<BM, BN>;
+  constexpr int WM = Sh::WM, WN = Sh::WN, MI = Sh::MI, NI = Sh::NI;
+  __shared__ u32x4 lds[Sh::S * Sh::STAGE / 16];
+  TileJob J = tile_job<BM, BN>(args);
+  const int ksl = gridDim.y;                                      // k slices
+  const int nk_all = J.P.k / (8 * (16 / (int)sizeof(T)));         // 128-byte k steps
+  J.k_first = (int)(((int64_t)nk_all * blockIdx.y) / ksl);
+  J.nk = (int)(((int64_t)nk_all * (blockIdx.y + 1)) / ksl) - J.k_first;
+  f32x4 acc[NI][MI];
+  if (!gemm_core<T, BM, BN>(J, lds_base(lds), 0, acc)) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
   // acc[ni][mi]: lane holds m = r16 of block mi and n = 4q .. 4q+3 of block ni.
-  OutT* C = static_cast<OutT*>(P.c) + (size_t)blockIdx.y * P.slice_stride;
+  OutT* C = static_cast<OutT*>(J.P.c) + (size_t)blockIdx.y * J.P.slice_stride;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    const int m = m0 + wm * WM + mi * 16 + r16;
-    if (m >= P.m) continue;
+    const int m = J.m0 + wm * WM + mi * 16 + r16;
+    if (m >= J.P.m) continue;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int n = n0 + wn * WN + ni * 16 + 4 * q;
-      if (n < P.n) Store4<OutT>::put(C + (size_t)m * P.ldc + n, acc[ni][mi]);
+      const int n = J.n0 + wn * WN + ni * 16 + 4 * q;
+      if (n < J.P.n) Store4<OutT>::put(C + (size_t)m * J.P.ldc + n, acc[ni][mi]);
     }
   }
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 that hold one row's columns.
+__device__ inline float quad_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// The q|k|v + context k|v projection with the work of the norm/RoPE/append
+// kernel in its epilogue (same definitions: NeMo page "draft_qwen3"
+// Qwen3DFlashAttention.forward and apply_rotary_pos_emb; "DFlash源码导读（二）"
+// sections 1-4). A tile is BM rows x one head (BN = D columns, no k split);
+// consumer wave (wm, wn) holds columns wn*D/2 .. wn*D/2 + D/2 - 1, so the
+// rotation partner of every value (t <-> t + D/2) sits in the same lane and
+// register of wave (wm, 1 - wn). After the main loop the two waves trade
+// halves through LDS (the ring is free by then) so that each finishes whole
+// rows of half the row blocks: the row's sum of squares (summed over the four
+// lanes of the row), RMSNorm with the head gain (and, for queries, the scale
+// head_dim^-1/2 log2 e), neox rotation at the row's position from the fp64-
+// built cos/sin table, and the stores: queries packed as rows i*g + hh of their
+// KV head's tile, keys to cache K, values (raw) transposed to cache V.
+// Positions outside the table are clamped and latched in the error flag.
+template <typename T, int BM, int D>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs args, NormRopeArgs a) {
+  using Sh = GemmShape<BM, D>;
+  constexpr int WM = Sh::WM, MI = Sh::MI, NI = Sh::NI, HALF = D / 2, REGS = MI * NI * 4;
+  static_assert(Sh::WN == HALF, "a tile holds one head");
+  static_assert(4 * REGS / 2 * 64 * 4 <= Sh::S * Sh::STAGE, "the exchange fits in the ring");
+  __shared__ u32x4 lds[Sh::S * Sh::STAGE / 16];
+  TileJob J = tile_job<BM, D>(args);
+  J.k_first = 0;
+  J.nk = J.P.k / (8 * (16 / (int)sizeof(T)));
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
+  const int nq = a.nq, nkv = a.nkv, bs = a.bs, g = nq / nkv, R = bs * g;
+  // The head of this tile: kind 0 query, 1 key, 2 value.
+  const int h = J.n0 / D;
+  int kind, j, hh = 0;
+  if (!J.second) {
+    kind = h < nq ? 0 : (h < nq + nkv ? 1 : 2);
+    j = kind == 0 ? h / g : (kind == 1 ? h - nq : h - nq - nkv);
+    hh = kind == 0 ? h % g : 0;
+  } else {
+    kind = h < nkv ? 1 : 2;
+    j = kind == 1 ? h : h - nkv;
+  }
+
+  // Consumers: this lane's rows (sequence, window row: context rows first,
+  // then block rows). After the swap below, wave (wm, wn) finishes whole rows
+  // of the row blocks wn*MH .. wn*MH + MH - 1; their positions are loaded
+  // before the main loop (nothing waits for them until the epilogue).
+  constexpr int MH = MI / 2;
+  int sb[MI], win[MI], crow[MI], pos[MH];  // sequence, window row, cache row; positions
+  bool ok[MI];
+  if (wave < kGemmConsumers) {
+    // The sequences a wave's rows touch are few and found with wave-uniform
+    // loops (scalar loads of the sequence table); each lane keeps its rows'.
+    const int r0 = J.m0 + wm * WM, rl = min(r0 + WM, J.P.m) - 1;
+    int pb[MI];  // first position index of the row's window
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      ok[mi] = r0 + mi * 16 + r16 <= rl;
+      sb[mi] = win[mi] = crow[mi] = pb[mi] = 0;
+    }
+    if (!J.second) {
+      for (int b = r0 / bs; b <= rl / bs; ++b) {
+        const int c0 = a.seq.ctx_off[b], c1 = a.seq.ctx_off[b + 1], L = a.seq.len[b];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int m = r0 + mi * 16 + r16;
+          if (ok[mi] && m / bs == b) {
+            sb[mi] = b;
+            win[mi] = (c1 - c0) + m % bs;
+            crow[mi] = L + win[mi];
+            pb[mi] = c0 + b * bs;
+          }
+        }
+      }
+    } else {
+      int lo = 0, hi = a.seq.batch;  // last b with ctx_off[b] <= r0
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.seq.ctx_off[mid] <= r0) lo = mid;
+        else hi = mid;
+      }
+      for (int b = lo; b < a.seq.batch && a.seq.ctx_off[b] <= rl; ++b) {
+        const int c0 = a.seq.ctx_off[b], L = a.seq.len[b];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int m = r0 + mi * 16 + r16;
+          if (ok[mi] && c0 <= m) {  // the last such b owns row m
+            sb[mi] = b;
+            win[mi] = m - c0;
+            crow[mi] = L + win[mi];
+            pb[mi] = c0 + b * bs;
+          }
+        }
+      }
+    }
+    if (kind != 2) {
+#pragma unroll
+      for (int u = 0; u < MH; ++u) {
+        // row block wn * MH + u, selected without indexing by a runtime value
+        const int pi = wn == 0 ? pb[u] + win[u] : pb[MH + u] + win[MH + u];
+        pos[u] = a.positions[pi];
+      }
+    }
+  }
+
+  f32x4 acc[NI][MI];
+  if (!gemm_core<T, BM, D>(J, lds_base(lds), 2, acc)) return;
+
+  float* xch = reinterpret_cast<float*>(lds);
+  constexpr int XR = MH * NI * 4;  // values one lane hands over
+  const int partner = wm * 2 + (1 - wn);
+  if (kind == 2) {
+    block_barrier();  // the epilogue's two barriers (no swap for values)
+    block_barrier();
+    // Values: raw, transposed into cache V (key index contiguous); each wave
+    // writes its own half of the columns for all its rows.
+    T* vbase = static_cast<T*>(a.vc);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (!ok[mi]) continue;
+      const int b = sb[mi];
+      const size_t col0 = ((size_t)(b * nkv + j) * D + wn * HALF) * a.cap + crow[mi];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vbase[col0 + (size_t)(ni * 16 + 4 * q + r) * a.cap] = Elem<T>::from_f32(acc[ni][mi][r]);
+    }
+    return;
+  }
+
+  // Queries and keys. WN is this wave's wn as a constant, so that the row
+  // blocks it finishes (WN * MH + u) index the register arrays statically.
+  auto finish = [&](auto wn_c) __attribute__((always_inline)) {
+    constexpr int WN = decltype(wn_c)::value;
+    // The head gains and cos/sin of this wave's rows go out now and arrive
+    // during the swap.
+    const T* gain = static_cast<const T*>(kind == 0 ? a.q_norm : a.k_norm);
+    T g1[NI][4], g2[NI][4];  // gains of columns t and t + D/2
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        g1[ni][r] = gain[ni * 16 + 4 * q + r];
+        g2[ni][r] = gain[HALF + ni * 16 + 4 * q + r];
+      }
+    const float* cos_t = a.cos_sin;
+    const float* sin_t = a.cos_sin + (size_t)a.max_pos * HALF;
+    f32x4 cs[MH][NI], sn[MH][NI];
+#pragma unroll
+    for (int u = 0; u < MH; ++u) {
+      const int mi = WN * MH + u;
+      int p = pos[u];
+      if (p < 0 || p >= a.max_pos) {
+        if (ok[mi] && q == 0) atomicOr(a.err, 1);
+        p = p < 0 ? 0 : a.max_pos - 1;
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        cs[u][ni] = *reinterpret_cast<const f32x4*>(cos_t + (size_t)p * HALF + ni * 16 + 4 * q);
+        sn[u][ni] = *reinterpret_cast<const f32x4*>(sin_t + (size_t)p * HALF + ni * 16 + 4 * q);
+      }
+    }
+    // Swap: hand the partner (wm, 1 - WN) this wave's half of the rows it
+    // finishes, then take the partner's half of this wave's rows.
+    block_barrier();  // the last fragment reads of the main loop are done
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int u = 0; u < MH; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          xch[(wave * XR + (ni * MH + u) * 4 + r) * 64 + lane] = acc[ni][(1 - WN) * MH + u][r];
+    block_barrier();
+
+    // Whole rows: RMSNorm over the head, then the rotation
+    // (t, t + D/2) -> (x1 cos - x2 sin, x2 cos + x1 sin).
+    const float scale = kind == 0 ? a.qscale : 1.0f;
+#pragma unroll
+    for (int u = 0; u < MH; ++u) {
+      const int mi = WN * MH + u;
+      const int b = sb[mi];
+      f32x4 x1[NI], x2[NI];
+      float ss = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float own = acc[ni][mi][r];
+          const float oth = xch[(partner * XR + (ni * MH + u) * 4 + r) * 64 + lane];
+          x1[ni][r] = WN == 0 ? own : oth;
+          x2[ni][r] = WN == 0 ? oth : own;
+          ss += own * own + oth * oth;
+        }
+      ss = quad_sum(ss);
+      const float inv = rsqrtf(ss * (1.0f / D) + a.eps) * scale;
+      if (!ok[mi]) continue;
+      T* dst;
+      if (kind == 0) {
+        const int i = (J.m0 + wm * WM + mi * 16 + r16) % bs;
+        dst = static_cast<T*>(a.qpack) + ((size_t)(b * nkv + j) * R + i * g + hh) * D;
+      } else {
+        dst = static_cast<T*>(a.kc) + ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D;
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        f32x4 o1, o2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float y1 = x1[ni][r] * inv * Elem<T>::to_f32(g1[ni][r]);
+          const float y2 = x2[ni][r] * inv * Elem<T>::to_f32(g2[ni][r]);
+          o1[r] = y1 * cs[u][ni][r] - y2 * sn[u][ni][r];
+          o2[r] = y2 * cs[u][ni][r] + y1 * sn[u][ni][r];
+        }
+        Store4<T>::put(dst + ni * 16 + 4 * q, o1);
+        Store4<T>::put(dst + HALF + ni * 16 + 4 * q, o2);
+      }
+    }
+  };
+  if (wn == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, 1>{});
 }
 
 template <typename T, typename OutT>
@@ -227,7 +479,28 @@ hipError_t launch_t(const GemmArgs& args, int total_tiles, int bm, int bn, int k
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_append_t(const GemmArgs& args, const NormRopeArgs& nr, int total_tiles, int bm, int d,
+                           hipStream_t s) {
+  const dim3 grid(total_tiles), block(kGemmThreads);
+  if (d == 128) {
+    if (bm == 128) hipLaunchKernelGGL((gemm_append_kernel<T, 128, 128>), grid, block, 0, s, args, nr);
+    else hipLaunchKernelGGL((gemm_append_kernel<T, 64, 128>), grid, block, 0, s, args, nr);
+  } else {
+    if (bm == 128) hipLaunchKernelGGL((gemm_append_kernel<T, 128, 64>), grid, block, 0, s, args, nr);
+    else hipLaunchKernelGGL((gemm_append_kernel<T, 64, 64>), grid, block, 0, s, args, nr);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,
+                              int total_tiles, int bm, hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  if (dtype == 1) return launch_append_t<__bf16>(args, nr, total_tiles, bm, head_dim, stream);
+  return launch_append_t<float>(args, nr, total_tiles, bm, head_dim, stream);
+}
 
 hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles, int bm, int bn,
                        int kslices, hipStream_t stream) {

@@ -56,6 +56,12 @@ struct NormRopeArgs {
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
                             int max_new_rows, hipStream_t stream);
 
+// The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
+// head_dim, no k split) doing the work of launch_norm_rope in its epilogue
+// (nr's qkv, ctxkv and kslices fields are unused).
+hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,
+                              int total_tiles, int bm, hipStream_t stream);
+
 // ------------------------------------------------------------------ attention
 // Flattened work: pairs (b, j) in b-major order, each owning the 64-key tiles
 // [lo_b, hi_b) of sequence b (lo_b > 0 only under a sliding window). Work-group

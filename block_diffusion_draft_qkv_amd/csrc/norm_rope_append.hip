@@ -14,8 +14,7 @@
 //     head_dim^-0.5 * log2(e) so that attention scores come out in the log2
 //     domain, and packs them as rows i*g + hh of the pair's query tile;
 //   * stores the raw value rows transposed into cache V (column L_b + r), via
-//     an LDS tile so that global writes run along the key axis, and zeroes V
-//     columns T_b .. (T_b rounded up to 64) - 1.
+//     an LDS tile so that global writes run along the key axis.
 // A work-group issues the loads of all its rows before using any (inputs and
 // positions, then the cos/sin rows those positions select), so each costs two
 // memory round trips whatever the row count.
@@ -150,9 +149,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   }
 
   // Values: raw rows of one 64-row tile, written transposed (key index
-  // contiguous) through LDS; the first tile's work-group also zeroes V from
-  // T_b to the end of its 64-key tile, which the attention kernel reads whole
-  // and needs finite there (those keys meet zero weights).
+  // contiguous) through LDS.
   const int r0 = (int)blockIdx.y * VT;
   if (r0 >= nnew) return;
   const int nr = nnew - r0 < VT ? nnew - r0 : VT;
@@ -201,15 +198,6 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   for (int idx = tid; idx < D * nr; idx += 256) {
     const int dd = idx / nr, rr = idx % nr;
     vdst[(size_t)dd * a.cap + r0 + rr] = vt[dd][rr];
-  }
-  if (r0 == 0) {
-    T* vpad = static_cast<T*>(a.vc) + pair * D * a.cap;
-    const int Tb = L + nnew;
-    const int pad = (Tb + 63) / 64 * 64 - Tb;
-    for (int idx = tid; idx < D * pad; idx += 256) {
-      const int dd = idx / pad, k = idx % pad;
-      vpad[(size_t)dd * a.cap + Tb + k] = Elem<T>::from_f32(0.f);
-    }
   }
 }
 

@@ -146,9 +146,9 @@ size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
  *                  latch DFLASH_ERR_RANGE for dflash_layer_poll_error.
  *   cache          rows [len_b, len_b + n_b + bs) of each sequence receive the
  *                  new context rows then the block rows; len_b then becomes
- *                  T_b = len_b + n_b + bs. V columns from T_b up to the next
- *                  multiple of 64 (dead rows) are set to zero; nothing else
- *                  in the cache is written.
+ *                  T_b = len_b + n_b + bs. Nothing else in the cache is
+ *                  written, and rows at or past a length are never used
+ *                  (they may hold anything, NaN included).
  *   out            device [B * bs, H]: o_proj of the attention output.
  *   workspace      device scratch of at least dflash_workspace_bytes(...)
  *                  bytes, 256-byte aligned; contents need no initialisation.
@@ -175,6 +175,20 @@ int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len);
  * error (DFLASH_ERR_RANGE if a position fell outside the table since the last
  * poll), or DFLASH_OK. */
 int dflash_layer_poll_error(dflash_layer* layer, void* stream);
+
+/* Where a step normalises and rotates q and k, packs the queries and appends
+ * the new rows to the cache (NeMo page "draft_qwen3": q_norm/k_norm and
+ * apply_rotary_pos_emb; "DFlash源码导读（二）" sections 1-4: cache update):
+ *   DFLASH_APPEND_AUTO      (default) in the epilogue of the q|k|v projection
+ *                           whenever that GEMM has enough tiles without
+ *                           splitting k, else in a separate kernel after it;
+ *   DFLASH_APPEND_FUSED     always in the projection's epilogue (never split k);
+ *   DFLASH_APPEND_SEPARATE  always in the separate kernel.
+ * The results agree up to the order of the fp32 sums of the projection. With
+ * the fused form the step's DFLASH_K_NORM_ROPE time is part of
+ * DFLASH_K_GEMM_QKV. Errors: DFLASH_ERR_ARG (null layer or unknown mode). */
+enum { DFLASH_APPEND_AUTO = 0, DFLASH_APPEND_FUSED = 1, DFLASH_APPEND_SEPARATE = 2 };
+int dflash_layer_set_append_mode(dflash_layer* layer, int32_t mode);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each
  * kernel of a step. enable != 0 turns it on (and clears the totals). */

@@ -103,9 +103,9 @@ def raw_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def check_cache_after_step(case: Case, cache, before_k, before_v, new_cache: oracle.OracleCache):
-    """New rows [L_b, T_b) match the oracle; rows < L_b and K rows >= T_b are
-    bit-identical to what they were, V columns [T_b, T_b rounded up to 64) are
-    zero and the rest bit-identical; lengths equal T_b exactly."""
+    """New rows [L_b, T_b) match the oracle; every other row of K and V (the
+    dead ones past T_b hold a NaN canary) is bit-identical to what it was;
+    lengths equal T_b exactly."""
     L, T = case.cached_len, case.total_len
     assert cache.lengths.tolist() == T.tolist()
     k_bits, v_bits = raw_bits(cache.k), raw_bits(cache.v)
@@ -114,9 +114,7 @@ def check_cache_after_step(case: Case, cache, before_k, before_v, new_cache: ora
         np.testing.assert_array_equal(k_bits[b, :, :lb], before_k[b, :, :lb])
         np.testing.assert_array_equal(k_bits[b, :, tb:], before_k[b, :, tb:])
         np.testing.assert_array_equal(v_bits[b, :, :, :lb], before_v[b, :, :, :lb])
-        pad = -(-tb // 64) * 64
-        assert np.all(v_bits[b, :, :, tb:pad] == 0), "V past T_b must be zero to the tile end"
-        np.testing.assert_array_equal(v_bits[b, :, :, pad:], before_v[b, :, :, pad:])
+        np.testing.assert_array_equal(v_bits[b, :, :, tb:], before_v[b, :, :, tb:])
         k_new = to64(cache.k[b, :, lb:tb])
         v_new = to64(cache.v[b, :, :, lb:tb].transpose(1, 2))
         assert_close(k_new, new_cache.k[b][:, lb:tb], case.cfg.dtype, f"cache K seq {b}")

@@ -20,8 +20,10 @@ def small(**kw):
     return LayerConfig(**base)
 
 
-def run_and_check(case, capacity=None):
+def run_and_check(case, capacity=None, append_mode=None):
     layer = make_layer(case)
+    if append_mode is not None:
+        layer.set_append_mode(append_mode)
     cache = make_cache(case, capacity)
     bk, bv = raw_bits(cache.k), raw_bits(cache.v)
     hs, th, pos = step_inputs(case)
@@ -32,6 +34,26 @@ def run_and_check(case, capacity=None):
     check_cache_after_step(case, cache, bk, bv, new)
     assert layer.poll_error() == 0
     return layer, cache, errs
+
+
+APPEND_CASES = {
+    "bf16_d128": dict(),
+    "fp32_d128": dict(dtype="fp32", batch=3, config_id=12),
+    "bf16_d64": dict(head_dim=64, hidden=256, block_size=8, config_id=13),
+    "fp32_d64_mha": dict(dtype="fp32", head_dim=64, hidden=256, n_q_heads=4, n_kv_heads=4,
+                         block_size=8, config_id=14),
+    "bf16_window": dict(sliding_window=300, cached_len=(200, 900), config_id=15),
+    "bf16_many_ctx": dict(batch=7, new_ctx=(30, 70), config_id=16),
+}
+
+
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+@pytest.mark.parametrize("name", sorted(APPEND_CASES))
+def test_append_in_projection_epilogue_or_separate(name, mode):
+    # The q|k|v projection either normalises, rotates and appends in its
+    # epilogue (one head per tile) or leaves fp32 rows for the separate kernel;
+    # both must match the oracle, cache rows included.
+    run_and_check(make_case(small(**APPEND_CASES[name]), seed=3), append_mode=mode)
 
 
 def test_c1_tiny_fp32():
