@@ -1,4 +1,5 @@
-"""Float64 CPU oracle of the DFlash draft-attention layer step.
+"""Float64 CPU oracle of the DFlash draft-attention layer step and of the
+multi-layer context K/V precompute.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -16,3 +17,4 @@ from .ref_fp64 import (  # noqa: F401
     rope_inv_freq,
     window_keep,
 )
+from .context_kv import context_kv_precompute  # noqa: F401

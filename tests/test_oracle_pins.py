@@ -392,3 +392,128 @@ def test_crop_keeps_exact_prefix_and_rejects_growth():
             oracle.crop(cache, 0, bad)
     with pytest.raises(IndexError):
         oracle.crop(cache, 1, 0)
+
+
+# ------------------------------------------- multi-layer context K/V precompute
+
+def ctxkv_tiny(**kw):
+    from workload import CtxKVConfig
+    base = dict(name="ctxkv-tiny", batch=2, hidden=10, n_layers=3, n_kv_heads=2, head_dim=4,
+                dtype="fp32", cached_len=2, new_ctx=3, rope_theta=10000.0, rms_eps=1e-6)
+    base.update(kw)
+    return CtxKVConfig(**base)
+
+
+def ctxkv_inputs(cfg, rng, lens, news):
+    from workload import CtxKVWeights
+    H, Ln, nkv, d = cfg.hidden, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    w = CtxKVWeights(hidden_norm=rng.uniform(0.5, 1.5, H),
+                     w_kv=rng.standard_normal((Ln, 2 * nkv * d, H)) * 0.3,
+                     k_norm=rng.uniform(0.5, 1.5, (Ln, d)))
+    offs = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    C = 3.0 * rng.standard_normal((int(offs[-1]), H))
+    pos = np.concatenate([np.arange(L, L + n) for L, n in zip(lens, news)])
+    caches = [oracle.OracleCache.from_arrays([rng.standard_normal((nkv, L, d)) for L in lens],
+                                             [rng.standard_normal((nkv, L, d)) for L in lens])
+              for _ in range(Ln)]
+    return w, C, offs, pos, caches
+
+
+def test_context_kv_precompute_matches_pure_python_brute_force():
+    """hidden_norm over the row, each layer's K/V rows of the stacked weight,
+    that layer's k_norm, neox rotation at the context positions, raw V, rows
+    appended after each layer's cache: in loops and the math module only."""
+    cfg = ctxkv_tiny()
+    rng = np.random.default_rng(7)
+    lens, news = [2, 0], [3, 2]
+    w, C, offs, pos, caches = ctxkv_inputs(cfg, rng, lens, news)
+    got = oracle.context_kv_precompute(cfg, w, caches, C, offs, pos)
+    H, nkv, d, half = cfg.hidden, cfg.n_kv_heads, cfg.head_dim, cfg.head_dim // 2
+    for layer in range(cfg.n_layers):
+        for b in range(len(lens)):
+            for r in range(news[b]):
+                x = [float(v) for v in C[offs[b] + r]]
+                ms = sum(v * v for v in x) / H
+                xn = [x[c] / math.sqrt(ms + cfg.rms_eps) * float(w.hidden_norm[c]) for c in range(H)]
+                p = int(pos[offs[b] + r])
+                for j in range(nkv):
+                    k = [sum(xn[c] * float(w.w_kv[layer][j * d + e][c]) for c in range(H)) for e in range(d)]
+                    v = [sum(xn[c] * float(w.w_kv[layer][(nkv + j) * d + e][c]) for c in range(H))
+                         for e in range(d)]
+                    mk = sum(t * t for t in k) / d
+                    k = [k[e] / math.sqrt(mk + cfg.rms_eps) * float(w.k_norm[layer][e]) for e in range(d)]
+                    kr = list(k)
+                    for t in range(half):
+                        a = p * cfg.rope_theta ** (-2.0 * t / d)
+                        kr[t] = k[t] * math.cos(a) - k[t + half] * math.sin(a)
+                        kr[t + half] = k[t + half] * math.cos(a) + k[t] * math.sin(a)
+                    row = lens[b] + r
+                    np.testing.assert_allclose(got[layer].k[b][j, row], kr, rtol=1e-12, atol=1e-12)
+                    np.testing.assert_allclose(got[layer].v[b][j, row], v, rtol=1e-12, atol=1e-12)
+            # the old rows stay as they were
+            np.testing.assert_array_equal(got[layer].k[b][:, :lens[b]], caches[layer].k[b])
+            np.testing.assert_array_equal(got[layer].v[b][:, :lens[b]], caches[layer].v[b])
+            assert got[layer].lengths[b] == lens[b] + news[b]
+
+
+def test_context_kv_precompute_equals_each_layer_step_on_normed_context():
+    """Precomputing is only a reordering: layer l's context rows equal those
+    that its own step appends when handed the hidden_norm-ed context."""
+    cfg = ctxkv_tiny(n_layers=2, hidden=12, head_dim=6)
+    rng = np.random.default_rng(8)
+    lens, news = [1, 4], [2, 3]
+    w, C, offs, pos, caches = ctxkv_inputs(cfg, rng, lens, news)
+    got = oracle.context_kv_precompute(cfg, w, caches, C, offs, pos)
+    normed = oracle.rms_norm(C, w.hidden_norm, cfg.rms_eps)
+    lcfg = tiny_cfg(hidden=cfg.hidden, n_q_heads=cfg.n_kv_heads, n_kv_heads=cfg.n_kv_heads,
+                    head_dim=cfg.head_dim, block_size=1, rope_theta=cfg.rope_theta)
+    nkv, d = cfg.n_kv_heads, cfg.head_dim
+    for layer in range(cfg.n_layers):
+        lw = Weights(w_q=rng.standard_normal((nkv * d, cfg.hidden)), w_k=w.w_kv[layer][:nkv * d],
+                     w_v=w.w_kv[layer][nkv * d:], w_o=rng.standard_normal((cfg.hidden, nkv * d)),
+                     q_norm=np.ones(d), k_norm=w.k_norm[layer])
+        X = rng.standard_normal((len(lens), cfg.hidden))
+        # the step's window is [context | one block token]: positions continue
+        wpos = np.concatenate([np.concatenate([pos[offs[b]:offs[b + 1]], [lens[b] + news[b]]])
+                               for b in range(len(lens))])
+        _, ref = oracle.layer_step(lcfg, lw, caches[layer], X, normed, offs, wpos)
+        for b in range(len(lens)):
+            n = lens[b] + news[b]
+            np.testing.assert_allclose(got[layer].k[b], ref.k[b][:, :n], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(got[layer].v[b], ref.v[b][:, :n], rtol=1e-12, atol=1e-12)
+
+
+def test_context_kv_precompute_removes_the_scale_of_the_context():
+    """hidden_norm makes the result independent of the context rows' scale
+    (exactly so with eps = 0): a dropped hidden_norm fails this."""
+    cfg = ctxkv_tiny(rms_eps=0.0)
+    rng = np.random.default_rng(9)
+    w, C, offs, pos, caches = ctxkv_inputs(cfg, rng, [1, 2], [2, 2])
+    a = oracle.context_kv_precompute(cfg, w, caches, C, offs, pos)
+    b = oracle.context_kv_precompute(cfg, w, caches, 37.5 * C, offs, pos)
+    for layer in range(cfg.n_layers):
+        for s in range(2):
+            np.testing.assert_allclose(a[layer].k[s], b[layer].k[s], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(a[layer].v[s], b[layer].v[s], rtol=1e-12, atol=1e-12)
+    # ... while the raw V of one layer scales with the hidden_norm gain
+    from workload import CtxKVWeights
+    w2 = CtxKVWeights(2.0 * w.hidden_norm, w.w_kv, w.k_norm)
+    c = oracle.context_kv_precompute(cfg, w2, caches, C, offs, pos)
+    np.testing.assert_allclose(c[0].v[1][:, 2:], 2.0 * a[0].v[1][:, 2:], rtol=1e-12)
+    np.testing.assert_allclose(c[0].k[1], a[0].k[1], rtol=1e-12, atol=1e-12)  # k_norm undoes it
+
+
+def test_context_kv_precompute_layers_use_their_own_weights():
+    """Reversing the layers' weights and caches reverses the results (no layer
+    reads another layer's K/V rows or k_norm gain)."""
+    from workload import CtxKVWeights
+    cfg = ctxkv_tiny()
+    rng = np.random.default_rng(10)
+    w, C, offs, pos, caches = ctxkv_inputs(cfg, rng, [3, 1], [1, 3])
+    a = oracle.context_kv_precompute(cfg, w, caches, C, offs, pos)
+    wr = CtxKVWeights(w.hidden_norm, w.w_kv[::-1].copy(), w.k_norm[::-1].copy())
+    r = oracle.context_kv_precompute(cfg, wr, caches[::-1], C, offs, pos)
+    for layer in range(cfg.n_layers):
+        for s in range(2):
+            np.testing.assert_array_equal(a[layer].k[s], r[cfg.n_layers - 1 - layer].k[s])
+            np.testing.assert_array_equal(a[layer].v[s], r[cfg.n_layers - 1 - layer].v[s])

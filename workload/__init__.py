@@ -12,3 +12,10 @@ from .configs import (  # noqa: F401
     make_case,
     round_bf16,
 )
+from .ctxkv import (  # noqa: F401
+    CTXKV_CONFIGS,
+    CtxKVCase,
+    CtxKVConfig,
+    CtxKVWeights,
+    make_ctxkv_case,
+)
