@@ -52,6 +52,8 @@ def parse():
                     help="sequences of the workload the oracle is timed on (0: skip)")
     ap.add_argument("--append-mode", default="auto", choices=("auto", "fused", "separate"),
                     help="where q/k norm + RoPE + cache append run (projection epilogue or own kernel)")
+    ap.add_argument("--ctxkv-steps", type=int, default=50,
+                    help="timed runs of the multi-layer context K/V precompute (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -117,6 +119,81 @@ def cpu_baseline(case, n_seq: int, runs: int = 5):
             "sample": f"{k} of {case.batch} sequences of the same workload "
                       f"({int(case.total_len[:k].sum())} keys), float64 numpy, median of "
                       f"{len(times)} runs of {t:.2f}s"}
+
+
+def bench_context_kv(steps: int, warmup: int):
+    """The multi-layer context K/V precompute on its two workloads: P3 (the
+    context rows of one C3 decode round, 3 layers) and P4 (a 4096-row prefill,
+    3 layers). Each run appends every layer's rows and the lengths are rewound
+    (host-only) before the next; the time is HIP events on the launch stream
+    around `steps` runs."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape, KVCache
+    from workload import make_ctxkv_case
+
+    res = {}
+    for name in ("P3", "P4"):
+        case = make_ctxkv_case(name, seed=0)
+        c = case.cfg
+        dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+
+        def dev(x, dtype=dt):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+        w = case.weights
+        pre = ContextKV(ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt, c.rope_theta,
+                                       c.rms_eps, c.max_position),
+                        dev(w.hidden_norm), dev(w.w_kv.reshape(-1, c.hidden)), dev(w.k_norm))
+        caches = []
+        for layer in range(c.n_layers):
+            kv = KVCache(case.batch, c.n_kv_heads, c.head_dim, case.capacity(), dt)
+            for b in range(case.batch):
+                kv.write_prefix(b, dev(case.cache_k[layer][b]), dev(case.cache_v[layer][b]))
+            caches.append(kv)
+        ctx, pos = dev(case.context_states), dev(case.positions, torch.int32)
+        offs = [int(o) for o in case.ctx_offsets]
+        ws = pre.workspace(offs[-1])
+        L0 = case.cached_len.copy()
+
+        def run():
+            pre.append(ctx, offs, pos, caches, workspace=ws)
+            for kv in caches:
+                kv.set_lengths(L0)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        if pre.poll_error() != 0:
+            raise RuntimeError("context position outside the RoPE table")
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        rows = offs[-1]
+        n_out = c.n_layers * 2 * c.n_kv_heads * c.head_dim
+        flops = 2.0 * rows * n_out * c.hidden
+        es = 2 if c.dtype == "bf16" else 4
+        weight_bytes = n_out * c.hidden * es
+        io_bytes = rows * c.hidden * es + rows * n_out * es   # states in, K/V rows out
+        res[name] = {
+            "workload": (f"{name}: {case.batch} sequence(s), {rows} context rows, {c.n_layers} layers, "
+                         f"H={c.hidden}, {c.n_kv_heads} KV heads, head_dim {c.head_dim}, {c.dtype}"),
+            "us_per_run": round(us, 2),
+            "context_rows_per_s": round(rows / (us * 1e-6), 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "hbm_gbs": round((weight_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
+            "floor_us": {"mfma": round(flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+                         "hbm": round((weight_bytes + io_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+        }
+        pre.close()
+        del caches
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -268,6 +345,10 @@ def main():
     if a.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(case, a.cpu_sample)
     layer.close()
+    del caches
+    torch.cuda.empty_cache()
+    if a.ctxkv_steps > 0:
+        line["context_kv_precompute"] = bench_context_kv(a.ctxkv_steps, 5)
     print(json.dumps(line), flush=True)
 
 

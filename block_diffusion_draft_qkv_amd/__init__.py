@@ -22,7 +22,8 @@ import torch
 from . import _lib
 from ._lib import DFlashError, check  # noqa: F401
 
-__all__ = ["DFlashLayer", "KVCache", "LayerShape", "DFlashError", "KERNEL_NAMES"]
+__all__ = ["DFlashLayer", "KVCache", "LayerShape", "ContextKV", "ContextKVShape", "DFlashError",
+           "KERNEL_NAMES"]
 KERNEL_NAMES = _lib.KERNEL_NAMES
 
 _DTYPES = {torch.float32: _lib.DFLASH_F32, torch.bfloat16: _lib.DFLASH_BF16}
@@ -173,6 +174,83 @@ class DFlashLayer:
     def close(self) -> None:
         if getattr(self, "_h", None):
             _lib.lib().dflash_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass(frozen=True)
+class ContextKVShape:
+    hidden: int
+    n_layers: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: torch.dtype = torch.bfloat16
+    rope_theta: float = 1e6
+    rms_eps: float = 1e-6
+    max_position: int = 4096 * 32
+
+
+class ContextKV:
+    """Context K/V of every draft layer at once (the multi-layer precompute):
+    ``hidden_norm`` ``[H]``, ``w_kv`` ``[L * 2 * nkv * d, H]`` (each layer's K
+    rows then V rows), ``k_norm`` ``[L, d]``, device tensors in ``shape.dtype``."""
+
+    def __init__(self, shape: ContextKVShape, hidden_norm: torch.Tensor, w_kv: torch.Tensor,
+                 k_norm: torch.Tensor):
+        self.shape = shape
+        self._weights = [t.contiguous() for t in (hidden_norm, w_kv, k_norm)]
+        for t in self._weights:
+            if t.dtype != shape.dtype or not t.is_cuda:
+                raise ValueError("weights must be device tensors of the dtype")
+        cfg = _lib.CtxKVConfig(shape.hidden, shape.n_layers, shape.n_kv_heads, shape.head_dim,
+                               shape.max_position, _DTYPES[shape.dtype], float(shape.rope_theta),
+                               float(shape.rms_eps))
+        w = _lib.CtxKVWeights(*[t.data_ptr() for t in self._weights])
+        handle = C.c_void_p()
+        with torch.cuda.device(self._weights[0].device):
+            check(_lib.lib().dflash_ctxkv_create(C.byref(cfg), C.byref(w), C.byref(handle)),
+                  "dflash_ctxkv_create")
+        self._h = handle
+        self._ws: Optional[torch.Tensor] = None
+
+    def workspace(self, total_ctx: int) -> torch.Tensor:
+        need = int(_lib.lib().dflash_ctxkv_workspace_bytes(self._h, int(total_ctx)))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+        return self._ws
+
+    def append(self, context_states: torch.Tensor, ctx_offsets, positions: torch.Tensor,
+               caches: Sequence[KVCache], workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Append every sequence's new context rows to every layer's cache."""
+        s = self.shape
+        if len(caches) != s.n_layers:
+            raise ValueError("one cache per layer")
+        B = caches[0].batch
+        if len(ctx_offsets) != B + 1:
+            raise ValueError("ctx_offsets must have batch + 1 entries")
+        if context_states.dtype != s.dtype or not context_states.is_contiguous():
+            raise ValueError("context_states must be contiguous in the dtype")
+        if positions.dtype != torch.int32 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 device tensor")
+        offs = (C.c_int32 * (B + 1))(*[int(o) for o in ctx_offsets])
+        descs = (C.POINTER(_lib.KVCacheDesc) * s.n_layers)(*[C.pointer(c.desc) for c in caches])
+        if workspace is None:
+            workspace = self.workspace(int(ctx_offsets[-1]))
+        st = _lib.lib().dflash_ctxkv_append(self._h, _ptr(context_states), offs, _ptr(positions), descs,
+                                            _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        check(st, "dflash_ctxkv_append")
+
+    def poll_error(self, stream=None) -> int:
+        return int(_lib.lib().dflash_ctxkv_poll_error(self._h, _stream_handle(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.lib().dflash_ctxkv_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -32,6 +32,8 @@ EXPORTS = (
     "dflash_attn_step", "dflash_cache_crop", "dflash_layer_poll_error",
     "dflash_layer_set_profiling", "dflash_layer_kernel_times", "dflash_status_string",
     "dflash_layer_set_append_mode",
+    "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
+    "dflash_ctxkv_append", "dflash_ctxkv_poll_error",
 )
 
 
@@ -50,6 +52,16 @@ class Weights(C.Structure):
 class KVCacheDesc(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("len", C.POINTER(C.c_int32)),
                 ("batch", C.c_int32), ("capacity", C.c_int32)]
+
+
+class CtxKVConfig(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("max_position", C.c_int32), ("dtype", C.c_int32),
+                ("rope_theta", C.c_double), ("rms_eps", C.c_double)]
+
+
+class CtxKVWeights(C.Structure):
+    _fields_ = [("hidden_norm", C.c_void_p), ("w_kv", C.c_void_p), ("k_norm", C.c_void_p)]
 
 
 class DFlashError(RuntimeError):
@@ -88,6 +100,19 @@ def lib() -> C.CDLL:
         h.dflash_layer_set_profiling.restype = C.c_int
         h.dflash_layer_kernel_times.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
         h.dflash_layer_kernel_times.restype = C.c_int
+        h.dflash_ctxkv_create.argtypes = [C.POINTER(CtxKVConfig), C.POINTER(CtxKVWeights),
+                                          C.POINTER(C.c_void_p)]
+        h.dflash_ctxkv_create.restype = C.c_int
+        h.dflash_ctxkv_destroy.argtypes = [C.c_void_p]
+        h.dflash_ctxkv_destroy.restype = None
+        h.dflash_ctxkv_workspace_bytes.argtypes = [C.c_void_p, C.c_int64]
+        h.dflash_ctxkv_workspace_bytes.restype = C.c_size_t
+        h.dflash_ctxkv_append.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32), C.c_void_p,
+                                          C.POINTER(C.POINTER(KVCacheDesc)), C.c_void_p, C.c_size_t,
+                                          C.c_void_p]
+        h.dflash_ctxkv_append.restype = C.c_int
+        h.dflash_ctxkv_poll_error.argtypes = [C.c_void_p, C.c_void_p]
+        h.dflash_ctxkv_poll_error.restype = C.c_int
         h.dflash_status_string.argtypes = [C.c_int]
         h.dflash_status_string.restype = C.c_char_p
         _lib = h

@@ -26,11 +26,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxBatch = 256;
-constexpr int kKeyTile = 64;       // cache capacity granule; V is zero-padded to it
+constexpr int kKeyTile = 64;       // cache capacity granule (attention key tiles)
 constexpr int kMaxQueryRows = 64;  // block_size * (n_q / n_kv) rows per KV head
 constexpr int kMaxGroups = 256;    // attention work-groups per launch
 constexpr int kMaxKvHeads = 256;   // (sequence, KV head) pairs index in 16 bits
 constexpr int kMaxCapacity = 1 << 21;  // cache rows; key tiles index in 16 bits
+constexpr int kMaxLayers = 16;     // draft layers one context K/V precompute fills
 
 // Per-sequence lengths of one step, passed to kernels by value.
 struct SeqTable {

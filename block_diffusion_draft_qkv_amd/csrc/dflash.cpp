@@ -55,6 +55,14 @@ struct dflash_layer {
   int64_t count[DFLASH_K_COUNT] = {};
 };
 
+struct dflash_ctxkv {
+  dflash_ctxkv_config cfg;
+  dflash_ctxkv_weights w;
+  int num_cus = 256;
+  float* cos_sin = nullptr;
+  int32_t* err = nullptr;
+};
+
 namespace {
 
 int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
@@ -93,9 +101,9 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
 struct TileChoice {
   int bm, bn, tiles, kslices;
 };
-TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, bool allow_split) {
+TileChoice choose_tiles(int num_cus, int m0, int n0, int m1, int n1, bool allow_split) {
   static const int cand[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
-  const int target = L->num_cus * 3 / 4;
+  const int target = num_cus * 3 / 4;
   auto count = [&](int bm, int bn) {
     int t = ((m0 + bm - 1) / bm) * ((n0 + bn - 1) / bn);
     if (m1 > 0) t += ((m1 + bm - 1) / bm) * ((n1 + bn - 1) / bn);
@@ -107,8 +115,27 @@ TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, b
   }
   const int t = count(64, 64);
   int ks = 1;
-  if (allow_split) ks = std::min(kMaxKSlices, std::max(1, (L->num_cus + t - 1) / t));
+  if (allow_split) ks = std::min(kMaxKSlices, std::max(1, (num_cus + t - 1) / t));
   return {64, 64, t, ks};
+}
+TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, bool allow_split) {
+  return choose_tiles(L->num_cus, m0, n0, m1, n1, allow_split);
+}
+
+// Workspace of a context precompute of mc rows: hidden_norm-ed rows in the
+// element type, then the fp32 projection [k slices][mc][L * 2 * nkv * d].
+struct CtxCarve {
+  size_t normed, proj, total;
+};
+CtxCarve ctx_carve(const dflash_ctxkv_config& c, int64_t mc) {
+  const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, m = std::max<int64_t>(mc, 1);
+  const int64_t n = (int64_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim;
+  CtxCarve w{};
+  size_t off = 0;
+  w.normed = off; off += align_up(m * c.hidden * es);
+  w.proj = off;   off += align_up(kMaxKSlices * m * n * 4);
+  w.total = off;
+  return w;
 }
 
 int validate_config(const dflash_config* c) {
@@ -124,6 +151,28 @@ int validate_config(const dflash_config* c) {
   if ((int64_t)c->block_size * (c->n_q_heads / c->n_kv_heads) > kMaxQueryRows)
     return DFLASH_ERR_UNSUPPORTED;
   return DFLASH_OK;
+}
+
+// RoPE cos/sin of pos * theta^(-2t/d) for t < d/2, angle and trig in float64,
+// uploaded as fp32 [max_pos][d/2] cos then [max_pos][d/2] sin.
+bool upload_rope_table(int max_pos, int d, double theta, float** out) {
+  const int half = d / 2;
+  const size_t n = (size_t)max_pos * half;
+  std::vector<float> table(2 * n);
+  std::vector<double> inv(half);
+  for (int t = 0; t < half; ++t) inv[t] = std::pow(theta, -2.0 * t / d);
+  for (int64_t p = 0; p < max_pos; ++p)
+    for (int t = 0; t < half; ++t) {
+      const double ang = (double)p * inv[t];
+      table[(size_t)p * half + t] = (float)std::cos(ang);
+      table[n + (size_t)p * half + t] = (float)std::sin(ang);
+    }
+  *out = nullptr;
+  if (hipMalloc(out, 2 * n * sizeof(float)) != hipSuccess) {
+    *out = nullptr;
+    return false;
+  }
+  return hipMemcpy(*out, table.data(), 2 * n * sizeof(float), hipMemcpyHostToDevice) == hipSuccess;
 }
 
 hipEvent_t pooled_event(dflash_layer* L) {
@@ -183,20 +232,7 @@ int dflash_layer_create(const dflash_config* cfg, const dflash_weights* weights,
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
     L->num_cus = cus;
 
-  // cos/sin of pos * theta^(-2t/d), angle and trig in float64, stored fp32.
-  const int half = cfg->head_dim / 2;
-  const size_t n = (size_t)cfg->max_position * half;
-  std::vector<float> table(2 * n);
-  std::vector<double> inv(half);
-  for (int t = 0; t < half; ++t) inv[t] = std::pow(cfg->rope_theta, -2.0 * t / cfg->head_dim);
-  for (int64_t p = 0; p < cfg->max_position; ++p)
-    for (int t = 0; t < half; ++t) {
-      const double ang = (double)p * inv[t];
-      table[(size_t)p * half + t] = (float)std::cos(ang);
-      table[n + (size_t)p * half + t] = (float)std::sin(ang);
-    }
-  if (hipMalloc(&L->cos_sin, 2 * n * sizeof(float)) != hipSuccess ||
-      hipMemcpy(L->cos_sin, table.data(), 2 * n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+  if (!upload_rope_table(cfg->max_position, cfg->head_dim, cfg->rope_theta, &L->cos_sin) ||
       hipMalloc(&L->err, sizeof(int32_t)) != hipSuccess ||
       hipMemset(L->err, 0, sizeof(int32_t)) != hipSuccess) {
     if (L->cos_sin) hipFree(L->cos_sin);
@@ -302,6 +338,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   }
   // HK2 (or the fused epilogue)
   NormRopeArgs na;
+  std::memset(&na, 0, sizeof(na));
   na.qkv = qkv;
   na.ctxkv = ctxkv;
   na.qkv_slice = (int64_t)Mq * Nqkv;
@@ -318,6 +355,8 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   na.nq = nq; na.nkv = nkv; na.bs = bs; na.cap = cache->capacity; na.max_pos = c.max_position;
   na.eps = (float)c.rms_eps;
   na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  na.ctx_ld = (int64_t)Nkv;
+  na.ctx_layer_off = 0;
   na.seq = seq;
   hipEvent_t ev;
   record(L, &ev, s);
@@ -331,7 +370,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
     record(L, &ev, s);
     int max_new = 0;
     for (int b = 0; b < B; ++b) max_new = std::max(max_new, ctx_offsets[b + 1] - ctx_offsets[b] + bs);
-    if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
     record_end(L, DFLASH_K_NORM_ROPE, ev, s);
   }
 
@@ -462,6 +501,152 @@ int dflash_layer_kernel_times(dflash_layer* L, double* ms, int64_t* count) {
   for (int k = 0; k < DFLASH_K_COUNT; ++k) {
     ms[k] = L->ms[k];
     count[k] = L->count[k];
+  }
+  return DFLASH_OK;
+}
+
+int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights,
+                        dflash_ctxkv** out) {
+  if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
+  *out = nullptr;
+  if (!weights->hidden_norm || !weights->w_kv || !weights->k_norm) return DFLASH_ERR_ARG;
+  if (cfg->hidden <= 0 || cfg->n_kv_heads <= 0 || cfg->n_layers <= 0 || cfg->max_position <= 0)
+    return DFLASH_ERR_SHAPE;
+  if (cfg->hidden % 64) return DFLASH_ERR_SHAPE;
+  if (cfg->n_layers > kMaxLayers || cfg->n_kv_heads > kMaxKvHeads) return DFLASH_ERR_UNSUPPORTED;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (!(cfg->rope_theta > 0.0) || !(cfg->rms_eps >= 0.0)) return DFLASH_ERR_ARG;
+  if (cfg->dtype != DFLASH_F32 && cfg->dtype != DFLASH_BF16) return DFLASH_ERR_ARG;
+  dflash_ctxkv* h = new (std::nothrow) dflash_ctxkv();
+  if (!h) return DFLASH_ERR_HIP;
+  h->cfg = *cfg;
+  h->w = *weights;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { delete h; return DFLASH_ERR_HIP; }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    h->num_cus = cus;
+  if (!upload_rope_table(cfg->max_position, cfg->head_dim, cfg->rope_theta, &h->cos_sin) ||
+      hipMalloc(&h->err, sizeof(int32_t)) != hipSuccess ||
+      hipMemset(h->err, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (h->cos_sin) hipFree(h->cos_sin);
+    if (h->err) hipFree(h->err);
+    delete h;
+    return DFLASH_ERR_HIP;
+  }
+  *out = h;
+  return DFLASH_OK;
+}
+
+void dflash_ctxkv_destroy(dflash_ctxkv* h) {
+  if (!h) return;
+  hipDeviceSynchronize();
+  hipFree(h->cos_sin);
+  hipFree(h->err);
+  delete h;
+}
+
+size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx) {
+  if (!h || total_ctx < 0) return 0;
+  return ctx_carve(h->cfg, total_ctx).total;
+}
+
+int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
+                        const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!h || !ctx_offsets || !caches) return DFLASH_ERR_ARG;
+  const dflash_ctxkv_config& c = h->cfg;
+  const int nl = c.n_layers, nkv = c.n_kv_heads, d = c.head_dim, H = c.hidden;
+  for (int l = 0; l < nl; ++l)
+    if (!caches[l] || !caches[l]->k || !caches[l]->v || !caches[l]->len) return DFLASH_ERR_ARG;
+  const dflash_kv_cache* c0 = caches[0];
+  const int B = c0->batch;
+  if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
+  if (c0->capacity <= 0 || c0->capacity % kKeyTile || c0->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
+  for (int l = 1; l < nl; ++l) {
+    if (caches[l]->batch != B || caches[l]->capacity != c0->capacity) return DFLASH_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+      if (caches[l]->len[b] != c0->len[b]) return DFLASH_ERR_SHAPE;
+  }
+  if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
+  SeqTable seq;
+  std::memset(&seq, 0, sizeof(seq));
+  seq.batch = B;
+  int max_new = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = (int64_t)ctx_offsets[b + 1] - ctx_offsets[b];
+    if (n < 0 || c0->len[b] < 0) return DFLASH_ERR_SHAPE;
+    if ((int64_t)c0->len[b] + n > c0->capacity) return DFLASH_ERR_CAPACITY;
+    seq.len[b] = c0->len[b];
+    seq.ctx_off[b] = ctx_offsets[b];
+    max_new = std::max<int>(max_new, (int)n);
+  }
+  seq.ctx_off[B] = ctx_offsets[B];
+  const int64_t Mc = ctx_offsets[B];
+  if (Mc == 0) return DFLASH_OK;
+  if (!context_states || !positions) return DFLASH_ERR_ARG;
+  if (!workspace) return DFLASH_ERR_WORKSPACE;
+  const CtxCarve wc = ctx_carve(c, Mc);
+  if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return DFLASH_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* normed = ws + wc.normed;
+  float* proj = reinterpret_cast<float*>(ws + wc.proj);
+  const int N = nl * 2 * nkv * d;
+
+  // hidden_norm over each raw context row
+  if (launch_rms_rows(c.dtype, context_states, h->w.hidden_norm, normed, (int)Mc, H, (float)c.rms_eps, s) !=
+      hipSuccess)
+    return DFLASH_ERR_HIP;
+  // every layer's K and V in one projection (fp32, k split when M is small)
+  const TileChoice t = choose_tiles(h->num_cus, (int)Mc, N, 0, 0, true);
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.nprob = 1;
+  ga.p[0] = {normed, h->w.w_kv, proj, (int32_t)Mc, N, H, H, H, N, (N + t.bn - 1) / t.bn, 0, Mc * N};
+  if (launch_gemm(c.dtype, true, ga, t.tiles, t.bm, t.bn, t.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
+  // per layer: k_norm + RoPE of K, cache append of K and V (HK2 without block rows)
+  NormRopeArgs na;
+  std::memset(&na, 0, sizeof(na));
+  na.qkv = proj;
+  na.ctxkv = proj;
+  na.qkv_slice = Mc * N;
+  na.ctx_slice = Mc * N;
+  na.kslices = t.kslices;
+  na.positions = positions;
+  na.cos_sin = h->cos_sin;
+  na.q_norm = h->w.k_norm;
+  na.k_norm = h->w.k_norm;
+  na.qpack = proj;
+  na.kc = c0->k;
+  na.vc = c0->v;
+  for (int l = 0; l < nl; ++l) {
+    na.layer_kc[l] = caches[l]->k;
+    na.layer_vc[l] = caches[l]->v;
+  }
+  na.err = h->err;
+  na.nq = nkv; na.nkv = nkv; na.bs = 0; na.cap = c0->capacity; na.max_pos = c.max_position;
+  na.eps = (float)c.rms_eps;
+  na.qscale = 1.0f;
+  na.ctx_ld = N;
+  na.ctx_layer_off = (int64_t)2 * nkv * d;
+  na.seq = seq;
+  if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, nl, s) != hipSuccess) return DFLASH_ERR_HIP;
+
+  for (int l = 0; l < nl; ++l)
+    for (int b = 0; b < B; ++b) caches[l]->len[b] += ctx_offsets[b + 1] - ctx_offsets[b];
+  return DFLASH_OK;
+}
+
+int dflash_ctxkv_poll_error(dflash_ctxkv* h, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  int32_t flag = 0;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DFLASH_ERR_HIP;
+  if (hipMemcpy(&flag, h->err, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_ERR_HIP;
+  if (flag) {
+    if (hipMemset(h->err, 0, sizeof(int32_t)) != hipSuccess) return DFLASH_ERR_HIP;
+    return DFLASH_ERR_RANGE;
   }
   return DFLASH_OK;
 }

@@ -49,12 +49,24 @@ struct NormRopeArgs {
   int32_t* err;
   int32_t nq, nkv, bs, cap, max_pos;
   float eps, qscale;
+  int64_t ctx_ld;          // elements between context rows of ctxkv (2 nkv d for a layer step)
+  // The multi-layer context precompute (bs = 0, no queries) runs grid.z =
+  // layers: layer z > 0 reads the columns ctxkv + z * ctx_layer_off, its gain
+  // k_norm + z * d and writes the cache layer_kc[z] / layer_vc[z].
+  int64_t ctx_layer_off;
+  void* layer_kc[kMaxLayers];
+  void* layer_vc[kMaxLayers];
   SeqTable seq;
 };
-// grid: B * n_kv (one column of work-groups per sequence and KV head);
-// max_new_rows: the largest n_b + bs of the batch.
+// grid: B * n_kv (one column of work-groups per sequence and KV head) times
+// `layers` (1 for a layer step); max_new_rows: the largest n_b + bs.
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
-                            int max_new_rows, hipStream_t stream);
+                            int max_new_rows, int layers, hipStream_t stream);
+
+// RMSNorm of `rows` rows of h elements (h % 64 == 0) with gain g [h]:
+// out = x / sqrt(mean(x^2) + eps) * g, fp32 math, stored in the element type.
+hipError_t launch_rms_rows(int dtype, const void* x, const void* g, void* out, int rows, int h,
+                           float eps, hipStream_t stream);
 
 // The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
 // head_dim, no k split) doing the work of launch_norm_rope in its epilogue

@@ -18,6 +18,12 @@
 // A work-group issues the loads of all its rows before using any (inputs and
 // positions, then the cos/sin rows those positions select), so each costs two
 // memory round trips whatever the row count.
+// The same kernel appends the new context rows of every draft layer for the
+// multi-layer context precompute (vLLM page "qwen3_dflash",
+// precompute_and_store_context_kv: grouped k_norm, RoPE at the context
+// positions, per-layer cache insert): then bs = 0 (no block rows, no queries)
+// and grid.z runs over the layers, layer z taking its own columns of the
+// all-layer projection, its own k_norm gain and its own cache.
 // RoPE is neox style (vLLM page "qwen3_dflash": is_neox_style): element t of
 // the first half pairs with element t + d/2. One lane owns one such pair, so a
 // head is d/2 lanes and the rotation needs no data exchange; the RMS reduction
@@ -55,7 +61,10 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   const int R = bs * g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / HALF, t = lane % HALF;
-  const size_t ld_blk = (size_t)(nq + 2 * nkv) * D, ld_ctx = (size_t)2 * nkv * D;
+  const size_t ld_blk = (size_t)(nq + 2 * nkv) * D, ld_ctx = (size_t)a.ctx_ld;
+  // Layer z of a multi-layer context precompute (z = 0 for a layer step).
+  const int z = blockIdx.z;
+  const float* ctxkv = a.ctxkv + (size_t)z * a.ctx_layer_off;
   const size_t pair = (size_t)b * nkv + j;
 
   if ((int)blockIdx.y >= yv) {
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       if (r < nnew) {
         kind[s] = 1;
         if (r < n) {
-          src[s] = a.ctxkv + (size_t)(c0 + r) * ld_ctx + (size_t)j * D;
+          src[s] = ctxkv + (size_t)(c0 + r) * ld_ctx + (size_t)j * D;
           stride[s] = a.ctx_slice;
         } else {
           src[s] = a.qkv + (size_t)(b * bs + r - n) * ld_blk + (size_t)(nq + j) * D;
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
         p[s] = p[s] < 0 ? 0 : a.max_pos - 1;
       }
     }
-    const T* kn = static_cast<const T*>(a.k_norm);
+    const T* kn = static_cast<const T*>(a.k_norm) + (size_t)z * D;
     const T* qn = static_cast<const T*>(a.q_norm);
     const float kg1 = Elem<T>::to_f32(kn[t]), kg2 = Elem<T>::to_f32(kn[t + HALF]);
     const float qg1 = Elem<T>::to_f32(qn[t]), qg2 = Elem<T>::to_f32(qn[t + HALF]);
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       cs[s] = cos_t[(size_t)p[s] * HALF + t];
       sn[s] = sin_t[(size_t)p[s] * HALF + t];
     }
-    T* kdst = static_cast<T*>(a.kc) + (pair * a.cap + L) * D;
+    T* kdst = static_cast<T*>(z == 0 ? a.kc : a.layer_kc[z]) + (pair * a.cap + L) * D;
     T* qdst = static_cast<T*>(a.qpack) + pair * R * D;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
     vstride[k] = a.qkv_slice;
     if (rb < nr) {
       if (rr < n) {
-        vsrc[k] = a.ctxkv + (size_t)(c0 + rr) * ld_ctx + (size_t)(nkv + j) * D;
+        vsrc[k] = ctxkv + (size_t)(c0 + rr) * ld_ctx + (size_t)(nkv + j) * D;
         vstride[k] = a.ctx_slice;
       } else {
         vsrc[k] = a.qkv + (size_t)(b * bs + rr - n) * ld_blk + (size_t)(nq + nkv + j) * D;
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
     }
   }
   __syncthreads();
-  T* vdst = static_cast<T*>(a.vc) + pair * D * a.cap + L;
+  T* vdst = static_cast<T*>(z == 0 ? a.vc : a.layer_vc[z]) + pair * D * a.cap + L;
   for (int idx = tid; idx < D * nr; idx += 256) {
     const int dd = idx / nr, rr = idx % nr;
     vdst[(size_t)dd * a.cap + r0 + rr] = vt[dd][rr];
@@ -204,13 +213,13 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
 }  // namespace
 
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
-                            int max_new_rows, hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
+                            int max_new_rows, int layers, hipStream_t stream) {
+  if (grid <= 0 || layers <= 0) return hipSuccess;
   const int wg_rows = 4 * kNormSlots * (128 / head_dim);
   const int R = args.bs * (args.nq / args.nkv);
   const int yk = (max_new_rows + R + wg_rows - 1) / wg_rows;
   const int yv = (max_new_rows + 63) / 64;
-  const dim3 g(grid, yv + yk), blk(256);
+  const dim3 g(grid, yv + yk, layers), blk(256);
   if (dtype == 1) {
     if (head_dim == 128)
       hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 128>), g, blk, 0, stream, args, yv);

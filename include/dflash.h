@@ -27,10 +27,12 @@
  *     changes.
  *   - Device pointers are borrowed: the caller allocates and frees every buffer
  *     passed in and keeps weights alive for the layer's lifetime. The library
- *     allocates only its own cos/sin table and error flag (at create).
+ *     allocates only each handle's own cos/sin table and error flag (at
+ *     create).
  *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream) and the calls return without synchronising,
- *     except dflash_layer_poll_error and dflash_layer_kernel_times.
+ *     except dflash_layer_poll_error, dflash_layer_kernel_times and
+ *     dflash_ctxkv_poll_error.
  *   - Element type of every activation, weight and cache buffer is the
  *     config's dtype (fp32 or bf16); accumulation is fp32.
  */
@@ -206,6 +208,84 @@ enum {
     DFLASH_K_COUNT = 5
 };
 int dflash_layer_kernel_times(dflash_layer* layer, double* ms, int64_t* count);
+
+/* ------------------------------------------------------------------------
+ * Multi-layer context K/V precompute (vLLM page "qwen3_dflash",
+ * DFlashQwen3Model: _build_context_kv_buffers, precompute_and_store_context_kv
+ * and the helpers it calls). Instead of each layer projecting its new context
+ * rows inside its step, the rows of every draft layer are made at once: the
+ * raw context states (the fc output) are RMS-normalised with the model's
+ * hidden_norm gain, one projection with the K/V rows of every layer's fused
+ * q|k|v weight gives each layer's K and V, each K head is RMS-normalised with
+ * its layer's k_norm gain and rotated (neox) at its context position, and each
+ * layer's rows are appended to that layer's cache. A layer step that follows
+ * is then called with no new context rows (ctx_offsets all 0).
+ * ------------------------------------------------------------------------ */
+
+/* Limits checked at create: 1 <= n_layers <= 16, head_dim in {64, 128},
+ * n_kv_heads <= 256, hidden % 64 == 0, rope_theta > 0, rms_eps >= 0,
+ * max_position >= 1. rms_eps is used by hidden_norm and by k_norm. */
+typedef struct {
+    int32_t hidden;
+    int32_t n_layers;        /* L draft layers                                     */
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t max_position;
+    int32_t dtype;           /* dflash_dtype                                       */
+    double rope_theta;
+    double rms_eps;
+} dflash_ctxkv_config;
+
+/* Device weights in the config dtype, borrowed (they must outlive the handle). */
+typedef struct {
+    const void* hidden_norm;  /* [H] gain of the RMSNorm over the context states  */
+    const void* w_kv;         /* [L * 2 * nkv * d, H]: layer l's K rows (its
+                                 nkv heads), then its V rows, i.e. the rows of its
+                                 fused q|k|v weight after the q rows; layers in
+                                 order                                            */
+    const void* k_norm;       /* [L, d] each layer's K RMSNorm gain               */
+} dflash_ctxkv_weights;
+
+typedef struct dflash_ctxkv dflash_ctxkv; /* opaque */
+
+/* Create a precompute handle on the current device; it builds its own RoPE
+ * cos/sin table exactly as dflash_layer_create does and an error flag.
+ * Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE / DFLASH_ERR_UNSUPPORTED (limits),
+ * DFLASH_ERR_HIP. */
+int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights,
+                        dflash_ctxkv** out);
+
+/* Release the handle (waits for the device). NULL is a no-op. */
+void dflash_ctxkv_destroy(dflash_ctxkv* h);
+
+/* Device workspace bytes for up to `total_ctx` context rows; 0 on bad input. */
+size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx);
+
+/* Append the new context rows of `caches[0 .. L-1]->batch` sequences to every
+ * layer's cache.
+ *   context_states  device [sum n_b, H] raw context rows (before hidden_norm),
+ *                   sequence b owning rows ctx_offsets[b] .. ctx_offsets[b+1]-1.
+ *   ctx_offsets     HOST [B + 1], ctx_offsets[0] == 0, non-decreasing.
+ *   positions       device int32 [sum n_b]: the position of every context row
+ *                   (normally len_b, len_b + 1, ...); each must lie in
+ *                   [0, max_position): a violation is clamped and latched as
+ *                   for a layer step (dflash_ctxkv_poll_error).
+ *   caches          HOST array of L cache descriptors, one per layer, with the
+ *                   same batch, capacity and lengths.
+ * Effects: rows [len_b, len_b + n_b) of every layer's K and V for every b,
+ * nothing else in the caches; then every layer's len[b] += n_b. Validation
+ * (shapes, equal lengths across layers, capacity, workspace) happens before
+ * anything is enqueued; on an error nothing runs and no length changes.
+ * Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE, DFLASH_ERR_CAPACITY,
+ * DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP. */
+int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
+                        const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream` and report the sticky device error (DFLASH_ERR_RANGE
+ * if a position fell outside the table since the last poll, which clears it),
+ * or DFLASH_OK. */
+int dflash_ctxkv_poll_error(dflash_ctxkv* h, void* stream);
 
 /* Static description of a status code. */
 const char* dflash_status_string(int status);
