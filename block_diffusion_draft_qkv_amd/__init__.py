@@ -245,6 +245,10 @@ class ContextKV:
                                             _ptr(workspace), workspace.numel(), _stream_handle(stream))
         check(st, "dflash_ctxkv_append")
 
+    def set_append_mode(self, mode: str) -> None:
+        """``"auto"`` (default), ``"fused"`` (projection epilogue) or ``"separate"``."""
+        check(_lib.lib().dflash_ctxkv_set_append_mode(self._h, _lib.APPEND_MODES[mode]), "set_append_mode")
+
     def poll_error(self, stream=None) -> int:
         return int(_lib.lib().dflash_ctxkv_poll_error(self._h, _stream_handle(stream)))
 

@@ -33,7 +33,7 @@ EXPORTS = (
     "dflash_layer_set_profiling", "dflash_layer_kernel_times", "dflash_status_string",
     "dflash_layer_set_append_mode",
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
-    "dflash_ctxkv_append", "dflash_ctxkv_poll_error",
+    "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
 )
 
 
@@ -113,6 +113,8 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_append.restype = C.c_int
         h.dflash_ctxkv_poll_error.argtypes = [C.c_void_p, C.c_void_p]
         h.dflash_ctxkv_poll_error.restype = C.c_int
+        h.dflash_ctxkv_set_append_mode.argtypes = [C.c_void_p, C.c_int32]
+        h.dflash_ctxkv_set_append_mode.restype = C.c_int
         h.dflash_status_string.argtypes = [C.c_int]
         h.dflash_status_string.restype = C.c_char_p
         _lib = h

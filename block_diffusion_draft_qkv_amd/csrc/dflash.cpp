@@ -59,6 +59,7 @@ struct dflash_ctxkv {
   dflash_ctxkv_config cfg;
   dflash_ctxkv_weights w;
   int num_cus = 256;
+  int append_mode = DFLASH_APPEND_AUTO;
   float* cos_sin = nullptr;
   int32_t* err = nullptr;
 };
@@ -94,10 +95,12 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   return w;
 }
 
-// Tile shape of a projection launch (one or two problems of m x n outputs):
-// the largest tiles that still give about one work-group per CU; problems too
-// small for that use 64 x 64 tiles and, when fp32 partial sums are allowed,
-// split k so that the launch still covers the CUs.
+// Tile shape of a projection launch (one or two problems of m x n outputs).
+// A work-group streams BM + BN rows of k per tile and a CU runs one at a time,
+// so among the shapes that give at least ~3/4 of a work-group per CU the one
+// with the fewest rounds x (BM + BN) wins (ties: the earlier, larger shape);
+// problems too small for any use 64 x 64 tiles and, when fp32 partial sums are
+// allowed, split k so that the launch still covers the CUs.
 struct TileChoice {
   int bm, bn, tiles, kslices;
 };
@@ -109,10 +112,18 @@ TileChoice choose_tiles(int num_cus, int m0, int n0, int m1, int n1, bool allow_
     if (m1 > 0) t += ((m1 + bm - 1) / bm) * ((n1 + bn - 1) / bn);
     return t;
   };
-  for (const auto& c : cand) {
-    const int t = count(c[0], c[1]);
-    if (t >= target) return {c[0], c[1], t, 1};
+  int best = -1;
+  long best_cost = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int t = count(cand[i][0], cand[i][1]);
+    if (t < target) continue;
+    const long cost = (long)((t + num_cus - 1) / num_cus) * (cand[i][0] + cand[i][1]);
+    if (best < 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
   }
+  if (best >= 0) return {cand[best][0], cand[best][1], count(cand[best][0], cand[best][1]), 1};
   const int t = count(64, 64);
   int ks = 1;
   if (allow_split) ks = std::min(kMaxKSlices, std::max(1, (num_cus + t - 1) / t));
@@ -510,6 +521,8 @@ int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weigh
   if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
   *out = nullptr;
   if (!weights->hidden_norm || !weights->w_kv || !weights->k_norm) return DFLASH_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(weights->hidden_norm) % 16 || reinterpret_cast<uintptr_t>(weights->w_kv) % 16)
+    return DFLASH_ERR_ARG;
   if (cfg->hidden <= 0 || cfg->n_kv_heads <= 0 || cfg->n_layers <= 0 || cfg->max_position <= 0)
     return DFLASH_ERR_SHAPE;
   if (cfg->hidden % 64) return DFLASH_ERR_SHAPE;
@@ -583,7 +596,7 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   seq.ctx_off[B] = ctx_offsets[B];
   const int64_t Mc = ctx_offsets[B];
   if (Mc == 0) return DFLASH_OK;
-  if (!context_states || !positions) return DFLASH_ERR_ARG;
+  if (!context_states || !positions || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
   if (!workspace) return DFLASH_ERR_WORKSPACE;
   const CtxCarve wc = ctx_carve(c, Mc);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
@@ -599,26 +612,19 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   if (launch_rms_rows(c.dtype, context_states, h->w.hidden_norm, normed, (int)Mc, H, (float)c.rms_eps, s) !=
       hipSuccess)
     return DFLASH_ERR_HIP;
-  // every layer's K and V in one projection (fp32, k split when M is small)
-  const TileChoice t = choose_tiles(h->num_cus, (int)Mc, N, 0, 0, true);
-  GemmArgs ga;
-  std::memset(&ga, 0, sizeof(ga));
-  ga.nprob = 1;
-  ga.p[0] = {normed, h->w.w_kv, proj, (int32_t)Mc, N, H, H, H, N, (N + t.bn - 1) / t.bn, 0, Mc * N};
-  if (launch_gemm(c.dtype, true, ga, t.tiles, t.bm, t.bn, t.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
-  // per layer: k_norm + RoPE of K, cache append of K and V (HK2 without block rows)
+  // Every layer's K and V in one projection. With enough 64-row tiles (one
+  // head each) its epilogue normalises, rotates and appends (no fp32 rows);
+  // otherwise fp32 rows (k split when M is small) go to HK2 over the layers.
+  const int heads = nl * 2 * nkv;
+  const int t64 = (int)((Mc + 63) / 64) * heads, t128 = (int)((Mc + 127) / 128) * heads;
+  const bool fused = h->append_mode == DFLASH_APPEND_FUSED ||
+                     (h->append_mode == DFLASH_APPEND_AUTO && t64 >= h->num_cus * 3 / 4);
   NormRopeArgs na;
   std::memset(&na, 0, sizeof(na));
-  na.qkv = proj;
-  na.ctxkv = proj;
-  na.qkv_slice = Mc * N;
-  na.ctx_slice = Mc * N;
-  na.kslices = t.kslices;
   na.positions = positions;
   na.cos_sin = h->cos_sin;
   na.q_norm = h->w.k_norm;
   na.k_norm = h->w.k_norm;
-  na.qpack = proj;
   na.kc = c0->k;
   na.vc = c0->v;
   for (int l = 0; l < nl; ++l) {
@@ -632,10 +638,42 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   na.ctx_ld = N;
   na.ctx_layer_off = (int64_t)2 * nkv * d;
   na.seq = seq;
-  if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, nl, s) != hipSuccess) return DFLASH_ERR_HIP;
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  if (fused) {
+    // the context problem is the second one (an empty first problem)
+    const long r64 = (long)((t64 + h->num_cus - 1) / h->num_cus) * (64 + d);
+    const long r128 = (long)((t128 + h->num_cus - 1) / h->num_cus) * (128 + d);
+    const int bm = r128 <= r64 ? 128 : 64, tiles = bm == 128 ? t128 : t64;
+    ga.nprob = 2;
+    ga.p[0] = {normed, h->w.w_kv, nullptr, 0, N, H, H, H, N, heads, 0, 0};
+    ga.p[1] = {normed, h->w.w_kv, proj, (int32_t)Mc, N, H, H, H, N, heads, 0, Mc * N};
+    na.qkv = proj;
+    na.ctxkv = proj;
+    na.qpack = proj;
+    if (launch_gemm_append(c.dtype, d, ga, na, tiles, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+  } else {
+    const TileChoice t = choose_tiles(h->num_cus, (int)Mc, N, 0, 0, true);
+    ga.nprob = 1;
+    ga.p[0] = {normed, h->w.w_kv, proj, (int32_t)Mc, N, H, H, H, N, (N + t.bn - 1) / t.bn, 0, Mc * N};
+    if (launch_gemm(c.dtype, true, ga, t.tiles, t.bm, t.bn, t.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
+    na.qkv = proj;
+    na.ctxkv = proj;
+    na.qkv_slice = Mc * N;
+    na.ctx_slice = Mc * N;
+    na.kslices = t.kslices;
+    na.qpack = proj;
+    if (launch_norm_rope(c.dtype, d, na, B * nkv, max_new, nl, s) != hipSuccess) return DFLASH_ERR_HIP;
+  }
 
   for (int l = 0; l < nl; ++l)
     for (int b = 0; b < B; ++b) caches[l]->len[b] += ctx_offsets[b + 1] - ctx_offsets[b];
+  return DFLASH_OK;
+}
+
+int dflash_ctxkv_set_append_mode(dflash_ctxkv* h, int32_t mode) {
+  if (!h || mode < DFLASH_APPEND_AUTO || mode > DFLASH_APPEND_SEPARATE) return DFLASH_ERR_ARG;
+  h->append_mode = mode;
   return DFLASH_OK;
 }
 

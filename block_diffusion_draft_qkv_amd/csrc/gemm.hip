@@ -273,17 +273,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
   const int nq = a.nq, nkv = a.nkv, bs = a.bs, g = nq / nkv, R = bs * g;
-  // The head of this tile: kind 0 query, 1 key, 2 value.
+  // The head of this tile: kind 0 query, 1 key, 2 value. Context columns
+  // come in groups of 2 nkv heads per layer (one group in a layer step, one
+  // per draft layer in the multi-layer context precompute).
   const int h = J.n0 / D;
-  int kind, j, hh = 0;
+  int kind, j, hh = 0, layer = 0;
   if (!J.second) {
     kind = h < nq ? 0 : (h < nq + nkv ? 1 : 2);
     j = kind == 0 ? h / g : (kind == 1 ? h - nq : h - nq - nkv);
     hh = kind == 0 ? h % g : 0;
   } else {
-    kind = h < nkv ? 1 : 2;
-    j = kind == 1 ? h : h - nkv;
+    layer = h / (2 * nkv);
+    const int hl = h - layer * 2 * nkv;
+    kind = hl < nkv ? 1 : 2;
+    j = kind == 1 ? hl : hl - nkv;
   }
+  T* const kc = static_cast<T*>(layer == 0 ? a.kc : a.layer_kc[layer]);
+  T* const vc = static_cast<T*>(layer == 0 ? a.vc : a.layer_vc[layer]);
 
   // Consumers: this lane's rows (sequence, window row: context rows first,
   // then block rows). After the swap below, wave (wm, wn) finishes whole rows
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
     block_barrier();
     // Values: raw, transposed into cache V (key index contiguous); each wave
     // writes its own half of the columns for all its rows.
-    T* vbase = static_cast<T*>(a.vc);
+    T* vbase = vc;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!ok[mi]) continue;
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
     constexpr int WN = decltype(wn_c)::value;
     // The head gains and cos/sin of this wave's rows go out now and arrive
     // during the swap.
-    const T* gain = static_cast<const T*>(kind == 0 ? a.q_norm : a.k_norm);
+    const T* gain = kind == 0 ? static_cast<const T*>(a.q_norm) : static_cast<const T*>(a.k_norm) + layer * D;
     T g1[NI][4], g2[NI][4];  // gains of columns t and t + D/2
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
         const int i = (J.m0 + wm * WM + mi * 16 + r16) % bs;
         dst = static_cast<T*>(a.qpack) + ((size_t)(b * nkv + j) * R + i * g + hh) * D;
       } else {
-        dst = static_cast<T*>(a.kc) + ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D;
+        dst = kc + ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D;
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {

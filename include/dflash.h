@@ -236,7 +236,8 @@ typedef struct {
     double rms_eps;
 } dflash_ctxkv_config;
 
-/* Device weights in the config dtype, borrowed (they must outlive the handle). */
+/* Device weights in the config dtype, borrowed (they must outlive the handle);
+ * hidden_norm and w_kv 16-byte aligned. */
 typedef struct {
     const void* hidden_norm;  /* [H] gain of the RMSNorm over the context states  */
     const void* w_kv;         /* [L * 2 * nkv * d, H]: layer l's K rows (its
@@ -264,7 +265,8 @@ size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx);
 /* Append the new context rows of `caches[0 .. L-1]->batch` sequences to every
  * layer's cache.
  *   context_states  device [sum n_b, H] raw context rows (before hidden_norm),
- *                   sequence b owning rows ctx_offsets[b] .. ctx_offsets[b+1]-1.
+ *                   16-byte aligned, sequence b owning rows
+ *                   ctx_offsets[b] .. ctx_offsets[b+1]-1.
  *   ctx_offsets     HOST [B + 1], ctx_offsets[0] == 0, non-decreasing.
  *   positions       device int32 [sum n_b]: the position of every context row
  *                   (normally len_b, len_b + 1, ...); each must lie in
@@ -281,6 +283,13 @@ size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx);
 int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
                         const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Where the precompute normalises, rotates and appends its K/V rows, as for
+ * dflash_layer_set_append_mode: DFLASH_APPEND_AUTO (default: in the
+ * projection's epilogue when it has about a tile per CU without splitting k,
+ * else in HK2 after an fp32 projection), DFLASH_APPEND_FUSED,
+ * DFLASH_APPEND_SEPARATE. Errors: DFLASH_ERR_ARG. */
+int dflash_ctxkv_set_append_mode(dflash_ctxkv* h, int32_t mode);
 
 /* Synchronise `stream` and report the sticky device error (DFLASH_ERR_RANGE
  * if a position fell outside the table since the last poll, which clears it),

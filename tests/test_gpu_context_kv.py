@@ -55,8 +55,10 @@ def oracle_caches(case):
             for layer in range(case.cfg.n_layers)]
 
 
-def run_and_check(case, capacity=None):
+def run_and_check(case, capacity=None, mode=None):
     pre = make_precompute(case)
+    if mode is not None:
+        pre.set_append_mode(mode)
     caches = make_caches(case, capacity)
     before = [(raw_bits(c.k), raw_bits(c.v)) for c in caches]
     dt = torch_dt(case)
@@ -88,17 +90,20 @@ def run_and_check(case, capacity=None):
     return pre, caches, ref, worst
 
 
+@pytest.mark.parametrize("mode", ["fused", "separate"])
 @pytest.mark.parametrize("name", ["P1", "small_bf16", "small_bf16_d64", "one_layer", "P3"])
-def test_context_kv_precompute_matches_oracle(name):
+def test_context_kv_precompute_matches_oracle(name, mode):
+    # In "fused" the projection's epilogue normalises, rotates and appends one
+    # head per tile; in "separate" HK2 does it over the layers from fp32 rows.
     case = {"P1": lambda: make_ctxkv_case("P1", seed=0),
             "small_bf16": lambda: make_ctxkv_case(small(), seed=1),
             "small_bf16_d64": lambda: make_ctxkv_case(small(head_dim=64, hidden=256, n_layers=5,
                                                             config_id=46), seed=2),
             "one_layer": lambda: make_ctxkv_case(small(n_layers=1, batch=2, config_id=47), seed=3),
             "P3": lambda: make_ctxkv_case("P3", seed=0)}[name]()
-    print(f"[{name}] layers {case.cfg.n_layers}, rows {int(case.ctx_offsets[-1])}", flush=True)
-    _, _, _, worst = run_and_check(case)
-    print(f"[{name}] max abs {worst[0]:.3e} rel-RMS {worst[1]:.3e}", flush=True)
+    print(f"[{name} {mode}] layers {case.cfg.n_layers}, rows {int(case.ctx_offsets[-1])}", flush=True)
+    _, _, _, worst = run_and_check(case, mode=mode)
+    print(f"[{name} {mode}] max abs {worst[0]:.3e} rel-RMS {worst[1]:.3e}", flush=True)
 
 
 def test_context_kv_prefill_rows_sampled():
