@@ -54,6 +54,8 @@ def parse():
                     help="where q/k norm + RoPE + cache append run (projection epilogue or own kernel)")
     ap.add_argument("--ctxkv-steps", type=int, default=50,
                     help="timed runs of the multi-layer context K/V precompute (0: skip)")
+    ap.add_argument("--context-kv-only", default=None, choices=("P3", "P4"),
+                    help="only time the context K/V precompute on this workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -121,7 +123,7 @@ def cpu_baseline(case, n_seq: int, runs: int = 5):
                       f"{len(times)} runs of {t:.2f}s"}
 
 
-def bench_context_kv(steps: int, warmup: int):
+def bench_context_kv(steps: int, warmup: int, names=("P3", "P4")):
     """The multi-layer context K/V precompute on its two workloads: P3 (the
     context rows of one C3 decode round, 3 layers) and P4 (a 4096-row prefill,
     3 layers). Each run appends every layer's rows and the lengths are rewound
@@ -134,7 +136,7 @@ def bench_context_kv(steps: int, warmup: int):
     from workload import make_ctxkv_case
 
     res = {}
-    for name in ("P3", "P4"):
+    for name in names:
         case = make_ctxkv_case(name, seed=0)
         c = case.cfg
         dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
@@ -204,6 +206,10 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.context_kv_only:
+        print(json.dumps({"context_kv_precompute": bench_context_kv(a.ctxkv_steps, 5, (a.context_kv_only,))}),
+              flush=True)
         return
 
     import numpy as np
