@@ -1,5 +1,5 @@
-"""Float64 CPU oracle of the DFlash draft-attention layer step and of the
-multi-layer context K/V precompute.
+"""Float64 CPU oracle of the DFlash draft-attention layer step, of the
+multi-layer context K/V precompute and of the draft decoder layer.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -18,3 +18,4 @@ from .ref_fp64 import (  # noqa: F401
     window_keep,
 )
 from .context_kv import context_kv_precompute  # noqa: F401
+from .decoder import decoder_layer_step, mlp, silu  # noqa: F401

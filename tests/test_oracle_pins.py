@@ -517,3 +517,74 @@ def test_context_kv_precompute_layers_use_their_own_weights():
         for s in range(2):
             np.testing.assert_array_equal(a[layer].k[s], r[cfg.n_layers - 1 - layer].k[s])
             np.testing.assert_array_equal(a[layer].v[s], r[cfg.n_layers - 1 - layer].v[s])
+
+
+# ----------------------------------------------------------- draft decoder layer
+
+def test_silu_closed_forms_and_limits():
+    xs = np.array([-700.0, -30.0, -1.0, -1e-3, 0.0, 1e-3, 1.0, 30.0, 700.0])
+    s = oracle.silu(xs)
+    assert s[4] == 0.0
+    np.testing.assert_allclose(s[6], 1.0 / (1.0 + math.exp(-1.0)), rtol=1e-15)
+    # silu(x) - silu(-x) = x(sigmoid(x) + sigmoid(-x)) = x
+    np.testing.assert_allclose(s[5:] - s[:4][::-1], xs[5:], rtol=1e-12, atol=1e-300)
+    assert s[-1] == 700.0 and abs(s[0]) < 1e-300 and np.all(np.isfinite(s))
+    # slope 1/2 at 0
+    assert abs((oracle.silu(np.array([1e-7]))[0] - oracle.silu(np.array([-1e-7]))[0]) / 2e-7 - 0.5) < 1e-6
+
+
+def decoder_inputs(cfg, rng, inter):
+    from workload import MLPWeights
+    H = cfg.hidden
+    mw = MLPWeights(input_norm=rng.uniform(0.5, 1.5, H), post_norm=rng.uniform(0.5, 1.5, H),
+                    w_gate_up=rng.standard_normal((2 * inter, H)) * 0.3,
+                    w_down=rng.standard_normal((H, inter)) * 0.3)
+    return mw
+
+
+def test_decoder_layer_matches_pure_python_brute_force():
+    """input_layernorm, the layer step (its own brute force), residual add,
+    post_attention_layernorm, silu(gate) * up, down, residual add: in loops and
+    the math module only."""
+    cfg = tiny_cfg(batch=2)
+    rng = np.random.default_rng(21)
+    w = rand_weights(cfg, rng)
+    mw = decoder_inputs(cfg, rng, inter=5)
+    lens, news = [2, 1], [3, 0]
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens, news)
+    got, new = oracle.decoder_layer_step(cfg, w, mw, cache, X, C, offs, pos)
+    H, eps = cfg.hidden, cfg.rms_eps
+
+    def norm(v, gain):
+        ms = sum(t * t for t in v) / len(v)
+        return [v[i] / math.sqrt(ms + eps) * float(gain[i]) for i in range(len(v))]
+
+    rows = [list(map(float, r)) for r in X]
+    a = np.array([norm(r, mw.input_norm) for r in rows])
+    att, _, _ = brute_step(cfg, w, cache, a, C, offs, pos)
+    inter = mw.w_gate_up.shape[0] // 2
+    for i, r in enumerate(rows):
+        h = [r[c] + float(att[i][c]) for c in range(H)]
+        m = norm(h, mw.post_norm)
+        act = []
+        for j in range(inter):
+            g = sum(m[c] * float(mw.w_gate_up[j][c]) for c in range(H))
+            u = sum(m[c] * float(mw.w_gate_up[inter + j][c]) for c in range(H))
+            act.append(g / (1.0 + math.exp(-g)) * u)
+        o = [h[c] + sum(act[j] * float(mw.w_down[c][j]) for j in range(inter)) for c in range(H)]
+        np.testing.assert_allclose(got[i], o, rtol=1e-11, atol=1e-11)
+
+
+def test_decoder_layer_with_silent_branches_passes_the_stream_through():
+    """With o_proj and down_proj zero both branches add exactly 0: the output
+    is the input stream bit for bit, while the cache still gets its rows."""
+    cfg = tiny_cfg(batch=2)
+    rng = np.random.default_rng(22)
+    w = rand_weights(cfg, rng)
+    w.w_o = np.zeros_like(w.w_o)
+    mw = decoder_inputs(cfg, rng, inter=4)
+    mw.w_down = np.zeros_like(mw.w_down)
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, [1, 3], [2, 1])
+    got, new = oracle.decoder_layer_step(cfg, w, mw, cache, X, C, offs, pos)
+    np.testing.assert_array_equal(got, X)
+    assert new.lengths == [1 + 2 + cfg.block_size, 3 + 1 + cfg.block_size]

@@ -19,3 +19,4 @@ from .ctxkv import (  # noqa: F401
     CtxKVWeights,
     make_ctxkv_case,
 )
+from .decoder import QWEN3_8B_INTERMEDIATE, MLPWeights, make_mlp_weights  # noqa: F401
