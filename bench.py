@@ -54,6 +54,10 @@ def parse():
                     help="where q/k norm + RoPE + cache append run (projection epilogue or own kernel)")
     ap.add_argument("--ctxkv-steps", type=int, default=50,
                     help="timed runs of the multi-layer context K/V precompute (0: skip)")
+    ap.add_argument("--decoder-steps", type=int, default=30,
+                    help="timed steps of the whole draft decoder layer at C3 (0: skip)")
+    ap.add_argument("--decoder-only", action="store_true",
+                    help="only time the draft decoder layer (for profiling)")
     ap.add_argument("--context-kv-only", default=None, choices=("P3", "P4"),
                     help="only time the context K/V precompute on this workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -198,6 +202,83 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4")):
     return res
 
 
+def bench_decoder(steps: int, warmup: int, seed: int = 0, copies: int = 3):
+    """One draft decoder layer step at C3 (input_layernorm, the attention layer
+    step, residual, post_attention_layernorm, SwiGLU MLP of width 12288,
+    residual), timed with HIP events on the launch stream over `steps` steps;
+    KV-cache copies rotate and lengths are rewound on the host as for the
+    layer step."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import DFlashDecoder, KVCache, LayerShape
+    from workload import QWEN3_8B_INTERMEDIATE, make_case, make_mlp_weights
+
+    case = make_case("C3", seed=seed)
+    cfg = case.cfg
+    inter = QWEN3_8B_INTERMEDIATE
+    mw = make_mlp_weights(case, inter)
+    dt = torch.bfloat16
+
+    def dev(x, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+    w = case.weights
+    dec = DFlashDecoder(LayerShape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, dt,
+                                   cfg.rope_theta, cfg.rms_eps, cfg.sliding_window, cfg.max_position), inter,
+                        dev(w.w_qkv), dev(w.w_o), dev(w.q_norm), dev(w.k_norm), dev(mw.input_norm),
+                        dev(mw.post_norm), dev(mw.w_gate_up), dev(mw.w_down))
+    B, bs = case.batch, cfg.block_size
+    caches = []
+    for i in range(copies):
+        c = KVCache(B, cfg.n_kv_heads, cfg.head_dim, case.capacity(), dt)
+        if i == 0:
+            for b in range(B):
+                c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
+        else:
+            c.k.copy_(caches[0].k)
+            c.v.copy_(caches[0].v)
+            c.set_lengths(case.cached_len)
+        caches.append(c)
+    x, th, pos = dev(case.hidden_states), dev(case.target_hidden), dev(case.positions, torch.int32)
+    offs = [int(o) for o in case.ctx_offsets]
+    out = torch.empty_like(x)
+    ws = dec.workspace(B, offs[-1])
+    L0 = case.cached_len.copy()
+
+    def one(i):
+        cache = caches[i % copies]
+        dec.step(x, th, offs, pos, cache, out=out, workspace=ws)
+        cache.set_lengths(L0)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        one(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    if dec.poll_error() != 0:
+        raise RuntimeError("position outside the RoPE table")
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    H, mq = cfg.hidden, B * bs
+    mlp_flops = 2.0 * mq * H * 3 * inter
+    res = {
+        "workload": (f"C3 decoder layer: B={B}, block {bs}, H={H}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads, "
+                     f"head_dim {cfg.head_dim}, MLP width {inter}, bf16"),
+        "us_per_step": round(us, 2),
+        "tokens_per_s": round(mq / (us * 1e-6), 1),
+        "mlp_gflop": round(mlp_flops / 1e9, 1),
+        "mlp_weight_mb": round(3 * inter * H * 2 / 1e6, 1),
+    }
+    dec.close()
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -206,6 +287,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.decoder_only:
+        print(json.dumps({"decoder_layer": bench_decoder(a.decoder_steps, 5)}), flush=True)
         return
     if a.context_kv_only:
         print(json.dumps({"context_kv_precompute": bench_context_kv(a.ctxkv_steps, 5, (a.context_kv_only,))}),
@@ -355,6 +439,8 @@ def main():
     torch.cuda.empty_cache()
     if a.ctxkv_steps > 0:
         line["context_kv_precompute"] = bench_context_kv(a.ctxkv_steps, 5)
+    if a.decoder_steps > 0:
+        line["decoder_layer"] = bench_decoder(a.decoder_steps, 5)
     print(json.dumps(line), flush=True)
 
 

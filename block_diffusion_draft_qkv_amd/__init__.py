@@ -22,8 +22,8 @@ import torch
 from . import _lib
 from ._lib import DFlashError, check  # noqa: F401
 
-__all__ = ["DFlashLayer", "KVCache", "LayerShape", "ContextKV", "ContextKVShape", "DFlashError",
-           "KERNEL_NAMES"]
+__all__ = ["DFlashLayer", "KVCache", "LayerShape", "ContextKV", "ContextKVShape", "DFlashDecoder",
+           "rms_norm", "DFlashError", "KERNEL_NAMES"]
 KERNEL_NAMES = _lib.KERNEL_NAMES
 
 _DTYPES = {torch.float32: _lib.DFLASH_F32, torch.bfloat16: _lib.DFLASH_BF16}
@@ -262,3 +262,104 @@ class ContextKV:
             self.close()
         except Exception:
             pass
+
+
+class _BorrowedLayer(DFlashLayer):
+    """The attention layer a decoder owns (no destroy of its own)."""
+
+    def __init__(self, shape: LayerShape, handle):
+        self.shape = shape
+        self._h = handle
+        self._weights = []
+        self._ws = None
+
+    def close(self) -> None:
+        self._h = None
+
+
+class DFlashDecoder:
+    """One draft decoder layer: input_layernorm, the attention layer step,
+    residual add, post_attention_layernorm, SwiGLU MLP, residual add.
+    ``w_gate_up`` is ``[2 I, H]`` (gate rows, then up rows), ``w_down``
+    ``[H, I]``; the attention weights are those of ``DFlashLayer``."""
+
+    def __init__(self, shape: LayerShape, intermediate: int, w_qkv, w_o, q_norm, k_norm, input_norm, post_norm,
+                 w_gate_up, w_down):
+        self.shape, self.intermediate = shape, int(intermediate)
+        self._weights = [t.contiguous() for t in (w_qkv, w_o, q_norm, k_norm, input_norm, post_norm, w_gate_up,
+                                                  w_down)]
+        for t in self._weights:
+            if t.dtype != shape.dtype or not t.is_cuda:
+                raise ValueError("weights must be device tensors of the layer dtype")
+        acfg = _lib.Config(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.block_size,
+                           shape.sliding_window, shape.max_position, _DTYPES[shape.dtype], float(shape.rope_theta),
+                           float(shape.rms_eps))
+        cfg = _lib.DecoderConfig(acfg, self.intermediate)
+        p = [t.data_ptr() for t in self._weights]
+        w = _lib.DecoderWeights(_lib.Weights(*p[:4]), *p[4:])
+        handle = C.c_void_p()
+        with torch.cuda.device(self._weights[0].device):
+            check(_lib.lib().dflash_decoder_create(C.byref(cfg), C.byref(w), C.byref(handle)),
+                  "dflash_decoder_create")
+        self._h = handle
+        self._ws: Optional[torch.Tensor] = None
+        self.attention = _BorrowedLayer(shape, C.c_void_p(_lib.lib().dflash_decoder_attention(handle)))
+
+    def workspace(self, batch: int, total_ctx: int) -> torch.Tensor:
+        need = int(_lib.lib().dflash_decoder_workspace_bytes(self._h, int(batch), int(total_ctx)))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+        return self._ws
+
+    def step(self, x: torch.Tensor, target_hidden: Optional[torch.Tensor], ctx_offsets, positions: torch.Tensor,
+             cache: KVCache, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+        s = self.shape
+        if len(ctx_offsets) != cache.batch + 1:
+            raise ValueError("ctx_offsets must have batch + 1 entries")
+        if x.dtype != s.dtype or not x.is_contiguous():
+            raise ValueError("x must be contiguous in the layer dtype")
+        if positions.dtype != torch.int32 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 device tensor")
+        if target_hidden is not None and target_hidden.numel() == 0:
+            target_hidden = None
+        if target_hidden is not None and (target_hidden.dtype != s.dtype or not target_hidden.is_contiguous()):
+            raise ValueError("target_hidden must be contiguous in the layer dtype")
+        offs = (C.c_int32 * (cache.batch + 1))(*[int(o) for o in ctx_offsets])
+        if out is None:
+            out = torch.empty_like(x)
+        if workspace is None:
+            workspace = self.workspace(cache.batch, int(ctx_offsets[-1]))
+        st = _lib.lib().dflash_decoder_step(self._h, _ptr(x), _ptr(target_hidden), offs, _ptr(positions),
+                                            C.byref(cache.desc), _ptr(out), _ptr(workspace), workspace.numel(),
+                                            _stream_handle(stream))
+        check(st, "dflash_decoder_step")
+        return out
+
+    def poll_error(self, stream=None) -> int:
+        return self.attention.poll_error(stream)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.lib().dflash_decoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float, out: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """Row RMSNorm (the draft model's final norm) of a contiguous [rows, H] tensor."""
+    if x.dtype not in _DTYPES or gain.dtype != x.dtype or not x.is_contiguous() or not gain.is_contiguous():
+        raise ValueError("x and gain must be contiguous fp32 or bf16 tensors of one dtype")
+    if out is None:
+        out = torch.empty_like(x)
+    rows, h = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.shape[0])
+    st = _lib.lib().dflash_rms_norm(_ptr(x), _ptr(gain), _ptr(out), int(rows), int(h), float(eps), _DTYPES[x.dtype],
+                                    _stream_handle(stream))
+    check(st, "dflash_rms_norm")
+    return out

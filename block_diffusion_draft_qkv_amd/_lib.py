@@ -34,6 +34,8 @@ EXPORTS = (
     "dflash_layer_set_append_mode",
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
     "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
+    "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
+    "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
 )
 
 
@@ -62,6 +64,15 @@ class CtxKVConfig(C.Structure):
 
 class CtxKVWeights(C.Structure):
     _fields_ = [("hidden_norm", C.c_void_p), ("w_kv", C.c_void_p), ("k_norm", C.c_void_p)]
+
+
+class DecoderConfig(C.Structure):
+    _fields_ = [("attn", Config), ("intermediate", C.c_int32)]
+
+
+class DecoderWeights(C.Structure):
+    _fields_ = [("attn", Weights), ("input_norm", C.c_void_p), ("post_norm", C.c_void_p),
+                ("w_gate_up", C.c_void_p), ("w_down", C.c_void_p)]
 
 
 class DFlashError(RuntimeError):
@@ -115,6 +126,22 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_poll_error.restype = C.c_int
         h.dflash_ctxkv_set_append_mode.argtypes = [C.c_void_p, C.c_int32]
         h.dflash_ctxkv_set_append_mode.restype = C.c_int
+        h.dflash_decoder_create.argtypes = [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights),
+                                            C.POINTER(C.c_void_p)]
+        h.dflash_decoder_create.restype = C.c_int
+        h.dflash_decoder_destroy.argtypes = [C.c_void_p]
+        h.dflash_decoder_destroy.restype = None
+        h.dflash_decoder_attention.argtypes = [C.c_void_p]
+        h.dflash_decoder_attention.restype = C.c_void_p
+        h.dflash_decoder_workspace_bytes.argtypes = [C.c_void_p, C.c_int32, C.c_int64]
+        h.dflash_decoder_workspace_bytes.restype = C.c_size_t
+        h.dflash_decoder_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32), C.c_void_p,
+                                          C.POINTER(KVCacheDesc), C.c_void_p, C.c_void_p, C.c_size_t,
+                                          C.c_void_p]
+        h.dflash_decoder_step.restype = C.c_int
+        h.dflash_rms_norm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_double,
+                                      C.c_int32, C.c_void_p]
+        h.dflash_rms_norm.restype = C.c_int
         h.dflash_status_string.argtypes = [C.c_int]
         h.dflash_status_string.restype = C.c_char_p
         _lib = h

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdflash.so")
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "norm_rope_append.hip", "attention.hip", "context_kv.hip", "dflash.cpp"]
+SOURCES = ["gemm.hip", "norm_rope_append.hip", "attention.hip", "row_norm.hip", "dflash.cpp"]
 
 
 def hipcc() -> str:

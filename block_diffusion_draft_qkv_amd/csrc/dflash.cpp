@@ -55,6 +55,13 @@ struct dflash_layer {
   int64_t count[DFLASH_K_COUNT] = {};
 };
 
+struct dflash_decoder {
+  dflash_decoder_config cfg;
+  dflash_decoder_weights w;
+  dflash_layer* attn = nullptr;
+  int num_cus = 256;
+};
+
 struct dflash_ctxkv {
   dflash_ctxkv_config cfg;
   dflash_ctxkv_weights w;
@@ -274,9 +281,12 @@ size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t tota
   return carve(L, batch, total_ctx).total;
 }
 
-int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* target_hidden,
-                     const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+// The layer step; with validate_only it returns after the host-side checks,
+// having enqueued nothing (the decoder layer checks before its first launch).
+static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void* target_hidden,
+                          const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream,
+                          bool validate_only) {
   if (!L || !hidden_states || !ctx_offsets || !positions || !cache || !out) return DFLASH_ERR_ARG;
   if (!cache->k || !cache->v || !cache->len) return DFLASH_ERR_ARG;
   const dflash_config& c = L->cfg;
@@ -315,6 +325,7 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
   const Carve wc = carve(L, B, Mc);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return DFLASH_ERR_WORKSPACE;
+  if (validate_only) return DFLASH_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -455,6 +466,13 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
 
   for (int b = 0; b < B; ++b) cache->len[b] += (ctx_offsets[b + 1] - ctx_offsets[b]) + bs;
   return DFLASH_OK;
+}
+
+int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* target_hidden,
+                     const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, workspace,
+                        workspace_bytes, stream, false);
 }
 
 int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len) {
@@ -609,7 +627,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   const int N = nl * 2 * nkv * d;
 
   // hidden_norm over each raw context row
-  if (launch_rms_rows(c.dtype, context_states, h->w.hidden_norm, normed, (int)Mc, H, (float)c.rms_eps, s) !=
+  if (launch_rms_rows(c.dtype, context_states, nullptr, h->w.hidden_norm, nullptr, normed, (int)Mc, H,
+                      (float)c.rms_eps, s) !=
       hipSuccess)
     return DFLASH_ERR_HIP;
   // Every layer's K and V in one projection. With enough 64-row tiles (one
@@ -686,6 +705,142 @@ int dflash_ctxkv_poll_error(dflash_ctxkv* h, void* stream) {
     if (hipMemset(h->err, 0, sizeof(int32_t)) != hipSuccess) return DFLASH_ERR_HIP;
     return DFLASH_ERR_RANGE;
   }
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------- decoder layer
+
+namespace {
+// Workspace of a decoder step: the attention's, then input_layernorm output a,
+// attention output, residual h, post_attention_layernorm output m ([Mq, H]
+// each) and the MLP activation [Mq, I], all in the element type.
+struct DecCarve {
+  size_t attn, a, att, h, m, act, total;
+};
+DecCarve dec_carve(const dflash_decoder* D, int64_t batch, int64_t total_ctx) {
+  const dflash_config& c = D->cfg.attn;
+  const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, mq = batch * c.block_size;
+  DecCarve w{};
+  size_t off = 0;
+  w.attn = off; off += align_up(carve(D->attn, batch, total_ctx).total);
+  w.a = off;    off += align_up(mq * c.hidden * es);
+  w.att = off;  off += align_up(mq * c.hidden * es);
+  w.h = off;    off += align_up(mq * c.hidden * es);
+  w.m = off;    off += align_up(mq * c.hidden * es);
+  w.act = off;  off += align_up(mq * D->cfg.intermediate * es);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+int dflash_decoder_create(const dflash_decoder_config* cfg, const dflash_decoder_weights* weights,
+                          dflash_decoder** out) {
+  if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
+  *out = nullptr;
+  if (!weights->input_norm || !weights->post_norm || !weights->w_gate_up || !weights->w_down)
+    return DFLASH_ERR_ARG;
+  for (const void* p : {weights->input_norm, weights->post_norm})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return DFLASH_ERR_ARG;
+  if (cfg->intermediate <= 0 || cfg->intermediate % 64) return DFLASH_ERR_SHAPE;
+  dflash_decoder* D = new (std::nothrow) dflash_decoder();
+  if (!D) return DFLASH_ERR_HIP;
+  D->cfg = *cfg;
+  D->w = *weights;
+  const int st = dflash_layer_create(&cfg->attn, &weights->attn, &D->attn);
+  if (st != DFLASH_OK) {
+    delete D;
+    return st;
+  }
+  D->num_cus = D->attn->num_cus;
+  *out = D;
+  return DFLASH_OK;
+}
+
+void dflash_decoder_destroy(dflash_decoder* D) {
+  if (!D) return;
+  dflash_layer_destroy(D->attn);
+  delete D;
+}
+
+size_t dflash_decoder_workspace_bytes(const dflash_decoder* D, int32_t batch, int64_t total_ctx) {
+  if (!D || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0) return 0;
+  return dec_carve(D, batch, total_ctx).total;
+}
+
+int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hidden, const int32_t* ctx_offsets,
+                        const int32_t* positions, dflash_kv_cache* cache, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!D || !x || !out || !ctx_offsets || !cache) return DFLASH_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return DFLASH_ERR_ARG;
+  const dflash_config& c = D->cfg.attn;
+  const int B = cache->batch;
+  if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
+  if (!workspace) return DFLASH_ERR_WORKSPACE;
+  const int64_t Mc = ctx_offsets[B];
+  if (Mc < 0) return DFLASH_ERR_SHAPE;
+  const DecCarve wc = dec_carve(D, B, Mc);
+  if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign) return DFLASH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* a = ws + wc.a;
+  void* att = ws + wc.att;
+  void* h = ws + wc.h;
+  void* m = ws + wc.m;
+  void* act = ws + wc.act;
+  const size_t attn_bytes = wc.a - wc.attn;
+  // every check of the attention step before anything is enqueued
+  int st = attn_step_impl(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
+                          stream, true);
+  if (st != DFLASH_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = c.hidden, I = D->cfg.intermediate, Mq = B * c.block_size;
+  const float eps = (float)c.rms_eps;
+  // input_layernorm, then the attention layer step (its o_proj output in att)
+  if (launch_rms_rows(c.dtype, x, nullptr, D->w.input_norm, nullptr, a, Mq, H, eps, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  st = attn_step_impl(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
+                      stream, false);
+  if (st != DFLASH_OK) return st;
+  // h = x + att (the residual stream), m = post_attention_layernorm(h)
+  if (launch_rms_rows(c.dtype, x, att, D->w.post_norm, h, m, Mq, H, eps, s) != hipSuccess) return DFLASH_ERR_HIP;
+  // act = silu(m Wg^T) * (m Wu^T)
+  {
+    const int tn = (2 * I + 127) / 128;
+    const int t64 = ((Mq + 63) / 64) * tn, t128 = ((Mq + 127) / 128) * tn;
+    const long r64 = (long)((t64 + D->num_cus - 1) / D->num_cus) * (64 + 128);
+    const long r128 = (long)((t128 + D->num_cus - 1) / D->num_cus) * (128 + 128);
+    const int bm = r128 <= r64 ? 128 : 64;
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.nprob = 1;
+    ga.p[0] = {m, D->w.w_gate_up, act, Mq, 2 * I, H, H, H, I, tn, 0, 0};
+    ga.p[0].b_pair = I;
+    if (launch_gemm_swiglu(c.dtype, ga, bm == 128 ? t128 : t64, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  // out = h + act Wd^T
+  {
+    const TileChoice t = choose_tiles(D->num_cus, Mq, H, 0, 0, false);
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.nprob = 1;
+    ga.p[0] = {act, D->w.w_down, out, Mq, H, I, I, I, H, (H + t.bn - 1) / t.bn, 0, 0};
+    ga.p[0].r = h;
+    if (launch_gemm(c.dtype, false, ga, t.tiles, t.bm, t.bn, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  return DFLASH_OK;
+}
+
+dflash_layer* dflash_decoder_attention(dflash_decoder* D) { return D ? D->attn : nullptr; }
+
+int dflash_rms_norm(const void* x, const void* gain, void* out, int32_t rows, int32_t hidden, double eps,
+                    int32_t dtype, void* stream) {
+  if (!x || !gain || !out || rows < 0 || hidden <= 0 || hidden % 64 || !(eps >= 0.0)) return DFLASH_ERR_ARG;
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return DFLASH_ERR_ARG;
+  for (const void* p : {x, gain, static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return DFLASH_ERR_ARG;
+  if (launch_rms_rows(dtype, x, nullptr, gain, nullptr, out, rows, hidden, (float)eps,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DFLASH_ERR_HIP;
   return DFLASH_OK;
 }
 

@@ -123,7 +123,13 @@ __device__ __forceinline__ bool gemm_core(const TileJob& J, uint32_t lds0, int e
     for (int i = 0; i < BPP; ++i) {
       const int row = (i * kGemmProducers + pw) * 8 + lane / 8;
       const int c = (lane % 8) ^ rswz<8>(row);
-      const int gr = n0 + row < P.n ? n0 + row : P.n - 1;
+      int gr;
+      if (P.b_pair == 0) {
+        gr = n0 + row < P.n ? n0 + row : P.n - 1;
+      } else {  // gate rows for the tile's first half, up rows for its second
+        const int j = n0 / 2 + (row < BN / 2 ? row : row - BN / 2);
+        gr = (j < P.b_pair ? j : P.b_pair - 1) + (row < BN / 2 ? 0 : P.b_pair);
+      }
       boff[i] = (uint32_t)((size_t)gr * P.ldb * sizeof(T)) + (uint32_t)(c * 16);
     }
     const char* Ab = static_cast<const char*>(P.a);
@@ -228,6 +234,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
   // acc[ni][mi]: lane holds m = r16 of block mi and n = 4q .. 4q+3 of block ni.
   OutT* C = static_cast<OutT*>(J.P.c) + (size_t)blockIdx.y * J.P.slice_stride;
+  const OutT* Rs = static_cast<const OutT*>(J.P.r);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int m = J.m0 + wm * WM + mi * 16 + r16;
@@ -235,7 +242,73 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int n = J.n0 + wn * WN + ni * 16 + 4 * q;
-      if (n < J.P.n) Store4<OutT>::put(C + (size_t)m * J.P.ldc + n, acc[ni][mi]);
+      if (n >= J.P.n) continue;
+      f32x4 v = acc[ni][mi];
+      if (Rs != nullptr) {
+        const OutT* rr = Rs + (size_t)m * J.P.ldc + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += Elem<OutT>::to_f32(rr[r]);
+      }
+      Store4<OutT>::put(C + (size_t)m * J.P.ldc + n, v);
+    }
+  }
+}
+
+// Qwen3MLP's gate/up projection with SiLU(gate) * up in the epilogue (NeMo
+// page "draft_qwen3": Qwen3DFlashDecoderLayer, mlp = Qwen3MLP; vLLM page
+// "qwen3_dflash": gate_proj and up_proj stacked as gate_up_proj). A tile is
+// BM rows x 128 columns whose first 64 are gate rows j0 .. j0+63 of the weight
+// and last 64 the up rows b_pair + j0 .. (b_pair set); consumer wave (wm, wn)
+// holds the gate (wn = 0) or up (wn = 1) half, so every value's partner sits
+// in the same lane and register of wave (wm, 1 - wn). The two waves trade half
+// of their row blocks through the free LDS ring and each finishes the other
+// half: silu(g) = g / (1 + e^-g), times u, rounded once to the output type.
+template <typename T, int BM>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_swiglu_kernel(GemmArgs args) {
+  constexpr int BN = 128;
+  using Sh = GemmShape<BM, BN>;
+  constexpr int MI = Sh::MI, NI = Sh::NI, WM = Sh::WM, MH = MI / 2, XR = MH * NI * 4;
+  static_assert(4 * XR * 64 * 4 <= Sh::S * Sh::STAGE, "the exchange fits in the ring");
+  __shared__ u32x4 lds[Sh::S * Sh::STAGE / 16];
+  TileJob J = tile_job<BM, BN>(args);
+  J.k_first = 0;
+  J.nk = J.P.k / (8 * (16 / (int)sizeof(T)));
+  f32x4 acc[NI][MI];
+  if (!gemm_core<T, BM, BN>(J, lds_base(lds), 2, acc)) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
+  float* xch = reinterpret_cast<float*>(lds);
+  const int partner = wm * 2 + (1 - wn);
+  block_barrier();  // the last fragment reads of the main loop are done
+  // hand over the row blocks the partner finishes: (1 - wn) * MH .. + MH - 1
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int u = 0; u < MH; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xch[(wave * XR + (ni * MH + u) * 4 + r) * 64 + lane] =
+            wn == 0 ? acc[ni][MH + u][r] : acc[ni][u][r];
+  block_barrier();
+  T* C = static_cast<T*>(J.P.c);
+  const int j0 = J.n0 / 2;
+#pragma unroll
+  for (int u = 0; u < MH; ++u) {
+    const int mi = wn * MH + u;
+    const int m = J.m0 + wm * WM + mi * 16 + r16;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float own = wn == 0 ? acc[ni][u][r] : acc[ni][MH + u][r];
+        const float oth = xch[(partner * XR + (ni * MH + u) * 4 + r) * 64 + lane];
+        const float g = wn == 0 ? own : oth, up = wn == 0 ? oth : own;
+        o[r] = g / (1.0f + __expf(-g)) * up;
+      }
+      const int j = j0 + ni * 16 + 4 * q;
+      if (m < J.P.m && j < J.P.b_pair) Store4<T>::put(C + (size_t)m * J.P.ldc + j, o);
     }
   }
 }
@@ -506,6 +579,19 @@ hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, con
   if (total_tiles <= 0) return hipSuccess;
   if (dtype == 1) return launch_append_t<__bf16>(args, nr, total_tiles, bm, head_dim, stream);
   return launch_append_t<float>(args, nr, total_tiles, bm, head_dim, stream);
+}
+
+hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, int bm, hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  const dim3 grid(total_tiles), block(kGemmThreads);
+  if (dtype == 1) {
+    if (bm == 128) hipLaunchKernelGGL((gemm_swiglu_kernel<__bf16, 128>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((gemm_swiglu_kernel<__bf16, 64>), grid, block, 0, stream, args);
+  } else {
+    if (bm == 128) hipLaunchKernelGGL((gemm_swiglu_kernel<float, 128>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((gemm_swiglu_kernel<float, 64>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles, int bm, int bn,

@@ -22,6 +22,12 @@ struct GemmProblem {
   int32_t tiles_n;       // ceil(n / BN)
   int32_t tile_begin;    // first flat tile index of this problem in the launch
   int64_t slice_stride;  // elements between k-slice outputs
+  // Optional, plain GEMM without a k split: C = A W^T + R (R [m][ldc] in the
+  // output type, rounded once after the sum).
+  const void* r = nullptr;
+  // SwiGLU GEMM: W rows [0, b_pair) are the gate rows, [b_pair, 2 b_pair) the
+  // up rows; output column j of a tile pairs gate row j and up row b_pair + j.
+  int32_t b_pair = 0;
 };
 struct GemmArgs {
   GemmProblem p[2];
@@ -64,9 +70,17 @@ hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, i
                             int max_new_rows, int layers, hipStream_t stream);
 
 // RMSNorm of `rows` rows of h elements (h % 64 == 0) with gain g [h]:
-// out = x / sqrt(mean(x^2) + eps) * g, fp32 math, stored in the element type.
-hipError_t launch_rms_rows(int dtype, const void* x, const void* g, void* out, int rows, int h,
-                           float eps, hipStream_t stream);
+// out = v / sqrt(mean(v^2) + eps) * g with v = x, or v = x + y rounded to the
+// element type (then also stored to hout) when y is given; fp32 math, stored in
+// the element type; 16-byte aligned rows.
+hipError_t launch_rms_rows(int dtype, const void* x, const void* y, const void* g, void* hout, void* out,
+                           int rows, int h, float eps, hipStream_t stream);
+
+// Qwen3MLP's gate/up projection with its activation in the epilogue:
+// C[m][j] = silu(A W_gate^T)[m][j] * (A W_up^T)[m][j] for j < n = b_pair, with
+// W = [W_gate; W_up] stacked ([2 n, k]); one problem, bm x 128 tiles (64 outputs
+// per tile), C in the element type.
+hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, int bm, hipStream_t stream);
 
 // The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
 // head_dim, no k split) doing the work of launch_norm_rope in its epilogue

@@ -296,6 +296,72 @@ int dflash_ctxkv_set_append_mode(dflash_ctxkv* h, int32_t mode);
  * or DFLASH_OK. */
 int dflash_ctxkv_poll_error(dflash_ctxkv* h, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Draft decoder layer: the attention layer step inside its block (NeMo page
+ * "draft_qwen3": Qwen3DFlashDecoderLayer with input_layernorm, self_attn,
+ * post_attention_layernorm and mlp = Qwen3MLP; vLLM page "qwen3_dflash":
+ * gate_proj/up_proj stacked as gate_up_proj, DFlashQwen3Model.forward threading
+ * the residual stream and ending with the final norm). For the noise stream x
+ * of the block's rows:
+ *   a   = RMSNorm(x) * input_norm
+ *   h   = x + attention_step(a, target_hidden, ...)     (o_proj included)
+ *   m   = RMSNorm(h) * post_norm
+ *   out = h + (silu(m Wg^T) * (m Wu^T)) Wd^T            silu(g) = g / (1 + e^-g)
+ * The context rows (target_hidden) enter only the attention, as in a layer
+ * step (they are already hidden_norm-ed upstream). Rounding: a, the
+ * attention output, h, m and the MLP activation are stored in the dtype; h is
+ * rounded after the add; out is rounded once after its add.
+ * ------------------------------------------------------------------------ */
+
+/* Limits: those of dflash_layer_create for `attn`, intermediate % 64 == 0. */
+typedef struct {
+    dflash_config attn;      /* the attention layer (its hidden is the block's)  */
+    int32_t intermediate;    /* I: the MLP width                                  */
+} dflash_decoder_config;
+
+/* Device weights in the dtype, borrowed; norms 16-byte aligned. */
+typedef struct {
+    dflash_weights attn;     /* as for dflash_layer_create                        */
+    const void* input_norm;  /* [H] input_layernorm gain                          */
+    const void* post_norm;   /* [H] post_attention_layernorm gain                 */
+    const void* w_gate_up;   /* [2I, H]: the gate_proj rows, then the up_proj rows */
+    const void* w_down;      /* [H, I] down_proj                                  */
+} dflash_decoder_weights;
+
+typedef struct dflash_decoder dflash_decoder; /* opaque: owns its attention layer */
+
+/* Create a decoder layer (and its attention layer handle). Errors as for
+ * dflash_layer_create, and DFLASH_ERR_SHAPE for intermediate. */
+int dflash_decoder_create(const dflash_decoder_config* cfg, const dflash_decoder_weights* weights,
+                          dflash_decoder** out);
+
+/* Release the decoder and its attention layer. NULL is a no-op. */
+void dflash_decoder_destroy(dflash_decoder* decoder);
+
+/* The decoder's attention layer (owned by the decoder, valid until it is
+ * destroyed), for dflash_layer_set_append_mode / _set_profiling /
+ * _kernel_times (the latter cover the attention kernels only). */
+dflash_layer* dflash_decoder_attention(dflash_decoder* decoder);
+
+/* Device workspace bytes of a decoder step for `batch` sequences with
+ * `total_ctx` new context rows in all; 0 on bad input. */
+size_t dflash_decoder_workspace_bytes(const dflash_decoder* decoder, int32_t batch, int64_t total_ctx);
+
+/* One decoder layer step. x and out: device [B * bs, H] (16-byte aligned; out
+ * must not overlap x); the other arguments, the cache effects and the errors
+ * are those of dflash_attn_step, whose checks all run before anything is
+ * enqueued. */
+int dflash_decoder_step(dflash_decoder* decoder, const void* x, const void* target_hidden,
+                        const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* RMSNorm of `rows` rows of `hidden` elements (the draft model's final norm):
+ * out = x / sqrt(mean(x^2) + eps) * gain, fp32 math, one rounding. Device
+ * pointers 16-byte aligned, hidden % 64 == 0. Errors: DFLASH_ERR_ARG,
+ * DFLASH_ERR_HIP. */
+int dflash_rms_norm(const void* x, const void* gain, void* out, int32_t rows, int32_t hidden, double eps,
+                    int32_t dtype, void* stream);
+
 /* Static description of a status code. */
 const char* dflash_status_string(int status);
 
