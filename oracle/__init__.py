@@ -18,4 +18,4 @@ from .ref_fp64 import (  # noqa: F401
     window_keep,
 )
 from .context_kv import context_kv_precompute  # noqa: F401
-from .decoder import decoder_layer_step, mlp, silu  # noqa: F401
+from .decoder import decoder_layer_step, draft_forward, mlp, silu  # noqa: F401

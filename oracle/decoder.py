@@ -52,3 +52,17 @@ def decoder_layer_step(cfg, weights, mlp_weights, cache: OracleCache, x, target_
     h = X + att
     m = rms_norm(h, mlp_weights.post_norm, cfg.rms_eps)
     return h + mlp(m, mlp_weights.w_gate_up, mlp_weights.w_down), new
+
+
+def draft_forward(cfg, layers, caches, x, target_hidden, ctx_offsets, positions, final_norm):
+    """The draft stack: the decoder layers in order, each with its own
+    attention weights, MLP weights and cache, the stream of one layer feeding
+    the next, then the final RMSNorm (vLLM page "qwen3_dflash",
+    DFlashQwen3Model.forward: the layers, then self.norm). ``layers`` is a list
+    of ``(weights, mlp_weights)``. Returns ``(out [B*bs, H], new caches)``."""
+    h = _f64(x)
+    new = []
+    for (w, mw), cache in zip(layers, caches):
+        h, c = decoder_layer_step(cfg, w, mw, cache, h, target_hidden, ctx_offsets, positions)
+        new.append(c)
+    return rms_norm(h, final_norm, cfg.rms_eps), new

@@ -117,3 +117,30 @@ def test_decoder_rejects_bad_steps_before_enqueueing():
     torch.cuda.synchronize()
     assert cache.lengths.tolist() == lens.tolist()
     assert torch.all(out == 7.0)
+
+
+def test_two_layer_draft_stack_with_final_norm():
+    """A two-layer draft stack (each layer its own weights and cache, the
+    stream of one feeding the next) and the final norm, against the oracle."""
+    from block_diffusion_draft_qkv_amd import rms_norm
+    cfg = small(batch=3, config_id=65)
+    cases = [make_case(cfg, seed=s) for s in (7, 8)]  # weights of two layers; inputs from the first
+    case = cases[0]
+    mws = [make_mlp_weights(c, 768) for c in cases]
+    decs = [make_decoder(c, mw) for c, mw in zip(cases, mws)]
+    caches = [make_cache(case), make_cache(case)]
+    fin = (1.0 + 0.02 * np.random.default_rng(9).standard_normal(cfg.hidden)).astype(np.float32)
+    from workload import round_bf16
+    fin = round_bf16(fin)
+    x, th, pos = step_inputs(case)
+    h = x
+    for dec, cache in zip(decs, caches):
+        h = dec.step(h, th, case.ctx_offsets, pos, cache)
+    out = rms_norm(h, dev(fin, torch.bfloat16), cfg.rms_eps)
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache.from_arrays(case.cache_k, case.cache_v)
+    ref, _ = oracle.draft_forward(cfg, [(c.weights, mw) for c, mw in zip(cases, mws)], [oc, oc.copy()],
+                                  case.hidden_states, case.target_hidden, case.ctx_offsets, case.positions, fin)
+    assert_close_stream(to64(out), ref, "bf16", "stack out")
+    for d in decs:
+        d.close()

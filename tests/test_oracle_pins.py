@@ -588,3 +588,21 @@ def test_decoder_layer_with_silent_branches_passes_the_stream_through():
     got, new = oracle.decoder_layer_step(cfg, w, mw, cache, X, C, offs, pos)
     np.testing.assert_array_equal(got, X)
     assert new.lengths == [1 + 2 + cfg.block_size, 3 + 1 + cfg.block_size]
+
+
+def test_draft_stack_is_layers_in_order_then_final_norm():
+    """Two layers feed each other in order (swapping them changes the result)
+    and the final RMSNorm is applied once at the end."""
+    cfg = tiny_cfg(batch=1)
+    rng = np.random.default_rng(23)
+    layers = [(rand_weights(cfg, rng), decoder_inputs(cfg, rng, inter=4)) for _ in range(2)]
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, [2], [1])
+    fin = rng.uniform(0.5, 1.5, cfg.hidden)
+    got, new = oracle.draft_forward(cfg, layers, [cache, cache.copy()], X, C, offs, pos, fin)
+    h1, c1 = oracle.decoder_layer_step(cfg, *layers[0], cache, X, C, offs, pos)
+    h2, c2 = oracle.decoder_layer_step(cfg, *layers[1], cache.copy(), h1, C, offs, pos)
+    ms = (h2 * h2).mean(axis=-1, keepdims=True)
+    np.testing.assert_allclose(got, h2 / np.sqrt(ms + cfg.rms_eps) * fin, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(new[1].k[0], c2.k[0])
+    swapped, _ = oracle.draft_forward(cfg, layers[::-1], [cache, cache.copy()], X, C, offs, pos, fin)
+    assert np.abs(swapped - got).max() > 1e-3
