@@ -22,8 +22,8 @@ import torch
 from . import _lib
 from ._lib import DFlashError, check  # noqa: F401
 
-__all__ = ["DFlashLayer", "KVCache", "LayerShape", "ContextKV", "ContextKVShape", "DFlashDecoder",
-           "rms_norm", "DFlashError", "KERNEL_NAMES"]
+__all__ = ["DFlashLayer", "KVCache", "PagedKVCache", "LayerShape", "ContextKV", "ContextKVShape",
+           "DFlashDecoder", "rms_norm", "run_round", "DFlashError", "KERNEL_NAMES"]
 KERNEL_NAMES = _lib.KERNEL_NAMES
 
 _DTYPES = {torch.float32: _lib.DFLASH_F32, torch.bfloat16: _lib.DFLASH_BF16}
@@ -362,4 +362,122 @@ def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float, out: Optional[torc
     st = _lib.lib().dflash_rms_norm(_ptr(x), _ptr(gain), _ptr(out), int(rows), int(h), float(eps), _DTYPES[x.dtype],
                                     _stream_handle(stream))
     check(st, "dflash_rms_norm")
+    return out
+
+
+class PagedKVCache:
+    """Draft KV cache of ``batch`` sequences in 64-row blocks (the paged layout
+    of include/dflash.h): pools ``k [num_blocks, n_kv, 64, d]`` and ``v
+    [num_blocks, n_kv, d, 64]``, a block table per sequence (``max_blocks``
+    entries; a device copy for the kernels and the host copy the library
+    checks) and a free list. Blocks are reserved before a step writes rows
+    and released when a crop drops them."""
+
+    BLOCK = 64
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, num_blocks: int, max_blocks: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        self.batch, self.n_kv_heads, self.head_dim = batch, n_kv_heads, head_dim
+        self.num_blocks, self.max_blocks, self.dtype = num_blocks, max_blocks, dtype
+        self.capacity = max_blocks * self.BLOCK
+        B = self.BLOCK
+        self.k = torch.empty((num_blocks, n_kv_heads, B, head_dim), dtype=dtype, device=device)
+        self.v = torch.empty((num_blocks, n_kv_heads, head_dim, B), dtype=dtype, device=device)
+        self._tab = (C.c_int32 * (batch * max_blocks))(*([-1] * (batch * max_blocks)))
+        self.table_host = np.ctypeslib.as_array(self._tab).reshape(batch, max_blocks)
+        self.table = torch.full((batch, max_blocks), -1, dtype=torch.int32, device=device)
+        self._len = (C.c_int32 * max(batch, 1))()
+        self.lengths = np.ctypeslib.as_array(self._len)[:batch]
+        self.free = list(range(num_blocks - 1, -1, -1))
+        self.desc = _lib.KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(), C.cast(self._len, C.POINTER(C.c_int32)),
+                                     batch, self.capacity, self.table.data_ptr(),
+                                     C.cast(self._tab, C.POINTER(C.c_int32)), max_blocks, num_blocks)
+        self._dirty = False
+
+    # ------------------------------------------------------------ blocks
+    def blocks_of(self, seq: int) -> int:
+        return int(np.count_nonzero(self.table_host[seq] >= 0))
+
+    def reserve(self, seq: int, rows: int) -> None:
+        """Back logical rows [0, rows) of ``seq`` with blocks."""
+        need = -(-int(rows) // self.BLOCK)
+        if need > self.max_blocks:
+            raise ValueError(f"sequence {seq} needs {need} blocks > max_blocks {self.max_blocks}")
+        for i in range(self.blocks_of(seq), need):
+            if not self.free:
+                raise MemoryError("no free cache block")
+            self.table_host[seq, i] = self.free.pop()
+            self._dirty = True
+
+    def release(self, seq: int, rows: int) -> None:
+        """Return the blocks of ``seq`` past logical row ``rows`` to the free list."""
+        keep = -(-int(rows) // self.BLOCK)
+        for i in range(self.blocks_of(seq) - 1, keep - 1, -1):
+            self.free.append(int(self.table_host[seq, i]))
+            self.table_host[seq, i] = -1
+            self._dirty = True
+
+    def sync(self) -> None:
+        """Copy the host table to the device table (stream-ordered before later steps)."""
+        if self._dirty:
+            self.table.copy_(torch.from_numpy(self.table_host.copy()))
+            self._dirty = False
+
+    # ------------------------------------------------------------ rows
+    def _slots(self, seq: int, r0: int, r1: int):
+        rows = np.arange(r0, r1)
+        return self.table_host[seq, rows // self.BLOCK], rows % self.BLOCK
+
+    def write_prefix(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Place rows [0, L) of ``seq`` (``k``, ``v``: ``[n_kv, L, d]``) and set its length to L."""
+        L = int(k.shape[1])
+        self.reserve(seq, L)
+        self.sync()
+        blk, off = self._slots(seq, 0, L)
+        bi = torch.from_numpy(blk.astype(np.int64)).to(self.k.device)
+        oi = torch.from_numpy(off.astype(np.int64)).to(self.k.device)
+        self.k[bi, :, oi, :] = k.transpose(0, 1).to(self.dtype)
+        self.v.permute(0, 3, 1, 2)[bi, oi] = v.transpose(0, 1).to(self.dtype)
+        self.lengths[seq] = L
+
+    def read(self, seq: int):
+        """Valid rows of ``seq`` gathered as ``(k, v)``, each ``[n_kv, len, d]``."""
+        L = int(self.lengths[seq])
+        blk, off = self._slots(seq, 0, L)
+        bi = torch.from_numpy(blk.astype(np.int64)).to(self.k.device)
+        oi = torch.from_numpy(off.astype(np.int64)).to(self.k.device)
+        k = self.k[bi, :, oi, :].transpose(0, 1)
+        v = self.v.permute(0, 3, 1, 2)[bi, oi].transpose(0, 1)
+        return k, v
+
+    def set_lengths(self, lengths: Sequence[int]) -> None:
+        self.lengths[:] = np.asarray(lengths, dtype=np.int32)
+
+    def crop(self, seq: int, new_len: int) -> None:
+        """Rewind ``seq`` to ``new_len`` rows and release the blocks past them."""
+        check(_lib.lib().dflash_cache_crop(C.byref(self.desc), int(seq), int(new_len)), "dflash_cache_crop")
+        self.release(seq, new_len)
+
+
+def run_round(model, cache, hidden_states: torch.Tensor, target_hidden: Optional[torch.Tensor], ctx_offsets,
+              accept: Sequence[int], out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One draft round on a paged (or contiguous) cache: reserve the blocks the
+    step appends to, run the layer (or decoder) step with positions len_b ..
+    len_b + n_b + bs - 1, then crop each sequence to its accepted prefix
+    len_b + n_b + accept[b] (releasing the blocks a crop drops)."""
+    B, bs = cache.batch, model.shape.block_size
+    L = cache.lengths.astype(np.int64).copy()
+    n = np.diff(np.asarray(ctx_offsets, dtype=np.int64))
+    if isinstance(cache, PagedKVCache):
+        for b in range(B):
+            cache.reserve(b, int(L[b] + n[b] + bs))
+        cache.sync()
+    pos = np.concatenate([np.arange(L[b], L[b] + n[b] + bs) for b in range(B)]).astype(np.int32)
+    pos_d = torch.from_numpy(pos).to(hidden_states.device)
+    out = model.step(hidden_states, target_hidden, ctx_offsets, pos_d, cache, out=out, stream=stream)
+    for b in range(B):
+        a = int(accept[b])
+        if not 0 <= a <= bs:
+            raise ValueError("accepted count outside [0, block_size]")
+        cache.crop(b, int(L[b] + n[b] + a))
     return out

@@ -53,7 +53,9 @@ class Weights(C.Structure):
 
 class KVCacheDesc(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("len", C.POINTER(C.c_int32)),
-                ("batch", C.c_int32), ("capacity", C.c_int32)]
+                ("batch", C.c_int32), ("capacity", C.c_int32),
+                ("block_table", C.c_void_p), ("block_table_host", C.POINTER(C.c_int32)),
+                ("max_blocks", C.c_int32), ("num_blocks", C.c_int32)]
 
 
 class CtxKVConfig(C.Structure):

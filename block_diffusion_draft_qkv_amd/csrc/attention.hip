@@ -230,11 +230,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
     if (++c.tile == c.hi) {
       if (++c.j == nkv) {
         c.j = 0;
-        ++c.b;
-        int lo, cnt;
-        seq_tiles(a, c.b, KT, lo, cnt);
-        c.lo = lo;
-        c.hi = lo + cnt;
+        if (++c.b < a.seq.batch) {  // past the last pair the cursor is never used
+          int lo, cnt;
+          seq_tiles(a, c.b, KT, lo, cnt);
+          c.lo = lo;
+          c.hi = lo + cnt;
+        }
       }
       c.tile = c.lo;
     }
@@ -259,11 +260,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
       const int c = (lane % CPR) ^ kswz<T, CPR>(row);
       kdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
     }
+    const int vstride = a.map.vstride();  // elements between V^T rows (cap, or 64 in a paged pool)
 #pragma unroll
     for (int i = 0; i < KPP; ++i) {
       const int blk = i * kProducerWaves + pw, row = blk * (64 / VCPR) + lane / VCPR;
       const int c = (lane % VCPR) ^ rswz<VCPR>(row);
-      vdma[i] = (uint32_t)(row * a.cap + c * E) * (uint32_t)sizeof(T);
+      vdma[i] = (uint32_t)(row * vstride + c * E) * (uint32_t)sizeof(T);
     }
 #pragma unroll
     for (int i = 0; i < QPP; ++i) {
@@ -271,6 +273,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
       const int c = (lane % CPR) ^ rswz<CPR>(row);
       qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
     }
+    // A paged cache's physical block of the cursor's tile is loaded one step
+    // ahead (right after the cursor moves), so the lookup's latency overlaps
+    // the wait for the previous step instead of delaying the next issue.
+    const bool paged = a.map.bt != nullptr;
+    int phys = 0;
+    auto lookup = [&]() {
+      if (paged && cur.b < a.seq.batch)
+        phys = __builtin_amdgcn_readfirstlane(a.map.phys(cur.b, cur.tile * KT));
+    };
+    lookup();
     // Issue step n (its tile is at the cursor; the Q tile too if a segment
     // starts there) and return the number of DMA blocks this wave issued.
     int iseg = 0;
@@ -287,8 +299,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
         blocks += QPP;
       }
       const uint32_t sl = lds0 + (uint32_t)(n % S) * TILE;
-      const void* kt = uniform_ptr(Kc + (pair * a.cap + (size_t)cur.tile * KT) * D * sizeof(T));
-      const void* vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)cur.tile * KT) * sizeof(T));
+      const void* kt;
+      const void* vt;
+      if (!paged) {
+        kt = uniform_ptr(Kc + (pair * a.cap + (size_t)cur.tile * KT) * D * sizeof(T));
+        vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)cur.tile * KT) * sizeof(T));
+      } else {
+        const size_t blk = (size_t)phys * nkv + cur.j, off = (size_t)(cur.tile * KT) % kKeyTile;
+        kt = uniform_ptr(Kc + (blk * kKeyTile + off) * D * sizeof(T));
+        vt = uniform_ptr(Vc + (blk * D * kKeyTile + off) * sizeof(T));
+      }
 #pragma unroll
       for (int i = 0; i < KPP; ++i)
         lds_dma16<true>(kdma[i], kt, sl + (uint32_t)(i * kProducerWaves + pw) * 1024u);
@@ -296,6 +316,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
       for (int i = 0; i < KPP; ++i)
         lds_dma16<true>(vdma[i], vt, sl + K_BYTES + (uint32_t)(i * kProducerWaves + pw) * 1024u);
       advance(cur);
+      lookup();
       return blocks;
     };
     // Steps 0 .. S-2 go out before the first barrier; `pending` is the number

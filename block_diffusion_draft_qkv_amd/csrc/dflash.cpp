@@ -193,6 +193,33 @@ bool upload_rope_table(int max_pos, int d, double theta, float** out) {
   return hipMemcpy(*out, table.data(), 2 * n * sizeof(float), hipMemcpyHostToDevice) == hipSuccess;
 }
 
+// Host checks of a cache's layout; rows_needed[b] rows of sequence b are
+// touched. For a paged cache every block holding such a row must name a
+// physical block in the pools (per the host mirror of the table).
+int check_layout(const dflash_kv_cache* c, const int64_t* rows_needed) {
+  if (!c->block_table) return DFLASH_OK;
+  if (!c->block_table_host || c->max_blocks <= 0 || c->num_blocks <= 0) return DFLASH_ERR_ARG;
+  if ((int64_t)c->max_blocks * kKeyTile != c->capacity) return DFLASH_ERR_SHAPE;
+  for (int b = 0; b < c->batch; ++b) {
+    const int64_t nb = (rows_needed[b] + kKeyTile - 1) / kKeyTile;
+    for (int64_t i = 0; i < nb; ++i) {
+      const int32_t p = c->block_table_host[(int64_t)b * c->max_blocks + i];
+      if (p < 0 || p >= c->num_blocks) return DFLASH_ERR_RANGE;
+    }
+  }
+  return DFLASH_OK;
+}
+
+CacheMap cache_map(const dflash_kv_cache* c, int nkv) {
+  CacheMap m;
+  m.bt = c->block_table;
+  m.bt_stride = c->block_table ? c->max_blocks : 0;
+  m.num_blocks = c->block_table ? c->num_blocks : 0;
+  m.cap = c->capacity;
+  m.nkv = nkv;
+  return m;
+}
+
 hipEvent_t pooled_event(dflash_layer* L) {
   if (!L->event_pool.empty()) {
     hipEvent_t e = L->event_pool.back();
@@ -321,6 +348,12 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   seq.ctx_off[B] = ctx_offsets[B];
   const int64_t Mc = ctx_offsets[B];
   if (Mc > 0 && !target_hidden) return DFLASH_ERR_ARG;
+  {
+    int64_t rows[kMaxBatch];
+    for (int b = 0; b < B; ++b) rows[b] = (int64_t)cache->len[b] + (ctx_offsets[b + 1] - ctx_offsets[b]) + bs;
+    const int lst = check_layout(cache, rows);
+    if (lst != DFLASH_OK) return lst;
+  }
   if (!workspace) return DFLASH_ERR_WORKSPACE;
   const Carve wc = carve(L, B, Mc);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
@@ -379,6 +412,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   na.qscale = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   na.ctx_ld = (int64_t)Nkv;
   na.ctx_layer_off = 0;
+  na.map = cache_map(cache, nkv);
   na.seq = seq;
   hipEvent_t ev;
   record(L, &ev, s);
@@ -409,6 +443,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   aa.window = c.sliding_window >= cache->capacity ? 0 : c.sliding_window;
   aa.total_tiles = n_tiles;
   aa.G = (int32_t)attn_groups(L, n_tiles);
+  aa.map = cache_map(cache, nkv);
   aa.seq = seq;
   // Each work-group's first (pair, tile): walk the pairs in flat order.
   {
@@ -595,6 +630,10 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   if (c0->capacity <= 0 || c0->capacity % kKeyTile || c0->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
   for (int l = 1; l < nl; ++l) {
     if (caches[l]->batch != B || caches[l]->capacity != c0->capacity) return DFLASH_ERR_SHAPE;
+    // one layout for every layer (a paged stack shares its block table)
+    if (caches[l]->block_table != c0->block_table || caches[l]->num_blocks != c0->num_blocks ||
+        caches[l]->max_blocks != c0->max_blocks)
+      return DFLASH_ERR_SHAPE;
     for (int b = 0; b < B; ++b)
       if (caches[l]->len[b] != c0->len[b]) return DFLASH_ERR_SHAPE;
   }
@@ -613,6 +652,12 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   }
   seq.ctx_off[B] = ctx_offsets[B];
   const int64_t Mc = ctx_offsets[B];
+  {
+    int64_t rows[kMaxBatch];
+    for (int b = 0; b < B; ++b) rows[b] = (int64_t)c0->len[b] + (ctx_offsets[b + 1] - ctx_offsets[b]);
+    const int lst = check_layout(c0, rows);
+    if (lst != DFLASH_OK) return lst;
+  }
   if (Mc == 0) return DFLASH_OK;
   if (!context_states || !positions || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
   if (!workspace) return DFLASH_ERR_WORKSPACE;
@@ -656,6 +701,7 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   na.qscale = 1.0f;
   na.ctx_ld = N;
   na.ctx_layer_off = (int64_t)2 * nkv * d;
+  na.map = cache_map(c0, nkv);
   na.seq = seq;
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));

@@ -370,6 +370,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
   // before the main loop (nothing waits for them until the epilogue).
   constexpr int MH = MI / 2;
   int sb[MI], win[MI], crow[MI], pos[MH];  // sequence, window row, cache row; positions
+  int blk[MI];                             // physical block of the row (paged cache)
   bool ok[MI];
   if (wave < kGemmConsumers) {
     // The sequences a wave's rows touch are few and found with wave-uniform
@@ -424,6 +425,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
         pos[u] = a.positions[pi];
       }
     }
+    // A paged cache's physical block of each row, loaded with the positions.
+    if (a.map.bt != nullptr) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) blk[mi] = ok[mi] ? a.map.phys(sb[mi], crow[mi]) : 0;
+    }
   }
 
   f32x4 acc[NI][MI];
@@ -438,16 +444,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
     // Values: raw, transposed into cache V (key index contiguous); each wave
     // writes its own half of the columns for all its rows.
     T* vbase = vc;
+    const size_t vs = (size_t)a.map.vstride();
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!ok[mi]) continue;
       const int b = sb[mi];
-      const size_t col0 = ((size_t)(b * nkv + j) * D + wn * HALF) * a.cap + crow[mi];
+      const size_t col = a.map.bt == nullptr
+                             ? (size_t)(b * nkv + j) * D * a.cap + crow[mi]
+                             : ((size_t)blk[mi] * nkv + j) * D * kKeyTile + crow[mi] % kKeyTile;
+      const size_t col0 = col + (size_t)(wn * HALF) * vs;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          vbase[col0 + (size_t)(ni * 16 + 4 * q + r) * a.cap] = Elem<T>::from_f32(acc[ni][mi][r]);
+          vbase[col0 + (size_t)(ni * 16 + 4 * q + r) * vs] = Elem<T>::from_f32(acc[ni][mi][r]);
     }
     return;
   }
@@ -523,7 +533,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
         const int i = (J.m0 + wm * WM + mi * 16 + r16) % bs;
         dst = static_cast<T*>(a.qpack) + ((size_t)(b * nkv + j) * R + i * g + hh) * D;
       } else {
-        dst = kc + ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D;
+        dst = kc + (a.map.bt == nullptr
+                        ? ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D
+                        : (((size_t)blk[mi] * nkv + j) * kKeyTile + crow[mi] % kKeyTile) * D);
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {

@@ -39,6 +39,34 @@ struct GemmArgs {
 hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles, int bm, int bn,
                        int kslices, hipStream_t stream);
 
+// ------------------------------------------------------------- cache layout
+// Where cache row `row` of sequence b, KV head j lives. Contiguous: K
+// [B][nkv][cap][d], V transposed [B][nkv][d][cap]. Paged (bt != nullptr):
+// 64-row blocks; logical block i of sequence b is physical block
+// bt[b * bt_stride + i] of the pools K [blocks][nkv][64][d] and V
+// [blocks][nkv][d][64]. Table entries are clamped into [0, num_blocks) (the
+// host checks its mirror of the table; the clamp keeps a stale device table
+// inside the pools).
+struct CacheMap {
+  const int32_t* bt;
+  int32_t bt_stride, num_blocks, cap, nkv;
+  __device__ inline int phys(int b, int row) const {
+    const int p = bt[(size_t)b * bt_stride + row / kKeyTile];
+    return p < 0 ? 0 : (p >= num_blocks ? num_blocks - 1 : p);
+  }
+  // element offset of K row `row`
+  __device__ inline size_t k_row(int b, int j, int row, int d) const {
+    if (!bt) return ((size_t)(b * nkv + j) * cap + row) * d;
+    return (((size_t)phys(b, row) * nkv + j) * kKeyTile + row % kKeyTile) * d;
+  }
+  // element offset of V^T (dim 0, row `row`); dim dd adds dd * vstride()
+  __device__ inline size_t v_col(int b, int j, int row, int d) const {
+    if (!bt) return (size_t)(b * nkv + j) * d * cap + row;
+    return ((size_t)phys(b, row) * nkv + j) * d * kKeyTile + row % kKeyTile;
+  }
+  __device__ inline int vstride() const { return bt ? kKeyTile : cap; }
+};
+
 // ------------------------------------------------- norm + RoPE + append + Q
 struct NormRopeArgs {
   const float* qkv;        // [kslices][B*bs][(nq + 2 nkv) d] block projections (fp32)
@@ -62,6 +90,7 @@ struct NormRopeArgs {
   int64_t ctx_layer_off;
   void* layer_kc[kMaxLayers];
   void* layer_vc[kMaxLayers];
+  CacheMap map;            // cache layout (the same for every layer)
   SeqTable seq;
 };
 // grid: B * n_kv (one column of work-groups per sequence and KV head) times
@@ -101,6 +130,7 @@ struct AttnArgs {
   float* part_ml;          // [2G][64][2] running max (log2 domain) and sum
   int32_t nq, nkv, bs, R, cap, window, G;
   int64_t total_tiles;
+  CacheMap map;            // cache layout
   SeqTable seq;
   // Start of work-group w's range: pair b * nkv + j in bits 0..15, absolute key
   // tile in bits 16..31 (filled by the host, which knows every length).

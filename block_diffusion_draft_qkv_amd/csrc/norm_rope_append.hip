@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       cs[s] = cos_t[(size_t)p[s] * HALF + t];
       sn[s] = sin_t[(size_t)p[s] * HALF + t];
     }
-    T* kdst = static_cast<T*>(z == 0 ? a.kc : a.layer_kc[z]) + (pair * a.cap + L) * D;
+    T* kbase = static_cast<T*>(z == 0 ? a.kc : a.layer_kc[z]);
     T* qdst = static_cast<T*>(a.qpack) + pair * R * D;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       const float o1 = y1 * cs[s] - y2 * sn[s];
       const float o2 = y2 * cs[s] + y1 * sn[s];
       const int r = base + s * RPW;
-      T* dst = key ? kdst + (size_t)r * D : qdst + (size_t)(r - nnew) * D;
+      T* dst = key ? kbase + a.map.k_row(b, j, L + r, D) : qdst + (size_t)(r - nnew) * D;
       if (kind[s] != 0) {
         dst[t] = Elem<T>::from_f32(o1);
         dst[t + HALF] = Elem<T>::from_f32(o2);
@@ -202,11 +202,15 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       vt[t + HALF][rb] = Elem<T>::from_f32(v2[k]);
     }
   }
+  // Where each row's column starts (a paged cache maps rows to blocks).
+  __shared__ size_t vcol[VT];
+  if (tid < nr) vcol[tid] = a.map.v_col(b, j, L + r0 + tid, D);
   __syncthreads();
-  T* vdst = static_cast<T*>(z == 0 ? a.vc : a.layer_vc[z]) + pair * D * a.cap + L;
+  T* vbase = static_cast<T*>(z == 0 ? a.vc : a.layer_vc[z]);
+  const size_t vs = (size_t)a.map.vstride();
   for (int idx = tid; idx < D * nr; idx += 256) {
     const int dd = idx / nr, rr = idx % nr;
-    vdst[(size_t)dd * a.cap + r0 + rr] = vt[dd][rr];
+    vbase[vcol[rr] + (size_t)dd * vs] = vt[dd][rr];
   }
 }
 

@@ -100,13 +100,30 @@ typedef struct {
  *        authoritative length (kernels receive it by value).
  * K holds post-norm, post-RoPE keys; V holds raw values. Rows at or past len
  * are dead: they never contribute to a result.
- * capacity must be a positive multiple of 64, at most 2^21 rows. */
+ * capacity must be a positive multiple of 64, at most 2^21 rows.
+ *
+ * Paged layout (block_table != NULL; the serving cache of the vLLM page
+ * "qwen3_dflash", whose cache update writes each row to the slot its
+ * slot_mapping names): rows come in blocks of 64; logical block i of sequence
+ * b (rows 64 i .. 64 i + 63) is physical block block_table[b * max_blocks + i]
+ * of the pools
+ *   k: [num_blocks][n_kv][64][head_dim]
+ *   v: [num_blocks][n_kv][head_dim][64]    (transposed within the block)
+ * and capacity must equal 64 * max_blocks. block_table (device) is what the
+ * kernels read; block_table_host is its host mirror, which the library checks
+ * (every block a step touches must name a physical block in [0, num_blocks))
+ * and the caller keeps equal to the device table. Sequences must not share a
+ * block that a step writes. The kernels clamp entries into [0, num_blocks). */
 typedef struct {
     void* k;
     void* v;
     int32_t* len;
     int32_t batch;
     int32_t capacity;
+    const int32_t* block_table;       /* device [batch][max_blocks], or NULL     */
+    const int32_t* block_table_host;  /* host mirror (required when paged)       */
+    int32_t max_blocks;               /* table row length                         */
+    int32_t num_blocks;               /* blocks in each pool                      */
 } dflash_kv_cache;
 
 typedef struct dflash_layer dflash_layer; /* opaque */
