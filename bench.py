@@ -56,6 +56,8 @@ def parse():
                     help="timed runs of the multi-layer context K/V precompute (0: skip)")
     ap.add_argument("--decoder-steps", type=int, default=30,
                     help="timed steps of the whole draft decoder layer at C3 (0: skip)")
+    ap.add_argument("--paged-steps", type=int, default=50,
+                    help="timed C3 steps on the paged cache, and as many driver rounds (0: skip)")
     ap.add_argument("--decoder-only", action="store_true",
                     help="only time the draft decoder layer (for profiling)")
     ap.add_argument("--context-kv-only", default=None, choices=("P3", "P4"),
@@ -279,6 +281,102 @@ def bench_decoder(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     return res
 
 
+def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
+    """The C3 layer step on the paged cache (64-row blocks handed out in a
+    shuffled order): `steps` steps with lengths rewound on the host, HIP
+    events on the launch stream, then the attention kernel's mean from a
+    profiled pass; and `steps` rounds of the draft-round driver (reserve the
+    appended blocks, copy the table, step, crop to the accepted prefix and
+    release the dropped blocks), host work included."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import DFlashLayer, LayerShape, PagedKVCache, run_round
+    from workload import make_case
+
+    case = make_case("C3", seed=seed)
+    cfg = case.cfg
+    dt = torch.bfloat16
+    B, bs, H = case.batch, cfg.block_size, cfg.hidden
+
+    def dev(x, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+    w = case.weights
+    layer = DFlashLayer(LayerShape(H, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, bs, dt, cfg.rope_theta,
+                                   cfg.rms_eps, cfg.sliding_window, cfg.max_position),
+                        dev(w.w_qkv), dev(w.w_o), dev(w.q_norm), dev(w.k_norm))
+    need = [-(-int(t) // 64) for t in case.total_len]
+    caches = []
+    for i in range(copies):
+        c = PagedKVCache(B, cfg.n_kv_heads, cfg.head_dim, sum(need) + 4 * B, max(need) + 4, dt)
+        np.random.default_rng(seed + i).shuffle(c.free)
+        for b in range(B):
+            c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
+            c.reserve(b, int(case.total_len[b]))
+        c.sync()
+        caches.append(c)
+    hs, th, pos = dev(case.hidden_states), dev(case.target_hidden), dev(case.positions, torch.int32)
+    offs = [int(o) for o in case.ctx_offsets]
+    out = torch.empty((B * bs, H), dtype=dt, device="cuda")
+    ws = layer.workspace(B, offs[-1])
+    L0 = case.cached_len.copy()
+
+    def one(i):
+        c = caches[i % copies]
+        layer.step(hs, th, offs, pos, c, out=out, workspace=ws)
+        c.set_lengths(L0)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(warmup + i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    layer.set_profiling(True)
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    ms, n = layer.kernel_times()["attn"]
+    layer.set_profiling(False)
+    attn_us = ms * 1e3 / n
+    T = case.total_len.astype(np.int64)
+    attn_bytes = int(T.sum()) * cfg.n_kv_heads * cfg.head_dim * 2 * 2 + 2 * B * bs * cfg.n_q_heads * cfg.head_dim * 2
+
+    # Driver rounds with simulated accepted counts; after each round the
+    # sequences are cropped back to their starting lengths (a rewind, host
+    # work included), so every round has C3's lengths and reserves its blocks
+    # anew.
+    c = caches[0]
+    for b in range(B):
+        c.crop(b, int(L0[b]))
+    rng = np.random.default_rng(seed + 7)
+    accepts = rng.integers(0, bs + 1, size=(steps, B))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(steps):
+        run_round(layer, c, hs, th, offs, accepts[r], out=out)
+        for b in range(B):
+            c.crop(b, int(L0[b]))
+    torch.cuda.synchronize()
+    t_round = (time.perf_counter() - t0) / steps
+    res = {
+        "workload": f"C3 layer step on a paged cache (64-row blocks, shuffled), B={B}, block {bs}",
+        "ms_per_step": round(t_step * 1e3, 4),
+        "tokens_per_s": round(B * bs / t_step, 1),
+        "attn_mean_us": round(attn_us, 2),
+        "attn_hbm_frac": round(attn_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "driver_round_ms": round(t_round * 1e3, 4),
+        "driver_tokens_per_s": round(B * bs / t_round, 1),
+    }
+    layer.close()
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -441,6 +539,8 @@ def main():
         line["context_kv_precompute"] = bench_context_kv(a.ctxkv_steps, 5)
     if a.decoder_steps > 0:
         line["decoder_layer"] = bench_decoder(a.decoder_steps, 5)
+    if a.paged_steps > 0:
+        line["paged"] = bench_paged(a.paged_steps, 10)
     print(json.dumps(line), flush=True)
 
 
