@@ -275,12 +275,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
     }
     // A paged cache's physical block of the cursor's tile is loaded one step
     // ahead (right after the cursor moves), so the lookup's latency overlaps
-    // the wait for the previous step instead of delaying the next issue.
+    // the wait for the previous step instead of delaying the next issue. It
+    // is a scalar load: a vector one would make the compiler wait for the
+    // whole vector-memory counter, i.e. for every DMA block still in flight.
     const bool paged = a.map.bt != nullptr;
     int phys = 0;
     auto lookup = [&]() {
-      if (paged && cur.b < a.seq.batch)
-        phys = __builtin_amdgcn_readfirstlane(a.map.phys(cur.b, cur.tile * KT));
+      if (paged && cur.b < a.seq.batch) phys = a.map.entry_uniform(cur.b, cur.tile * KT);
     };
     lookup();
     // Issue step n (its tile is at the cursor; the Q tile too if a segment
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
         kt = uniform_ptr(Kc + (pair * a.cap + (size_t)cur.tile * KT) * D * sizeof(T));
         vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)cur.tile * KT) * sizeof(T));
       } else {
-        const size_t blk = (size_t)phys * nkv + cur.j, off = (size_t)(cur.tile * KT) % kKeyTile;
+        const size_t blk = (size_t)a.map.clamp_block(phys) * nkv + cur.j, off = (size_t)(cur.tile * KT) % kKeyTile;
         kt = uniform_ptr(Kc + (blk * kKeyTile + off) * D * sizeof(T));
         vt = uniform_ptr(Vc + (blk * D * kKeyTile + off) * sizeof(T));
       }

@@ -50,9 +50,20 @@ hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_
 struct CacheMap {
   const int32_t* bt;
   int32_t bt_stride, num_blocks, cap, nkv;
-  __device__ inline int phys(int b, int row) const {
-    const int p = bt[(size_t)b * bt_stride + row / kKeyTile];
+  __device__ inline int clamp_block(int p) const {
     return p < 0 ? 0 : (p >= num_blocks ? num_blocks - 1 : p);
+  }
+  __device__ inline int phys(int b, int row) const {
+    return clamp_block(bt[(size_t)b * bt_stride + row / kKeyTile]);
+  }
+  // The raw table entry for wave-uniform b and row, read through the
+  // constant address space: the table does not change while a kernel runs,
+  // so the load is a scalar one and its wait (lgkmcnt) leaves the
+  // vector-memory counter, which LDS-DMA streams pace themselves by, alone.
+  // Clamp it with clamp_block where it is used, so the wait lands there.
+  __device__ inline int entry_uniform(int b, int row) const {
+    using ctab = const __attribute__((address_space(4))) int32_t;
+    return ((ctab*)bt)[(size_t)b * bt_stride + row / kKeyTile];
   }
   // element offset of K row `row`
   __device__ inline size_t k_row(int b, int j, int row, int d) const {
