@@ -1,5 +1,6 @@
 """Float64 CPU oracle of the DFlash draft-attention layer step, of the
-multi-layer context K/V precompute and of the draft decoder layer.
+multi-layer context K/V precompute (bf16 and MXFP8) and of the draft decoder
+layer.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -19,3 +20,13 @@ from .ref_fp64 import (  # noqa: F401
 )
 from .context_kv import context_kv_precompute  # noqa: F401
 from .decoder import decoder_layer_step, draft_forward, mlp, silu  # noqa: F401
+from .mxfp8 import (  # noqa: F401
+    context_kv_precompute_mxfp8,
+    e4m3_encode,
+    e4m3_value,
+    e8m0_value,
+    mx_dequantize,
+    mx_quantize,
+    mxfp8_linear,
+    round_bf16,
+)

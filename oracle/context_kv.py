@@ -44,24 +44,31 @@ def context_kv_precompute(cfg, weights, caches: Sequence[OracleCache], context_s
     ``context_states [sum n_b, H]`` packs each sequence's raw context rows,
     sequence b owning rows ``ctx_offsets[b] : ctx_offsets[b+1]``, whose
     positions are ``positions`` at the same rows. Returns the L new caches."""
-    H, Ln, nkv, d = cfg.hidden, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    H, Ln = cfg.hidden, cfg.n_layers
     if len(caches) != Ln:
         raise ValueError("one cache per layer")
     C = _f64(context_states).reshape(-1, H)
+    normed = rms_norm(C, weights.hidden_norm, cfg.rms_eps)
+    return [append_layer_kv(cfg, caches[layer], linear(normed, _f64(weights.w_kv[layer])),
+                            weights.k_norm[layer], ctx_offsets, positions)
+            for layer in range(Ln)]
+
+
+def append_layer_kv(cfg, cache: OracleCache, kv, k_norm, ctx_offsets, positions) -> OracleCache:
+    """One layer's part after the projection: ``kv [sum n_b, 2*nkv*d]`` holds
+    that layer's K heads then V heads per context row. K is RMS-normalised with
+    the layer's ``k_norm`` gain and rotated at the row positions; V stays raw;
+    both are appended after each sequence's valid rows of a copy of ``cache``."""
+    nkv, d = cfg.n_kv_heads, cfg.head_dim
     offs = [int(o) for o in ctx_offsets]
     pos = np.asarray(positions, dtype=np.int64)
-    normed = rms_norm(C, weights.hidden_norm, cfg.rms_eps)
-    out = []
-    for layer in range(Ln):
-        kv = linear(normed, _f64(weights.w_kv[layer]))      # [rows, 2*nkv*d]
-        new = caches[layer].copy()
-        for b in range(len(offs) - 1):
-            rows = kv[offs[b]:offs[b + 1]]
-            k = rows[:, :nkv * d].reshape(-1, nkv, d).transpose(1, 0, 2)
-            v = rows[:, nkv * d:].reshape(-1, nkv, d).transpose(1, 0, 2)
-            k = rms_norm(k, _f64(weights.k_norm[layer]), cfg.rms_eps)
-            k = rope(k, pos[offs[b]:offs[b + 1]], cfg.rope_theta)
-            new.k[b] = np.concatenate([new.k[b], k], axis=1)
-            new.v[b] = np.concatenate([new.v[b], v], axis=1)
-        out.append(new)
-    return out
+    new = cache.copy()
+    for b in range(len(offs) - 1):
+        rows = kv[offs[b]:offs[b + 1]]
+        k = rows[:, :nkv * d].reshape(-1, nkv, d).transpose(1, 0, 2)
+        v = rows[:, nkv * d:].reshape(-1, nkv, d).transpose(1, 0, 2)
+        k = rms_norm(k, _f64(k_norm), cfg.rms_eps)
+        k = rope(k, pos[offs[b]:offs[b + 1]], cfg.rope_theta)
+        new.k[b] = np.concatenate([new.k[b], k], axis=1)
+        new.v[b] = np.concatenate([new.v[b], v], axis=1)
+    return new

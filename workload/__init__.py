@@ -17,6 +17,8 @@ from .ctxkv import (  # noqa: F401
     CtxKVCase,
     CtxKVConfig,
     CtxKVWeights,
+    MXKVWeights,
     make_ctxkv_case,
+    make_mxfp8_kv_weights,
 )
 from .decoder import QWEN3_8B_INTERMEDIATE, MLPWeights, make_mlp_weights  # noqa: F401

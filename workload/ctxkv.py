@@ -9,6 +9,16 @@ target layers, and a draft has one layer per extracted target layer).
 * P3 decode round: C3's batch, B=32 sequences with cached rows U{512..8192}
   and U{1..16} new context rows each (about 272 rows), 3 layers.
 * P4 prefill: one 4096-row prompt into an empty cache, 3 layers.
+* M1, M2: small bf16 cases for the MXFP8 projection (hidden 256 and 512, a
+  multiple of 128): M1 2 layers, 2 KV heads, head_dim 64, rows U{1..30}; M2 3
+  layers, 4 KV heads, head_dim 128, cached rows U{0..200}, new rows U{1..100}.
+
+MXFP8 K/V weights (``make_mxfp8_kv_weights``) are drawn directly as bytes, not
+quantised from anything: E4M3 fields sign ~ U{0,1}, exponent ~ the integer
+nearest N(10, 1.2²) clipped to 1..15, mantissa ~ U{0..7} (6 at most where the
+exponent is 15, which keeps clear of the NaN code), so element values sit
+around 8..15; E8M0 scale bytes ~ U{116, 117}, i.e. 2^-11 or 2^-10, which
+puts the weights near the bf16 recipe's N(0, 0.02²) (RMS about 0.018).
 
 Recipe: K/V projection weights N(0, 0.02²); RMSNorm gains (hidden_norm and
 every layer's k_norm) 1 + 0.02·N(0, 1); raw context states 4·N(0, 1) (the
@@ -52,6 +62,8 @@ CTXKV_CONFIGS = {
     "P1": CtxKVConfig("P1", 2, 256, 2, 2, 64, "fp32", (0, 40), (1, 30), config_id=41),
     "P3": CtxKVConfig("P3", 32, 4096, 3, 8, 128, "bf16", (512, 8192), (1, 16), config_id=43),
     "P4": CtxKVConfig("P4", 1, 4096, 3, 8, 128, "bf16", 0, 4096, config_id=44),
+    "M1": CtxKVConfig("M1", 2, 256, 2, 2, 64, "bf16", (0, 40), (1, 30), config_id=45),
+    "M2": CtxKVConfig("M2", 3, 512, 3, 4, 128, "bf16", (0, 200), (1, 100), config_id=46),
 }
 
 
@@ -60,6 +72,12 @@ class CtxKVWeights:
     hidden_norm: np.ndarray  # [H]
     w_kv: np.ndarray         # [L, 2*nkv*d, H]: layer l's K rows, then its V rows
     k_norm: np.ndarray       # [L, d]
+
+
+@dataclass
+class MXKVWeights:
+    w_kv_codes: np.ndarray   # [L, 2*nkv*d, H] uint8 E4M3 codes (rows as CtxKVWeights.w_kv)
+    w_kv_scales: np.ndarray  # [L, 2*nkv*d, H/32] uint8 E8M0 bytes, one per 32 consecutive k
 
 
 @dataclass
@@ -115,3 +133,21 @@ def make_ctxkv_case(cfg: Union[str, CtxKVConfig], seed: int = 0) -> CtxKVCase:
           for _ in range(Ln)]
     return CtxKVCase(cfg, seed, CtxKVWeights(hidden_norm, w_kv, k_norm), ctx, offs, pos,
                      L.astype(np.int32), ck, cv)
+
+
+def make_mxfp8_kv_weights(cfg: Union[str, CtxKVConfig], seed: int = 0) -> MXKVWeights:
+    """Seeded MXFP8 K/V weights of ``cfg``'s shape, drawn as bytes (recipe above)."""
+    if isinstance(cfg, str):
+        cfg = CTXKV_CONFIGS[cfg]
+    H, Ln, nkv, d = cfg.hidden, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32")
+    r = _rng(cfg, seed, 5)
+    shape = (Ln, 2 * nkv * d, H)
+    sign = r.integers(0, 2, shape, dtype=np.int64)
+    expo = np.clip(np.rint(r.normal(10.0, 1.2, shape)), 1, 15).astype(np.int64)
+    mant = r.integers(0, 8, shape, dtype=np.int64)
+    mant = np.where(expo == 15, np.minimum(mant, 6), mant)
+    codes = ((sign << 7) | (expo << 3) | mant).astype(np.uint8)
+    scales = r.integers(116, 118, (Ln, 2 * nkv * d, H // 32)).astype(np.uint8)
+    return MXKVWeights(codes, scales)
