@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import DFlashError, check  # noqa: F401
 
 __all__ = ["DFlashLayer", "KVCache", "PagedKVCache", "LayerShape", "ContextKV", "ContextKVShape",
-           "DFlashDecoder", "rms_norm", "run_round", "DFlashError", "KERNEL_NAMES"]
+           "DFlashDecoder", "rms_norm", "mxfp8_quantize", "run_round", "DFlashError", "KERNEL_NAMES"]
 KERNEL_NAMES = _lib.KERNEL_NAMES
 
 _DTYPES = {torch.float32: _lib.DFLASH_F32, torch.bfloat16: _lib.DFLASH_BF16}
@@ -198,23 +198,39 @@ class ContextKVShape:
 class ContextKV:
     """Context K/V of every draft layer at once (the multi-layer precompute):
     ``hidden_norm`` ``[H]``, ``w_kv`` ``[L * 2 * nkv * d, H]`` (each layer's K
-    rows then V rows), ``k_norm`` ``[L, d]``, device tensors in ``shape.dtype``."""
+    rows then V rows), ``k_norm`` ``[L, d]``, device tensors in ``shape.dtype``.
+
+    With ``w_kv_scale`` the weights are MXFP8 (bf16 only): ``w_kv`` holds E4M3
+    codes (uint8) and ``w_kv_scale`` ``[L * 2 * nkv * d, H / 32]`` their E8M0
+    block scales (uint8), and the projection is the block-scaled GEMM."""
 
     def __init__(self, shape: ContextKVShape, hidden_norm: torch.Tensor, w_kv: torch.Tensor,
-                 k_norm: torch.Tensor):
+                 k_norm: torch.Tensor, w_kv_scale: Optional[torch.Tensor] = None):
         self.shape = shape
+        self.mxfp8 = w_kv_scale is not None
         self._weights = [t.contiguous() for t in (hidden_norm, w_kv, k_norm)]
-        for t in self._weights:
-            if t.dtype != shape.dtype or not t.is_cuda:
-                raise ValueError("weights must be device tensors of the dtype")
+        for i, t in enumerate(self._weights):
+            want = torch.uint8 if (self.mxfp8 and i == 1) else shape.dtype
+            if t.dtype != want or not t.is_cuda:
+                raise ValueError("weights must be device tensors of the dtype (uint8 codes for MXFP8)")
         cfg = _lib.CtxKVConfig(shape.hidden, shape.n_layers, shape.n_kv_heads, shape.head_dim,
                                shape.max_position, _DTYPES[shape.dtype], float(shape.rope_theta),
                                float(shape.rms_eps))
-        w = _lib.CtxKVWeights(*[t.data_ptr() for t in self._weights])
         handle = C.c_void_p()
         with torch.cuda.device(self._weights[0].device):
-            check(_lib.lib().dflash_ctxkv_create(C.byref(cfg), C.byref(w), C.byref(handle)),
-                  "dflash_ctxkv_create")
+            if self.mxfp8:
+                sc = w_kv_scale.contiguous()
+                if sc.dtype != torch.uint8 or not sc.is_cuda:
+                    raise ValueError("w_kv_scale must be a uint8 device tensor")
+                self._weights.append(sc)
+                hn, wk, kn = self._weights[:3]
+                w = _lib.CtxKVMXFP8Weights(hn.data_ptr(), wk.data_ptr(), sc.data_ptr(), kn.data_ptr())
+                check(_lib.lib().dflash_ctxkv_create_mxfp8(C.byref(cfg), C.byref(w), C.byref(handle)),
+                      "dflash_ctxkv_create_mxfp8")
+            else:
+                w = _lib.CtxKVWeights(*[t.data_ptr() for t in self._weights])
+                check(_lib.lib().dflash_ctxkv_create(C.byref(cfg), C.byref(w), C.byref(handle)),
+                      "dflash_ctxkv_create")
         self._h = handle
         self._ws: Optional[torch.Tensor] = None
 
@@ -262,6 +278,21 @@ class ContextKV:
             self.close()
         except Exception:
             pass
+
+
+def mxfp8_quantize(x: torch.Tensor, stream=None):
+    """MXFP8 codes ``[rows, cols]`` and E8M0 scales ``[rows, cols / 32]``
+    (uint8 device tensors) of a bf16 device matrix, by the rule the MXFP8
+    precompute applies to its activations."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2:
+        raise ValueError("x must be a 2-D bf16 device tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    check(_lib.lib().dflash_mxfp8_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream_handle(stream)),
+          "dflash_mxfp8_quantize")
+    return codes, scales
 
 
 class _BorrowedLayer(DFlashLayer):

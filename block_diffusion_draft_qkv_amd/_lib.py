@@ -34,6 +34,7 @@ EXPORTS = (
     "dflash_layer_set_append_mode",
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
     "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
+    "dflash_ctxkv_create_mxfp8", "dflash_mxfp8_quantize",
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
 )
@@ -66,6 +67,11 @@ class CtxKVConfig(C.Structure):
 
 class CtxKVWeights(C.Structure):
     _fields_ = [("hidden_norm", C.c_void_p), ("w_kv", C.c_void_p), ("k_norm", C.c_void_p)]
+
+
+class CtxKVMXFP8Weights(C.Structure):
+    _fields_ = [("hidden_norm", C.c_void_p), ("w_kv", C.c_void_p), ("w_kv_scale", C.c_void_p),
+                ("k_norm", C.c_void_p)]
 
 
 class DecoderConfig(C.Structure):
@@ -116,6 +122,11 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_create.argtypes = [C.POINTER(CtxKVConfig), C.POINTER(CtxKVWeights),
                                           C.POINTER(C.c_void_p)]
         h.dflash_ctxkv_create.restype = C.c_int
+        h.dflash_ctxkv_create_mxfp8.argtypes = [C.POINTER(CtxKVConfig), C.POINTER(CtxKVMXFP8Weights),
+                                                C.POINTER(C.c_void_p)]
+        h.dflash_ctxkv_create_mxfp8.restype = C.c_int
+        h.dflash_mxfp8_quantize.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+        h.dflash_mxfp8_quantize.restype = C.c_int
         h.dflash_ctxkv_destroy.argtypes = [C.c_void_p]
         h.dflash_ctxkv_destroy.restype = None
         h.dflash_ctxkv_workspace_bytes.argtypes = [C.c_void_p, C.c_int64]

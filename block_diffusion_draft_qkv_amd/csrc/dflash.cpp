@@ -64,7 +64,9 @@ struct dflash_decoder {
 
 struct dflash_ctxkv {
   dflash_ctxkv_config cfg;
-  dflash_ctxkv_weights w;
+  dflash_ctxkv_weights w;      // with mx, w.w_kv holds E4M3 codes
+  bool mx = false;             // MXFP8 weights (dflash_ctxkv_create_mxfp8)
+  const uint8_t* w_scale = nullptr;
   int num_cus = 256;
   int append_mode = DFLASH_APPEND_AUTO;
   float* cos_sin = nullptr;
@@ -141,17 +143,24 @@ TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, b
 }
 
 // Workspace of a context precompute of mc rows: hidden_norm-ed rows in the
-// element type, then the fp32 projection [k slices][mc][L * 2 * nkv * d].
+// element type, then the fp32 projection [k slices][mc][L * 2 * nkv * d]. With
+// MXFP8 weights: the hidden_norm-ed rows as E4M3 codes [mc][H] and their E8M0
+// scales [mc][H / 32] (the projection always appends in its epilogue).
 struct CtxCarve {
-  size_t normed, proj, total;
+  size_t normed, proj, scales, total;
 };
-CtxCarve ctx_carve(const dflash_ctxkv_config& c, int64_t mc) {
+CtxCarve ctx_carve(const dflash_ctxkv_config& c, int64_t mc, bool mx) {
   const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, m = std::max<int64_t>(mc, 1);
   const int64_t n = (int64_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim;
   CtxCarve w{};
   size_t off = 0;
-  w.normed = off; off += align_up(m * c.hidden * es);
-  w.proj = off;   off += align_up(kMaxKSlices * m * n * 4);
+  if (mx) {
+    w.normed = off; off += align_up(m * c.hidden);
+    w.scales = off; off += align_up(m * c.hidden / 32);
+  } else {
+    w.normed = off; off += align_up(m * c.hidden * es);
+    w.proj = off;   off += align_up(kMaxKSlices * m * n * 4);
+  }
   w.total = off;
   return w;
 }
@@ -569,24 +578,29 @@ int dflash_layer_kernel_times(dflash_layer* L, double* ms, int64_t* count) {
   return DFLASH_OK;
 }
 
-int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights,
-                        dflash_ctxkv** out) {
+namespace {
+int ctxkv_create_impl(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights, const uint8_t* w_scale,
+                      bool mx, dflash_ctxkv** out) {
   if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
   *out = nullptr;
   if (!weights->hidden_norm || !weights->w_kv || !weights->k_norm) return DFLASH_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(weights->hidden_norm) % 16 || reinterpret_cast<uintptr_t>(weights->w_kv) % 16)
     return DFLASH_ERR_ARG;
+  if (mx && (!w_scale || reinterpret_cast<uintptr_t>(w_scale) % 4)) return DFLASH_ERR_ARG;
   if (cfg->hidden <= 0 || cfg->n_kv_heads <= 0 || cfg->n_layers <= 0 || cfg->max_position <= 0)
     return DFLASH_ERR_SHAPE;
-  if (cfg->hidden % 64) return DFLASH_ERR_SHAPE;
+  if (cfg->hidden % (mx ? 128 : 64)) return DFLASH_ERR_SHAPE;
   if (cfg->n_layers > kMaxLayers || cfg->n_kv_heads > kMaxKvHeads) return DFLASH_ERR_UNSUPPORTED;
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
   if (!(cfg->rope_theta > 0.0) || !(cfg->rms_eps >= 0.0)) return DFLASH_ERR_ARG;
   if (cfg->dtype != DFLASH_F32 && cfg->dtype != DFLASH_BF16) return DFLASH_ERR_ARG;
+  if (mx && cfg->dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
   dflash_ctxkv* h = new (std::nothrow) dflash_ctxkv();
   if (!h) return DFLASH_ERR_HIP;
   h->cfg = *cfg;
   h->w = *weights;
+  h->mx = mx;
+  h->w_scale = w_scale;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) { delete h; return DFLASH_ERR_HIP; }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
@@ -602,6 +616,33 @@ int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weigh
   *out = h;
   return DFLASH_OK;
 }
+}  // namespace
+
+int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights,
+                        dflash_ctxkv** out) {
+  return ctxkv_create_impl(cfg, weights, nullptr, false, out);
+}
+
+int dflash_ctxkv_create_mxfp8(const dflash_ctxkv_config* cfg, const dflash_ctxkv_mxfp8_weights* weights,
+                              dflash_ctxkv** out) {
+  if (!weights) return DFLASH_ERR_ARG;
+  dflash_ctxkv_weights w;
+  w.hidden_norm = weights->hidden_norm;
+  w.w_kv = weights->w_kv;
+  w.k_norm = weights->k_norm;
+  return ctxkv_create_impl(cfg, &w, static_cast<const uint8_t*>(weights->w_kv_scale), true, out);
+}
+
+int dflash_mxfp8_quantize(const void* x, int64_t rows, int32_t cols, void* codes, void* scales, void* stream) {
+  if (rows < 0 || rows > INT32_MAX || cols <= 0 || cols % 128) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!x || !codes || !scales) return DFLASH_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 16) return DFLASH_ERR_ARG;
+  if (launch_rms_rows_mx(x, nullptr, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), (int)rows, cols,
+                         0.f, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  return DFLASH_OK;
+}
 
 void dflash_ctxkv_destroy(dflash_ctxkv* h) {
   if (!h) return;
@@ -613,7 +654,7 @@ void dflash_ctxkv_destroy(dflash_ctxkv* h) {
 
 size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx) {
   if (!h || total_ctx < 0) return 0;
-  return ctx_carve(h->cfg, total_ctx).total;
+  return ctx_carve(h->cfg, total_ctx, h->mx).total;
 }
 
 int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
@@ -661,7 +702,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   if (Mc == 0) return DFLASH_OK;
   if (!context_states || !positions || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
   if (!workspace) return DFLASH_ERR_WORKSPACE;
-  const CtxCarve wc = ctx_carve(c, Mc);
+  if (h->mx && h->append_mode == DFLASH_APPEND_SEPARATE) return DFLASH_ERR_UNSUPPORTED;
+  const CtxCarve wc = ctx_carve(c, Mc, h->mx);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return DFLASH_ERR_WORKSPACE;
 
@@ -671,17 +713,21 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   float* proj = reinterpret_cast<float*>(ws + wc.proj);
   const int N = nl * 2 * nkv * d;
 
-  // hidden_norm over each raw context row
-  if (launch_rms_rows(c.dtype, context_states, nullptr, h->w.hidden_norm, nullptr, normed, (int)Mc, H,
-                      (float)c.rms_eps, s) !=
-      hipSuccess)
+  // hidden_norm over each raw context row (as MXFP8 rows for MXFP8 weights)
+  if (h->mx) {
+    if (launch_rms_rows_mx(context_states, h->w.hidden_norm, static_cast<uint8_t*>(normed),
+                           reinterpret_cast<uint8_t*>(ws + wc.scales), (int)Mc, H, (float)c.rms_eps, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+  } else if (launch_rms_rows(c.dtype, context_states, nullptr, h->w.hidden_norm, nullptr, normed, (int)Mc, H,
+                             (float)c.rms_eps, s) != hipSuccess) {
     return DFLASH_ERR_HIP;
+  }
   // Every layer's K and V in one projection. With enough 64-row tiles (one
   // head each) its epilogue normalises, rotates and appends (no fp32 rows);
   // otherwise fp32 rows (k split when M is small) go to HK2 over the layers.
   const int heads = nl * 2 * nkv;
   const int t64 = (int)((Mc + 63) / 64) * heads, t128 = (int)((Mc + 127) / 128) * heads;
-  const bool fused = h->append_mode == DFLASH_APPEND_FUSED ||
+  const bool fused = h->mx || h->append_mode == DFLASH_APPEND_FUSED ||
                      (h->append_mode == DFLASH_APPEND_AUTO && t64 >= h->num_cus * 3 / 4);
   NormRopeArgs na;
   std::memset(&na, 0, sizeof(na));
@@ -716,7 +762,14 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
     na.qkv = proj;
     na.ctxkv = proj;
     na.qpack = proj;
-    if (launch_gemm_append(c.dtype, d, ga, na, tiles, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (h->mx) {
+      // E4M3 rows of H bytes; the scales of both operands ride in the problem
+      ga.p[1].sa = reinterpret_cast<const uint8_t*>(ws + wc.scales);
+      ga.p[1].sb = h->w_scale;
+      if (launch_gemm_append_mx(d, ga, na, tiles, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+    } else if (launch_gemm_append(c.dtype, d, ga, na, tiles, bm, s) != hipSuccess) {
+      return DFLASH_ERR_HIP;
+    }
   } else {
     const TileChoice t = choose_tiles(h->num_cus, (int)Mc, N, 0, 0, true);
     ga.nprob = 1;

@@ -217,6 +217,197 @@ __device__ __forceinline__ bool gemm_core(const TileJob& J, uint32_t lds0, int e
   return true;
 }
 
+// MXFP8 operands (OCP MX: E4M3 elements, one E8M0 scale byte per 32
+// consecutive k). A k step is 128 elements: the same 128 bytes per row as a
+// bf16 step, plus 4 scale bytes per row (the step's four blocks), which the
+// producers stream into the stage behind the data with 256-byte LDS-DMA
+// loads (64 rows each; the (BM + BN) / 64 of a step alternate between the two
+// producers, so their per-step block counts may differ by one).
+template <int BM, int BN> struct GemmShapeMX {
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int AS_OFF = A_BYTES + B_BYTES, BS_OFF = AS_OFF + BM * 4, STAGE = BS_OFF + BN * 4;
+  static constexpr int APP = BM / 8 / kGemmProducers, BPP = BN / 8 / kGemmProducers;
+  static constexpr int SCALE_LOADS = (BM + BN) / 64;
+  static constexpr int PER0 = APP + BPP + (SCALE_LOADS + 1) / 2, PER1 = APP + BPP + SCALE_LOADS / 2;
+  static constexpr int S_LDS = (160 * 1024) / STAGE, S_VM = 1 + 63 / PER0;
+  static constexpr int S = S_LDS < S_VM ? (S_LDS < 8 ? S_LDS : 8) : (S_VM < 8 ? S_VM : 8);
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int MI = WM / 16, NI = WN / 16;
+  static_assert((S - 1) * PER0 <= 63, "outstanding DMA blocks must fit vmcnt");
+  static_assert(STAGE % 16 == 0, "stages stay 16-byte aligned");
+};
+
+// The MXFP8 main loop, with gemm_core's protocol (producers return false after
+// `extra` more barriers, consumers true with their sub-tile in acc). In a
+// 16x16x128 scaled MFMA, lane (q, r) of an operand holds row r's k 16q ..
+// 16q + 15 in its first 16 bytes and k 64 + 16q .. 64 + 16q + 15 in its last
+// 16 (logical chunks q and q + 4 of the 128-byte step row), and supplies the
+// scale of k block q (k 32q .. 32q + 31) of row r; measured on gfx950 with
+// one-hot operands. Consumers read step s + 1's fragments while the MFMAs of
+// step s run (two fragment sets).
+template <int BM, int BN>
+__device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, int extra,
+                                             f32x4 (&acc)[GemmShapeMX<BM, BN>::NI][GemmShapeMX<BM, BN>::MI]) {
+  using Sh = GemmShapeMX<BM, BN>;
+  constexpr int S = Sh::S, STAGE = Sh::STAGE, A_BYTES = Sh::A_BYTES, AS_OFF = Sh::AS_OFF, BS_OFF = Sh::BS_OFF;
+  constexpr int APP = Sh::APP, BPP = Sh::BPP, WM = Sh::WM, WN = Sh::WN, MI = Sh::MI, NI = Sh::NI;
+  constexpr int SL = Sh::SCALE_LOADS, ASL = BM / 64;
+  const GemmProblem& P = J.P;
+  const int m0 = J.m0, n0 = J.n0, nk = J.nk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kbs = P.k / 32;  // scale bytes per row
+
+  if (wave >= kGemmConsumers) {
+    // ---------------------------------------------------------- producers
+    const int pw = wave - kGemmConsumers;
+    uint32_t aoff[APP], boff[BPP], soff[(SL + 1) / 2];
+#pragma unroll
+    for (int i = 0; i < APP; ++i) {
+      const int row = (i * kGemmProducers + pw) * 8 + lane / 8;
+      const int c = (lane % 8) ^ rswz<8>(row);
+      const int gr = m0 + row < P.m ? m0 + row : P.m - 1;
+      aoff[i] = (uint32_t)((size_t)gr * P.lda) + (uint32_t)(c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < BPP; ++i) {
+      const int row = (i * kGemmProducers + pw) * 8 + lane / 8;
+      const int c = (lane % 8) ^ rswz<8>(row);
+      const int gr = n0 + row < P.n ? n0 + row : P.n - 1;
+      boff[i] = (uint32_t)((size_t)gr * P.ldb) + (uint32_t)(c * 16);
+    }
+    // Scale load u = 2 i + pw: A rows 64 u .. 64 u + 63 when u < BM / 64,
+    // else B rows 64 (u - BM / 64) ..; lane l fetches its row's 4 bytes.
+#pragma unroll
+    for (int i = 0; i < (SL + 1) / 2; ++i) {
+      const int u = 2 * i + pw;
+      int gr = 0;
+      if (u < ASL) {
+        gr = m0 + 64 * u + lane;
+        gr = gr < P.m ? gr : P.m - 1;
+      } else if (u < SL) {
+        gr = n0 + 64 * (u - ASL) + lane;
+        gr = gr < P.n ? gr : P.n - 1;
+      }
+      soff[i] = (uint32_t)gr * (uint32_t)kbs;
+    }
+    const char* Ab = static_cast<const char*>(P.a);
+    const char* Bb = static_cast<const char*>(P.b);
+    auto issue = [&](int step) {
+      const size_t kbyte = (size_t)step * 128;
+      const uint32_t sl = lds0 + (uint32_t)(step % S) * STAGE;
+      const void* ab = uniform_ptr(Ab + kbyte);
+      const void* bb = uniform_ptr(Bb + kbyte);
+#pragma unroll
+      for (int i = 0; i < APP; ++i)
+        lds_dma16(aoff[i], ab, sl + (uint32_t)(i * kGemmProducers + pw) * 1024u);
+#pragma unroll
+      for (int i = 0; i < BPP; ++i)
+        lds_dma16(boff[i], bb, sl + A_BYTES + (uint32_t)(i * kGemmProducers + pw) * 1024u);
+      const void* sab = uniform_ptr(P.sa + (size_t)step * 4);
+      const void* sbb = uniform_ptr(P.sb + (size_t)step * 4);
+#pragma unroll
+      for (int i = 0; i < (SL + 1) / 2; ++i) {
+        const int u = 2 * i + pw;
+        if (u < ASL) lds_dma4(soff[i], sab, sl + AS_OFF + (uint32_t)u * 256u);
+        else if (u < SL) lds_dma4(soff[i], sbb, sl + BS_OFF + (uint32_t)(u - ASL) * 256u);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s);
+    for (int it = 0; it < nk; ++it) {
+      const int after = nk - 1 - it < S - 2 ? nk - 1 - it : S - 2;
+      if (pw == 0) stage_wait<Sh::PER0, S>(after);
+      else stage_wait<Sh::PER1, S>(after);
+      block_barrier();
+      if (it + S - 1 < nk) issue(it + S - 1);
+    }
+    for (int e = 0; e < extra; ++e) block_barrier();
+    return false;
+  }
+
+  // ------------------------------------------------------------ consumers
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, r16 = lane & 15;
+  uint32_t ard[2], brd[2];
+  {
+    const int sw = rswz<8>(r16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ard[j] = (uint32_t)((wm * WM + r16) * 8 + ((q + 4 * j) ^ sw)) * 16u;
+      brd[j] = (uint32_t)((wn * WN + r16) * 8 + ((q + 4 * j) ^ sw)) * 16u + A_BYTES;
+    }
+  }
+  const uint32_t asc = (uint32_t)(AS_OFF + (wm * WM + r16) * 4 + q);
+  const uint32_t bsc = (uint32_t)(BS_OFF + (wn * WN + r16) * 4 + q);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Frag {
+    u32x4 a[MI][2], b[NI][2];
+    uint32_t sa[MI], sb[NI];
+  };
+  auto read = [&](Frag& f, int step) {
+    const uint32_t sl = lds0 + (uint32_t)(step % S) * STAGE;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      f.a[mi][0] = lds_read16(sl + ard[0] + (uint32_t)(mi * 16 * 128));
+      f.a[mi][1] = lds_read16(sl + ard[1] + (uint32_t)(mi * 16 * 128));
+      f.sa[mi] = lds_read_u8(sl + asc + (uint32_t)(mi * 64));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      f.b[ni][0] = lds_read16(sl + brd[0] + (uint32_t)(ni * 16 * 128));
+      f.b[ni][1] = lds_read16(sl + brd[1] + (uint32_t)(ni * 16 * 128));
+      f.sb[ni] = lds_read_u8(sl + bsc + (uint32_t)(ni * 64));
+    }
+  };
+  // C^T = W . A^T: the weight fragment is the MFMA's first operand, so a lane
+  // ends with m = r16 and n = 4q .. 4q + 3, as in the bf16 loop.
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const i32x8 wb = {(int)f.b[ni][0][0], (int)f.b[ni][0][1], (int)f.b[ni][0][2], (int)f.b[ni][0][3],
+                        (int)f.b[ni][1][0], (int)f.b[ni][1][1], (int)f.b[ni][1][2], (int)f.b[ni][1][3]};
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const i32x8 xa = {(int)f.a[mi][0][0], (int)f.a[mi][0][1], (int)f.a[mi][0][2], (int)f.a[mi][0][3],
+                          (int)f.a[mi][1][0], (int)f.a[mi][1][1], (int)f.a[mi][1][2], (int)f.a[mi][1][3]};
+        acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb, xa, acc[ni][mi], 0, 0, 0,
+                                                                      (int)f.sb[ni], 0, (int)f.sa[mi]);
+      }
+    }
+  };
+  Frag f0, f1;
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    block_barrier();
+    read(f0, it);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it > 0) mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    read(f1, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (it < nk) {
+    block_barrier();
+    read(f0, it);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it > 0) mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+  } else if (nk > 0) {
+    mma(f1);
+  }
+  return true;
+}
+
 template <typename T, typename OutT, int BM, int BN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   using Sh = GemmShape<BM, BN>;
@@ -333,16 +524,19 @@ __device__ inline float quad_sum(float v) {
 // built cos/sin table, and the stores: queries packed as rows i*g + hh of their
 // KV head's tile, keys to cache K, values (raw) transposed to cache V.
 // Positions outside the table are clamped and latched in the error flag.
-template <typename T, int BM, int D>
+// With MX the operands are MXFP8 (gemm_core_mx; T, the cache and gain type, is
+// bf16): the multi-layer context precompute's block-scaled K/V projection
+// (vLLM page "qwen3_dflash", _build_mxfp8_context_kv_proj).
+template <typename T, int BM, int D, bool MX = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs args, NormRopeArgs a) {
-  using Sh = GemmShape<BM, D>;
+  using Sh = std::conditional_t<MX, GemmShapeMX<BM, D>, GemmShape<BM, D>>;
   constexpr int WM = Sh::WM, MI = Sh::MI, NI = Sh::NI, HALF = D / 2, REGS = MI * NI * 4;
   static_assert(Sh::WN == HALF, "a tile holds one head");
   static_assert(4 * REGS / 2 * 64 * 4 <= Sh::S * Sh::STAGE, "the exchange fits in the ring");
   __shared__ u32x4 lds[Sh::S * Sh::STAGE / 16];
   TileJob J = tile_job<BM, D>(args);
   J.k_first = 0;
-  J.nk = J.P.k / (8 * (16 / (int)sizeof(T)));
+  J.nk = MX ? J.P.k / 128 : J.P.k / (8 * (16 / (int)sizeof(T)));
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
   const int nq = a.nq, nkv = a.nkv, bs = a.bs, g = nq / nkv, R = bs * g;
@@ -433,7 +627,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
   }
 
   f32x4 acc[NI][MI];
-  if (!gemm_core<T, BM, D>(J, lds_base(lds), 2, acc)) return;
+  bool consumer;
+  if constexpr (MX) consumer = gemm_core_mx<BM, D>(J, lds_base(lds), 2, acc);
+  else consumer = gemm_core<T, BM, D>(J, lds_base(lds), 2, acc);
+  if (!consumer) return;
 
   float* xch = reinterpret_cast<float*>(lds);
   constexpr int XR = MH * NI * 4;  // values one lane hands over
@@ -585,6 +782,20 @@ hipError_t launch_append_t(const GemmArgs& args, const NormRopeArgs& nr, int tot
 }
 
 }  // namespace
+
+hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormRopeArgs& nr, int total_tiles,
+                                 int bm, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  const dim3 grid(total_tiles), block(kGemmThreads);
+  if (head_dim == 128) {
+    if (bm == 128) hipLaunchKernelGGL((gemm_append_kernel<__bf16, 128, 128, true>), grid, block, 0, s, args, nr);
+    else hipLaunchKernelGGL((gemm_append_kernel<__bf16, 64, 128, true>), grid, block, 0, s, args, nr);
+  } else {
+    if (bm == 128) hipLaunchKernelGGL((gemm_append_kernel<__bf16, 128, 64, true>), grid, block, 0, s, args, nr);
+    else hipLaunchKernelGGL((gemm_append_kernel<__bf16, 64, 64, true>), grid, block, 0, s, args, nr);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,
                               int total_tiles, int bm, hipStream_t stream) {

@@ -28,6 +28,11 @@ struct GemmProblem {
   // SwiGLU GEMM: W rows [0, b_pair) are the gate rows, [b_pair, 2 b_pair) the
   // up rows; output column j of a tile pairs gate row j and up row b_pair + j.
   int32_t b_pair = 0;
+  // MXFP8 operands (gemm_append with the MX flag): a and b hold E4M3 codes
+  // ([m][lda], [n][ldb] bytes) and sa / sb their E8M0 scales, one byte per 32
+  // consecutive k, rows of k / 32 bytes.
+  const uint8_t* sa = nullptr;
+  const uint8_t* sb = nullptr;
 };
 struct GemmArgs {
   GemmProblem p[2];
@@ -125,6 +130,15 @@ hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, 
 // The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
 // head_dim, no k split) doing the work of launch_norm_rope in its epilogue
 // (nr's qkv, ctxkv and kslices fields are unused).
+// gemm_append over MXFP8 operands (GemmProblem sa / sb set, k % 128 == 0);
+// the caches and gains are bf16.
+hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormRopeArgs& nr, int total_tiles,
+                                 int bm, hipStream_t stream);
+// MXFP8 rows of bf16 x [rows][h] (h % 128 == 0): with g, hidden_norm first
+// (x / sqrt(mean(x^2) + eps) * g rounded to bf16), without g x itself; codes
+// [rows][h] E4M3 bytes and scales [rows][h / 32] E8M0 bytes.
+hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
+                              float eps, hipStream_t stream);
 hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,
                               int total_tiles, int bm, hipStream_t stream);
 

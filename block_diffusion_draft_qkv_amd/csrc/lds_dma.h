@@ -39,6 +39,15 @@ __device__ inline void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds)
                  : "memory", "m0");
 }
 
+// The 4-byte-per-lane form: the wave's 64 dwords land at LDS bytes
+// lds .. lds + 255 (lane l at 4 l). Default cache policy.
+__device__ inline void lds_dma4(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) leaving expcnt and lgkmcnt alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
 #define DFLASH_VMWAIT(N) \
@@ -61,6 +70,10 @@ __device__ inline uint32_t lds_base(const void* shared_array) {
 
 __device__ inline u32x4 lds_read16(uint32_t byte_addr) {
   return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)byte_addr;
+}
+
+__device__ inline uint32_t lds_read_u8(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) uint8_t*)(uintptr_t)byte_addr;
 }
 
 // Chunk swizzle for rows of CPR 16-byte chunks read 16 consecutive rows at a

@@ -5,6 +5,8 @@
 //    the activation dtype), a decoder layer's input_layernorm and the draft
 //    model's final norm (NeMo page "draft_qwen3": Qwen3DFlashDecoderLayer
 //    input_layernorm; vLLM page: DFlashQwen3Model.forward, self.norm).
+//  * rms_rows_mx: the hidden_norm written as MXFP8 rows for the block-scaled
+//    context K/V projection (or a plain MXFP8 quantisation of bf16 rows).
 //  * add_rms_rows: h = x + y rounded to the element type (the residual
 //    stream), and out = rmsnorm(h) * g: a decoder layer's residual add followed
 //    by post_attention_layernorm (vLLM threads the residual through the norm the
@@ -101,7 +103,103 @@ __global__ __launch_bounds__(256) void rms_rows_kernel(const T* __restrict__ x, 
   for (int c = tid + kChunks * 256; c < nchunk; c += 256) put(c, hrow ? hrow[c] : row[c]);
 }
 
+// E4M3 code of t with |t| <= 448 (OCP FP8: bias 7, 3 mantissa bits,
+// subnormals m * 2^-9): round to nearest, ties to even, sign kept for zero.
+__device__ inline uint32_t e4m3_code(float t) {
+  const uint32_t bits = __float_as_uint(t);
+  const float a = fabsf(t);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)rintf(a * 0x1p9f);  // 0 .. 8 (8 is the smallest normal, 0x08)
+  } else {
+    int e = (int)((bits >> 23) & 0xff) - 127;                      // a in [2^e, 2^(e+1))
+    const float frac = (__uint_as_float((bits & 0x007fffffu) | 0x3f800000u) - 1.0f) * 8.0f;
+    uint32_t m = (uint32_t)rintf(frac);                            // exact product, RNE
+    if (m == 8) { m = 0; ++e; }
+    code = ((uint32_t)(e + 7) << 3) | m;
+  }
+  return code | ((bits >> 24) & 0x80u);
+}
+
+// MXFP8 quantisation of bf16 rows (OCP MX: one E8M0 scale per 32 consecutive
+// elements, E4M3 elements), optionally after the hidden_norm: the input of the
+// block-scaled context K/V projection (vLLM page "qwen3_dflash",
+// _build_mxfp8_context_kv_proj; the states are hidden_norm-ed into the
+// activation dtype first, _normalize_context_states). Per block: amax, shared
+// exponent floor(log2 amax) - 8 clamped to [-127, 127] (scale byte =
+// biased exponent of amax - 8, clamped to [0, 254]), elements x / 2^exponent
+// saturated to +-448 and rounded to nearest even. A block is four consecutive
+// threads' 16-byte chunks; amax is reduced over those four lanes.
+__global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restrict__ x,
+                                                          const __bf16* __restrict__ g,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, int h, float eps) {
+  constexpr int V = 8;
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunk = h / V;  // a multiple of 16: blocks never straddle threads of two passes
+  const size_t roff = (size_t)blockIdx.x * h;
+  const u32x4* row = reinterpret_cast<const u32x4*>(x + roff);
+  const u32x4* gv = reinterpret_cast<const u32x4*>(g);
+  float inv = 1.f;
+  if (g != nullptr) {
+    float ss = 0.f;
+    for (int c = tid; c < nchunk; c += 256) {
+      const u32x4 v = row[c];
+      const __bf16* e = reinterpret_cast<const __bf16*>(&v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) ss += (float)e[i] * (float)e[i];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    inv = rsqrtf((part[0] + part[1] + part[2] + part[3]) / (float)h + eps);
+  }
+  uint2* out = reinterpret_cast<uint2*>(codes + roff);
+  for (int c = tid; c < nchunk; c += 256) {  // the row is re-read from L2 after the norm
+    const u32x4 v = row[c];
+    const __bf16* e = reinterpret_cast<const __bf16*>(&v);
+    float y[V];
+    if (g != nullptr) {
+      const u32x4 gc = gv[c];
+      const __bf16* ge = reinterpret_cast<const __bf16*>(&gc);
+#pragma unroll
+      for (int i = 0; i < V; ++i) y[i] = (float)(__bf16)((float)e[i] * inv * (float)ge[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) y[i] = (float)e[i];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
+    const int sbyte = min(max(ef - 8, 0), 254);
+    const float mul = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-(sbyte - 127), normal
+    uint2 packed = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float t = fminf(fmaxf(y[i] * mul, -448.f), 448.f);
+      const uint32_t cd = e4m3_code(t);
+      if (i < 4) packed.x |= cd << (8 * i);
+      else packed.y |= cd << (8 * (i - 4));
+    }
+    out[c] = packed;
+    if ((tid & 3) == 0) scales[(size_t)blockIdx.x * (h / 32) + c / 4] = (uint8_t)sbyte;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
+                              float eps, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rms_rows_mx_kernel, dim3(rows), dim3(256), 0, stream, static_cast<const __bf16*>(x),
+                     static_cast<const __bf16*>(g), codes, scales, h, eps);
+  return hipGetLastError();
+}
 
 hipError_t launch_rms_rows(int dtype, const void* x, const void* y, const void* g, void* hout, void* out,
                            int rows, int h, float eps, hipStream_t stream) {

@@ -34,7 +34,8 @@
  *     except dflash_layer_poll_error, dflash_layer_kernel_times and
  *     dflash_ctxkv_poll_error.
  *   - Element type of every activation, weight and cache buffer is the
- *     config's dtype (fp32 or bf16); accumulation is fp32.
+ *     config's dtype (fp32 or bf16), except the MXFP8 weights of
+ *     dflash_ctxkv_create_mxfp8; accumulation is fp32.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -264,6 +265,25 @@ typedef struct {
     const void* k_norm;       /* [L, d] each layer's K RMSNorm gain               */
 } dflash_ctxkv_weights;
 
+/* MXFP8 weights of the precompute (vLLM page "qwen3_dflash",
+ * _build_mxfp8_context_kv_proj: when every layer's qkv_proj is an MXFP8
+ * linear, the context K/V projection is one block-scaled GEMM over the K/V
+ * rows of all layers, rows and block scales copied as they are because the
+ * scales belong to output rows). The format is OCP Microscaling MXFP8: FP8
+ * E4M3 elements (bias 7, 3 mantissa bits, largest 448, S.1111.111 NaN) and
+ * one E8M0 scale byte (2^(s - 127)) per 32 consecutive elements along hidden.
+ * Borrowed device pointers; the config dtype must be DFLASH_BF16 (states,
+ * gains and caches) and hidden a multiple of 128. */
+typedef struct {
+    const void* hidden_norm;  /* [H] bf16, 16-byte aligned                        */
+    const void* w_kv;         /* [L * 2 * nkv * d, H] E4M3 bytes, rows ordered as
+                                 dflash_ctxkv_weights.w_kv; 16-byte aligned       */
+    const void* w_kv_scale;   /* [L * 2 * nkv * d, H / 32] E8M0 bytes: row r's
+                                 block j scales w_kv[r][32 j .. 32 j + 31];
+                                 4-byte aligned                                   */
+    const void* k_norm;       /* [L, d] bf16                                      */
+} dflash_ctxkv_mxfp8_weights;
+
 typedef struct dflash_ctxkv dflash_ctxkv; /* opaque */
 
 /* Create a precompute handle on the current device; it builds its own RoPE
@@ -272,6 +292,18 @@ typedef struct dflash_ctxkv dflash_ctxkv; /* opaque */
  * DFLASH_ERR_HIP. */
 int dflash_ctxkv_create(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights* weights,
                         dflash_ctxkv** out);
+
+/* The same handle over MXFP8 weights. Each append then writes the
+ * hidden_norm-ed rows (rounded to bf16) as MXFP8 rows (dflash_mxfp8_quantize's
+ * rule) and runs the block-scaled projection (scaled 16x16x128 FP8 MFMA, fp32
+ * sums) with the k_norm / RoPE / append epilogue; the other calls are
+ * unchanged, except that DFLASH_APPEND_SEPARATE is not supported (append then
+ * returns DFLASH_ERR_UNSUPPORTED).
+ * Errors: those of dflash_ctxkv_create; DFLASH_ERR_UNSUPPORTED if the dtype is
+ * not bf16; DFLASH_ERR_SHAPE if hidden % 128; DFLASH_ERR_ARG for a missing or
+ * misaligned scale pointer. */
+int dflash_ctxkv_create_mxfp8(const dflash_ctxkv_config* cfg, const dflash_ctxkv_mxfp8_weights* weights,
+                              dflash_ctxkv** out);
 
 /* Release the handle (waits for the device). NULL is a no-op. */
 void dflash_ctxkv_destroy(dflash_ctxkv* h);
@@ -312,6 +344,21 @@ int dflash_ctxkv_set_append_mode(dflash_ctxkv* h, int32_t mode);
  * if a position fell outside the table since the last poll, which clears it),
  * or DFLASH_OK. */
 int dflash_ctxkv_poll_error(dflash_ctxkv* h, void* stream);
+
+/* MXFP8 quantisation of bf16 rows, the rule the precompute applies to its
+ * activations (the pages do not define the format; this is the OCP MX
+ * conversion): per block of 32 consecutive elements of a row, the shared
+ * exponent is floor(log2(amax)) - 8 clamped to [-127, 127] (scale byte 0 for
+ * an all-zero block), and each element x / 2^exponent is rounded to the
+ * nearest E4M3 value (ties to even), saturating at +-448 and keeping the sign
+ * of a zero. NaN inputs are outside the contract.
+ *   x       device bf16 [rows, cols], 16-byte aligned, cols % 128 == 0
+ *   codes   device [rows, cols] E4M3 bytes, 16-byte aligned (output)
+ *   scales  device [rows, cols / 32] E8M0 bytes (output)
+ * Enqueued on `stream`. Errors: DFLASH_ERR_SHAPE (rows < 0 or > 2^31 - 1,
+ * cols not a positive multiple of 128), DFLASH_ERR_ARG (null or misaligned
+ * pointer), DFLASH_ERR_HIP. rows == 0 is a no-op. */
+int dflash_mxfp8_quantize(const void* x, int64_t rows, int32_t cols, void* codes, void* scales, void* stream);
 
 /* ------------------------------------------------------------------------
  * Draft decoder layer: the attention layer step inside its block (NeMo page

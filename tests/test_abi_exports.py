@@ -16,7 +16,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdflash.so no
 def declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():

@@ -1,0 +1,165 @@
+"""GPU parity of the MXFP8 context K/V precompute and of its quantiser.
+
+* The quantiser is bit-exact against the oracle's OCP MX rule on the same bf16
+  inputs. Both sides decide every code from the same values, so any
+  difference is an error. The cases are random blocks over a wide range of
+  scales, exact ties, saturation, all-zero blocks, tiny and subnormal blocks,
+  and negative values that round to zero.
+* The precompute (hidden_norm rounded to bf16, MXFP8 quantisation, block-scaled
+  projection, k_norm, RoPE, append) is checked against the float64 oracle to
+  the stored-value bound. Cache rows outside the appended ones must be
+  bit-identical and lengths exact. The kernel computes hidden_norm in fp32, so a
+  rare element may round to the other neighbouring bf16 value and then take
+  the neighbouring E4M3 code. That is one element of 4096 in a sum, well
+  inside the bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import assert_close_stored, dev, raw_bits, to64
+from test_gpu_context_kv import make_caches, oracle_caches
+from workload import make_ctxkv_case, make_mxfp8_kv_weights, round_bf16
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+
+def bf16_matrix_with_edges(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-20, 20, (rows, cols // 32))).repeat(32, axis=1)
+    x = round_bf16(x).astype(np.float64)
+    blk = x[0].reshape(-1, 32)
+    blk[0] = 0.0                                            # all-zero block
+    blk[1] = 0.0
+    blk[1, 5] = 2.0 ** -126                                 # smallest normal alone: exponent clamped to -127
+    blk[2] = -(2.0 ** -133) * np.arange(1, 33)              # bf16 subnormals m * 2^-133
+    blk[3] = [1.0, 1.0625, 1.1875, -1.0625, 1.3125, 1.4375, 0.5, 0.53125] * 4
+    blk[3] *= 2.0 ** -3                                     # exact E4M3 ties at amax 2^-3 (scale 2^-11)
+    blk[4] = 0.0
+    blk[4, 0] = 1.90625                                     # saturates at 448
+    blk[4, 1:] = -(2.0 ** -20)                              # rounds to -0 (code 0x80)
+    blk[5] = -0.0
+    x[0] = blk.reshape(-1)
+    return x
+
+
+@pytest.mark.parametrize("rows,cols", [(257, 640), (4096, 4096)])
+def test_mxfp8_quantize_is_bit_exact(rows, cols):
+    from block_diffusion_draft_qkv_amd import mxfp8_quantize
+    x = bf16_matrix_with_edges(rows, cols, seed=rows)
+    print(f"[quantize {rows}x{cols}]", flush=True)
+    codes, scales = mxfp8_quantize(dev(x, torch.bfloat16))
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mx_quantize(x)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    np.testing.assert_array_equal(got_s, want_s)
+    bad = np.argwhere(got_c != want_c)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}: " \
+                          f"{got_c[tuple(bad[0])]:#x} vs {want_c[tuple(bad[0])]:#x}"
+
+
+class MXW:
+    def __init__(self, case, mx):
+        self.hidden_norm = case.weights.hidden_norm
+        self.k_norm = case.weights.k_norm
+        self.w_kv_codes = mx.w_kv_codes
+        self.w_kv_scales = mx.w_kv_scales
+
+
+def make_mx_precompute(case, mx):
+    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape
+    c, w = case.cfg, case.weights
+    shape = ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, torch.bfloat16, c.rope_theta,
+                           c.rms_eps, c.max_position)
+    codes = torch.from_numpy(mx.w_kv_codes.reshape(-1, c.hidden)).cuda()
+    scales = torch.from_numpy(mx.w_kv_scales.reshape(-1, c.hidden // 32)).cuda()
+    return ContextKV(shape, dev(w.hidden_norm, torch.bfloat16), codes, dev(w.k_norm, torch.bfloat16),
+                     w_kv_scale=scales)
+
+
+def run_mx(case, seed):
+    mx = make_mxfp8_kv_weights(case.cfg, seed)
+    pre = make_mx_precompute(case, mx)
+    caches = make_caches(case)
+    before = [(raw_bits(c.k), raw_bits(c.v)) for c in caches]
+    pos = torch.from_numpy(case.positions.astype(np.int32)).cuda()
+    pre.append(dev(case.context_states, torch.bfloat16), case.ctx_offsets, pos, caches)
+    torch.cuda.synchronize()
+    assert pre.poll_error() == 0
+    return mx, pre, caches, before
+
+
+@pytest.mark.parametrize("name", ["M1", "M2", "P3"])
+def test_mxfp8_precompute_matches_oracle(name):
+    case = make_ctxkv_case(name, seed=0)
+    print(f"[mxfp8 {name}] layers {case.cfg.n_layers}, rows {int(case.ctx_offsets[-1])}", flush=True)
+    mx, pre, caches, before = run_mx(case, seed=0)
+    ref = oracle.context_kv_precompute_mxfp8(case.cfg, MXW(case, mx), oracle_caches(case), case.context_states,
+                                             case.ctx_offsets, case.positions)
+    L, n = case.cached_len, case.new_ctx
+    worst = (0.0, 0.0)
+    for layer, kv in enumerate(caches):
+        assert kv.lengths.tolist() == (L + n).tolist()
+        kb, vb = raw_bits(kv.k), raw_bits(kv.v)
+        bk, bv = before[layer]
+        for b in range(case.batch):
+            lb, tb = int(L[b]), int(L[b] + n[b])
+            np.testing.assert_array_equal(kb[b, :, :lb], bk[b, :, :lb])
+            np.testing.assert_array_equal(kb[b, :, tb:], bk[b, :, tb:])
+            np.testing.assert_array_equal(vb[b, :, :, :lb], bv[b, :, :, :lb])
+            np.testing.assert_array_equal(vb[b, :, :, tb:], bv[b, :, :, tb:])
+            if tb > lb:
+                e1 = assert_close_stored(to64(kv.k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], "bf16",
+                                         f"layer {layer} K seq {b}")
+                e2 = assert_close_stored(to64(kv.v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                                         "bf16", f"layer {layer} V seq {b}")
+                worst = (max(worst[0], e1[0], e2[0]), max(worst[1], e1[1], e2[1]))
+    print(f"[mxfp8 {name}] max abs {worst[0]:.3e} rel-RMS {worst[1]:.3e}", flush=True)
+
+
+def test_mxfp8_prefill_rows_sampled():
+    """The 4096-row prefill at full size; the oracle checks a sample of rows of
+    every layer (rows are independent: quantisation is per row)."""
+    case = make_ctxkv_case("P4", seed=0)
+    mx, pre, caches, _ = run_mx(case, seed=1)
+    rows = np.random.default_rng(1).choice(int(case.ctx_offsets[-1]), 48, replace=False)
+    cfg = case.cfg
+    empty = [oracle.OracleCache.from_arrays([np.zeros((cfg.n_kv_heads, 0, cfg.head_dim))] * len(rows),
+                                            [np.zeros((cfg.n_kv_heads, 0, cfg.head_dim))] * len(rows))
+             for _ in range(cfg.n_layers)]
+    ref = oracle.context_kv_precompute_mxfp8(cfg, MXW(case, mx), empty, case.context_states[rows],
+                                             np.arange(len(rows) + 1), case.positions[rows])
+    for layer, kv in enumerate(caches):
+        assert kv.lengths.tolist() == [4096]
+        for i, r in enumerate(rows):
+            assert_close_stored(to64(kv.k[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
+            assert_close_stored(to64(kv.v[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
+                                f"layer {layer} V row {r}")
+
+
+def test_mxfp8_rejections_leave_the_caches_alone():
+    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape, DFlashError, mxfp8_quantize
+    case = make_ctxkv_case("M1", seed=0)
+    mx = make_mxfp8_kv_weights(case.cfg, 0)
+    c = case.cfg
+    codes = torch.from_numpy(mx.w_kv_codes.reshape(-1, c.hidden)).cuda()
+    scales = torch.from_numpy(mx.w_kv_scales.reshape(-1, c.hidden // 32)).cuda()
+    f32 = ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, torch.float32, c.rope_theta, c.rms_eps,
+                         c.max_position)
+    with pytest.raises(DFlashError):
+        ContextKV(f32, dev(case.weights.hidden_norm, torch.float32), codes,
+                  dev(case.weights.k_norm, torch.float32), w_kv_scale=scales)
+    pre = make_mx_precompute(case, mx)
+    pre.set_append_mode("separate")
+    caches = make_caches(case)
+    before = [(raw_bits(k.k), k.lengths.copy()) for k in caches]
+    with pytest.raises(DFlashError):
+        pre.append(dev(case.context_states, torch.bfloat16), case.ctx_offsets,
+                   torch.from_numpy(case.positions.astype(np.int32)).cuda(), caches)
+    torch.cuda.synchronize()
+    for (bits, lens), kv in zip(before, caches):
+        np.testing.assert_array_equal(raw_bits(kv.k), bits)
+        assert kv.lengths.tolist() == lens.tolist()
+    with pytest.raises(DFlashError):
+        mxfp8_quantize(torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda"))
