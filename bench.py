@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "draft-block tokens/s + attention HBM GB/s (% of peak), B=32 ctx 512–8K"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_splitkv_c3_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", "attention.hip")
 
@@ -129,21 +130,23 @@ def cpu_baseline(case, n_seq: int, runs: int = 5):
                       f"{len(times)} runs of {t:.2f}s"}
 
 
-def bench_context_kv(steps: int, warmup: int, names=("P3", "P4")):
+def bench_context_kv(steps: int, warmup: int, names=("P3", "P4"), formats=("bf16", "mxfp8")):
     """The multi-layer context K/V precompute on its two workloads: P3 (the
     context rows of one C3 decode round, 3 layers) and P4 (a 4096-row prefill,
-    3 layers). Each run appends every layer's rows and the lengths are rewound
-    (host-only) before the next; the time is HIP events on the launch stream
-    around `steps` runs."""
+    3 layers), with bf16 weights and with MXFP8 weights (entries
+    "<name>_mxfp8"). Each run appends every layer's rows and the lengths are
+    rewound (host-only) before the next; the time is HIP events on the launch
+    stream around `steps` runs."""
     import numpy as np
     import torch
 
     from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape, KVCache
-    from workload import make_ctxkv_case
+    from workload import make_ctxkv_case, make_mxfp8_kv_weights
 
     res = {}
-    for name in names:
+    for name, fmt in [(n, f) for n in names for f in formats]:
         case = make_ctxkv_case(name, seed=0)
+        mx = fmt == "mxfp8"
         c = case.cfg
         dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
 
@@ -151,9 +154,15 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4")):
             return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
 
         w = case.weights
-        pre = ContextKV(ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt, c.rope_theta,
-                                       c.rms_eps, c.max_position),
-                        dev(w.hidden_norm), dev(w.w_kv.reshape(-1, c.hidden)), dev(w.k_norm))
+        shape = ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt, c.rope_theta, c.rms_eps,
+                               c.max_position)
+        if mx:
+            mw = make_mxfp8_kv_weights(c, 0)
+            pre = ContextKV(shape, dev(w.hidden_norm), torch.from_numpy(mw.w_kv_codes.reshape(-1, c.hidden)).cuda(),
+                            dev(w.k_norm),
+                            w_kv_scale=torch.from_numpy(mw.w_kv_scales.reshape(-1, c.hidden // 32)).cuda())
+        else:
+            pre = ContextKV(shape, dev(w.hidden_norm), dev(w.w_kv.reshape(-1, c.hidden)), dev(w.k_norm))
         caches = []
         for layer in range(c.n_layers):
             kv = KVCache(case.batch, c.n_kv_heads, c.head_dim, case.capacity(), dt)
@@ -186,16 +195,18 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4")):
         n_out = c.n_layers * 2 * c.n_kv_heads * c.head_dim
         flops = 2.0 * rows * n_out * c.hidden
         es = 2 if c.dtype == "bf16" else 4
-        weight_bytes = n_out * c.hidden * es
+        weight_bytes = n_out * c.hidden * es if not mx else n_out * c.hidden * 33 // 32   # codes + scales
         io_bytes = rows * c.hidden * es + rows * n_out * es   # states in, K/V rows out
-        res[name] = {
+        peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+        res[name + ("_mxfp8" if mx else "")] = {
             "workload": (f"{name}: {case.batch} sequence(s), {rows} context rows, {c.n_layers} layers, "
-                         f"H={c.hidden}, {c.n_kv_heads} KV heads, head_dim {c.head_dim}, {c.dtype}"),
+                         f"H={c.hidden}, {c.n_kv_heads} KV heads, head_dim {c.head_dim}, {c.dtype}"
+                         + (", MXFP8 weights and activations" if mx else "")),
             "us_per_run": round(us, 2),
             "context_rows_per_s": round(rows / (us * 1e-6), 1),
             "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "hbm_gbs": round((weight_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
-            "floor_us": {"mfma": round(flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+            "floor_us": {"mfma": round(flops / (peak * 1e12) * 1e6, 2),
                          "hbm": round((weight_bytes + io_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
         }
         pre.close()

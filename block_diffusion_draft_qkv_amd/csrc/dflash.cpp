@@ -66,7 +66,7 @@ struct dflash_ctxkv {
   dflash_ctxkv_config cfg;
   dflash_ctxkv_weights w;      // with mx, w.w_kv holds E4M3 codes
   bool mx = false;             // MXFP8 weights (dflash_ctxkv_create_mxfp8)
-  const uint8_t* w_scale = nullptr;
+  uint8_t* w_scale = nullptr;  // their scales, repacked step-major (owned)
   int num_cus = 256;
   int append_mode = DFLASH_APPEND_AUTO;
   float* cos_sin = nullptr;
@@ -600,16 +600,22 @@ int ctxkv_create_impl(const dflash_ctxkv_config* cfg, const dflash_ctxkv_weights
   h->cfg = *cfg;
   h->w = *weights;
   h->mx = mx;
-  h->w_scale = w_scale;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) { delete h; return DFLASH_ERR_HIP; }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
     h->num_cus = cus;
-  if (!upload_rope_table(cfg->max_position, cfg->head_dim, cfg->rope_theta, &h->cos_sin) ||
-      hipMalloc(&h->err, sizeof(int32_t)) != hipSuccess ||
-      hipMemset(h->err, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  // MXFP8: the weight scales [N][H / 32] repacked step-major for the GEMM's
+  // scale loads (the caller's array is only read here).
+  const int64_t n_rows = (int64_t)cfg->n_layers * 2 * cfg->n_kv_heads * cfg->head_dim;
+  bool ok = upload_rope_table(cfg->max_position, cfg->head_dim, cfg->rope_theta, &h->cos_sin) &&
+            hipMalloc(&h->err, sizeof(int32_t)) == hipSuccess && hipMemset(h->err, 0, sizeof(int32_t)) == hipSuccess;
+  if (ok && mx)
+    ok = hipMalloc(&h->w_scale, (size_t)n_rows * cfg->hidden / 32) == hipSuccess &&
+         launch_scales_step_major(w_scale, h->w_scale, (int)n_rows, cfg->hidden, nullptr) == hipSuccess;
+  if (!ok || hipDeviceSynchronize() != hipSuccess) {
     if (h->cos_sin) hipFree(h->cos_sin);
     if (h->err) hipFree(h->err);
+    if (h->w_scale) hipFree(h->w_scale);
     delete h;
     return DFLASH_ERR_HIP;
   }
@@ -639,7 +645,7 @@ int dflash_mxfp8_quantize(const void* x, int64_t rows, int32_t cols, void* codes
   if (!x || !codes || !scales) return DFLASH_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 16) return DFLASH_ERR_ARG;
   if (launch_rms_rows_mx(x, nullptr, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), (int)rows, cols,
-                         0.f, static_cast<hipStream_t>(stream)) != hipSuccess)
+                         0.f, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DFLASH_ERR_HIP;
   return DFLASH_OK;
 }
@@ -649,6 +655,7 @@ void dflash_ctxkv_destroy(dflash_ctxkv* h) {
   hipDeviceSynchronize();
   hipFree(h->cos_sin);
   hipFree(h->err);
+  if (h->w_scale) hipFree(h->w_scale);
   delete h;
 }
 
@@ -716,7 +723,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   // hidden_norm over each raw context row (as MXFP8 rows for MXFP8 weights)
   if (h->mx) {
     if (launch_rms_rows_mx(context_states, h->w.hidden_norm, static_cast<uint8_t*>(normed),
-                           reinterpret_cast<uint8_t*>(ws + wc.scales), (int)Mc, H, (float)c.rms_eps, s) != hipSuccess)
+                           reinterpret_cast<uint8_t*>(ws + wc.scales), (int)Mc, H, (float)c.rms_eps, (int)Mc,
+                           s) != hipSuccess)
       return DFLASH_ERR_HIP;
   } else if (launch_rms_rows(c.dtype, context_states, nullptr, h->w.hidden_norm, nullptr, normed, (int)Mc, H,
                              (float)c.rms_eps, s) != hipSuccess) {

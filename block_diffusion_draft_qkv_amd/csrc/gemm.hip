@@ -222,7 +222,9 @@ __device__ __forceinline__ bool gemm_core(const TileJob& J, uint32_t lds0, int e
 // bf16 step, plus 4 scale bytes per row (the step's four blocks), which the
 // producers stream into the stage behind the data with 256-byte LDS-DMA
 // loads (64 rows each; the (BM + BN) / 64 of a step alternate between the two
-// producers, so their per-step block counts may differ by one).
+// producers, so their per-step block counts may differ by one). The scales
+// are stored step-major, so a load reads 256 contiguous bytes; row-major
+// scales put every lane on a cache line of its own.
 template <int BM, int BN> struct GemmShapeMX {
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int AS_OFF = A_BYTES + B_BYTES, BS_OFF = AS_OFF + BM * 4, STAGE = BS_OFF + BN * 4;
@@ -256,7 +258,6 @@ __device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, in
   const int m0 = J.m0, n0 = J.n0, nk = J.nk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kbs = P.k / 32;  // scale bytes per row
 
   if (wave >= kGemmConsumers) {
     // ---------------------------------------------------------- producers
@@ -289,7 +290,7 @@ __device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, in
         gr = n0 + 64 * (u - ASL) + lane;
         gr = gr < P.n ? gr : P.n - 1;
       }
-      soff[i] = (uint32_t)gr * (uint32_t)kbs;
+      soff[i] = (uint32_t)gr * 4u;
     }
     const char* Ab = static_cast<const char*>(P.a);
     const char* Bb = static_cast<const char*>(P.b);
@@ -304,8 +305,8 @@ __device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, in
 #pragma unroll
       for (int i = 0; i < BPP; ++i)
         lds_dma16(boff[i], bb, sl + A_BYTES + (uint32_t)(i * kGemmProducers + pw) * 1024u);
-      const void* sab = uniform_ptr(P.sa + (size_t)step * 4);
-      const void* sbb = uniform_ptr(P.sb + (size_t)step * 4);
+      const void* sab = uniform_ptr(P.sa + (size_t)step * P.m * 4);
+      const void* sbb = uniform_ptr(P.sb + (size_t)step * P.n * 4);
 #pragma unroll
       for (int i = 0; i < (SL + 1) / 2; ++i) {
         const int u = 2 * i + pw;

@@ -30,7 +30,7 @@ struct GemmProblem {
   int32_t b_pair = 0;
   // MXFP8 operands (gemm_append with the MX flag): a and b hold E4M3 codes
   // ([m][lda], [n][ldb] bytes) and sa / sb their E8M0 scales, one byte per 32
-  // consecutive k, rows of k / 32 bytes.
+  // consecutive k, step-major: [k / 128][m or n rows][4 bytes].
   const uint8_t* sa = nullptr;
   const uint8_t* sb = nullptr;
 };
@@ -136,9 +136,12 @@ hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormR
                                  int bm, hipStream_t stream);
 // MXFP8 rows of bf16 x [rows][h] (h % 128 == 0): with g, hidden_norm first
 // (x / sqrt(mean(x^2) + eps) * g rounded to bf16), without g x itself; codes
-// [rows][h] E4M3 bytes and scales [rows][h / 32] E8M0 bytes.
+// [rows][h] E4M3 bytes and scales [rows][h / 32] E8M0 bytes, or step-major
+// [h / 128][step_rows][4] when step_rows > 0 (step_rows >= rows).
 hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
-                              float eps, hipStream_t stream);
+                              float eps, int step_rows, hipStream_t stream);
+// E8M0 scales [n][k / 32] (4-byte aligned) -> step-major [k / 128][n][4].
+hipError_t launch_scales_step_major(const void* src, void* dst, int n, int k, hipStream_t stream);
 hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,
                               int total_tiles, int bm, hipStream_t stream);
 

@@ -103,24 +103,6 @@ __global__ __launch_bounds__(256) void rms_rows_kernel(const T* __restrict__ x, 
   for (int c = tid + kChunks * 256; c < nchunk; c += 256) put(c, hrow ? hrow[c] : row[c]);
 }
 
-// E4M3 code of t with |t| <= 448 (OCP FP8: bias 7, 3 mantissa bits,
-// subnormals m * 2^-9): round to nearest, ties to even, sign kept for zero.
-__device__ inline uint32_t e4m3_code(float t) {
-  const uint32_t bits = __float_as_uint(t);
-  const float a = fabsf(t);
-  uint32_t code;
-  if (a < 0x1p-6f) {
-    code = (uint32_t)rintf(a * 0x1p9f);  // 0 .. 8 (8 is the smallest normal, 0x08)
-  } else {
-    int e = (int)((bits >> 23) & 0xff) - 127;                      // a in [2^e, 2^(e+1))
-    const float frac = (__uint_as_float((bits & 0x007fffffu) | 0x3f800000u) - 1.0f) * 8.0f;
-    uint32_t m = (uint32_t)rintf(frac);                            // exact product, RNE
-    if (m == 8) { m = 0; ++e; }
-    code = ((uint32_t)(e + 7) << 3) | m;
-  }
-  return code | ((bits >> 24) & 0x80u);
-}
-
 // MXFP8 quantisation of bf16 rows (OCP MX: one E8M0 scale per 32 consecutive
 // elements, E4M3 elements), optionally after the hidden_norm: the input of the
 // block-scaled context K/V projection (vLLM page "qwen3_dflash",
@@ -128,37 +110,57 @@ __device__ inline uint32_t e4m3_code(float t) {
 // activation dtype first, _normalize_context_states). Per block: amax, shared
 // exponent floor(log2 amax) - 8 clamped to [-127, 127] (scale byte =
 // biased exponent of amax - 8, clamped to [0, 254]), elements x / 2^exponent
-// saturated to +-448 and rounded to nearest even. A block is four consecutive
-// threads' 16-byte chunks; amax is reduced over those four lanes.
+// (exact: a power of two) clamped to +-448 and converted by gfx950's packed
+// FP8 conversion (OCP E4M3, round to nearest even, sign kept for zero; the
+// clamp makes it saturate). The conversion does in one instruction per two
+// elements what an integer encoding took some fifteen for: the kernel is
+// bound by its vector ALU work otherwise.
+//
+// One 256-thread work-group per row (rows are few in a decode round, so each
+// needs many lanes), the row kept in registers (hidden <= 8192); thread t
+// holds chunks t + 256 k of 8 elements, and a 32-element block is the chunks
+// of four consecutive threads, whose amax is reduced over those lanes. Scales
+// go out row-major [rows][h / 32], or, with step_rows > 0, step-major
+// [h / 128][step_rows][4] (a row's four blocks of a 128-wide k step together,
+// the rows of one step contiguous), the layout the MXFP8 GEMM streams.
 __global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restrict__ x,
                                                           const __bf16* __restrict__ g,
                                                           uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales, int h, float eps) {
+                                                          uint8_t* __restrict__ scales, int h, float eps,
+                                                          int step_rows) {
   constexpr int V = 8;
   __shared__ float part[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nchunk = h / V;  // a multiple of 16: blocks never straddle threads of two passes
+  const int nchunk = h / V;  // a multiple of 16: a block's four chunks are in one pass
   const size_t roff = (size_t)blockIdx.x * h;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + roff);
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
+  uint2* out = reinterpret_cast<uint2*>(codes + roff);
+  u32x4 keep[kChunks];
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int c = tid + k * 256;
+    if (c < nchunk) keep[k] = row[c];
+  }
   float inv = 1.f;
   if (g != nullptr) {
     float ss = 0.f;
-    for (int c = tid; c < nchunk; c += 256) {
-      const u32x4 v = row[c];
+    auto sq = [&](const u32x4& v) {
       const __bf16* e = reinterpret_cast<const __bf16*>(&v);
 #pragma unroll
       for (int i = 0; i < V; ++i) ss += (float)e[i] * (float)e[i];
-    }
+    };
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k)
+      if (tid + k * 256 < nchunk) sq(keep[k]);
+    for (int c = tid + kChunks * 256; c < nchunk; c += 256) sq(row[c]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
     if (lane == 0) part[wave] = ss;
     __syncthreads();
     inv = rsqrtf((part[0] + part[1] + part[2] + part[3]) / (float)h + eps);
   }
-  uint2* out = reinterpret_cast<uint2*>(codes + roff);
-  for (int c = tid; c < nchunk; c += 256) {  // the row is re-read from L2 after the norm
-    const u32x4 v = row[c];
+  auto put = [&](int c, const u32x4& v) {
     const __bf16* e = reinterpret_cast<const __bf16*>(&v);
     float y[V];
     if (g != nullptr) {
@@ -178,26 +180,55 @@ __global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restri
     const int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
     const int sbyte = min(max(ef - 8, 0), 254);
     const float mul = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-(sbyte - 127), normal
-    uint2 packed = {0u, 0u};
+    float t[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const float t = fminf(fmaxf(y[i] * mul, -448.f), 448.f);
-      const uint32_t cd = e4m3_code(t);
-      if (i < 4) packed.x |= cd << (8 * i);
-      else packed.y |= cd << (8 * (i - 4));
-    }
+    for (int i = 0; i < V; ++i) t[i] = fminf(fmaxf(y[i] * mul, -448.f), 448.f);
+    uint2 packed;
+    packed.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    packed.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], (int)packed.x, true);
+    packed.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false);
+    packed.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], (int)packed.y, true);
     out[c] = packed;
-    if ((tid & 3) == 0) scales[(size_t)blockIdx.x * (h / 32) + c / 4] = (uint8_t)sbyte;
+    if ((tid & 3) == 0) {
+      const size_t at = step_rows > 0 ? ((size_t)(c / 16) * step_rows + blockIdx.x) * 4 + (c / 4) % 4
+                                      : (size_t)blockIdx.x * (h / 32) + c / 4;
+      scales[at] = (uint8_t)sbyte;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int c = tid + k * 256;
+    if (c < nchunk) put(c, keep[k]);
   }
+  for (int c = tid + kChunks * 256; c < nchunk; c += 256) put(c, row[c]);  // longer rows: from L2
+}
+
+// Row-major E8M0 scales [n][k / 32] -> step-major [k / 128][n][4]: one
+// thread per (row, step) moves the step's four bytes.
+__global__ __launch_bounds__(256) void scales_step_major_kernel(const uint32_t* __restrict__ src,
+                                                                uint32_t* __restrict__ dst, int n, int steps) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // i = row * steps + step
+  if (i >= (int64_t)n * steps) return;
+  const int64_t row = i / steps, step = i % steps;
+  dst[step * n + row] = src[i];
 }
 
 }  // namespace
 
 hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
-                              float eps, hipStream_t stream) {
+                              float eps, int step_rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rms_rows_mx_kernel, dim3(rows), dim3(256), 0, stream, static_cast<const __bf16*>(x),
-                     static_cast<const __bf16*>(g), codes, scales, h, eps);
+                     static_cast<const __bf16*>(g), codes, scales, h, eps, step_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_scales_step_major(const void* src, void* dst, int n, int k, hipStream_t stream) {
+  const int steps = k / 128;
+  const int64_t total = (int64_t)n * steps;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scales_step_major_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), n, steps);
   return hipGetLastError();
 }
 

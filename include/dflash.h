@@ -28,7 +28,7 @@
  *   - Device pointers are borrowed: the caller allocates and frees every buffer
  *     passed in and keeps weights alive for the layer's lifetime. The library
  *     allocates only each handle's own cos/sin table and error flag (at
- *     create).
+ *     create), and an MXFP8 precompute handle its repacked weight scales.
  *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream) and the calls return without synchronising,
  *     except dflash_layer_poll_error, dflash_layer_kernel_times and
@@ -272,8 +272,11 @@ typedef struct {
  * scales belong to output rows). The format is OCP Microscaling MXFP8: FP8
  * E4M3 elements (bias 7, 3 mantissa bits, largest 448, S.1111.111 NaN) and
  * one E8M0 scale byte (2^(s - 127)) per 32 consecutive elements along hidden.
- * Borrowed device pointers; the config dtype must be DFLASH_BF16 (states,
- * gains and caches) and hidden a multiple of 128. */
+ * Borrowed device pointers, except w_kv_scale, which create only reads: it
+ * repacks the scales into a buffer of its own ([H / 128][rows][4], so that
+ * the GEMM reads a k step's scales of consecutive rows contiguously;
+ * L * 2 * nkv * d * H / 32 bytes, freed by destroy). The config dtype must be
+ * DFLASH_BF16 (states, gains and caches) and hidden a multiple of 128. */
 typedef struct {
     const void* hidden_norm;  /* [H] bf16, 16-byte aligned                        */
     const void* w_kv;         /* [L * 2 * nkv * d, H] E4M3 bytes, rows ordered as
