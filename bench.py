@@ -361,16 +361,14 @@ def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     # work included), so every round has C3's lengths and reserves its blocks
     # anew.
     c = caches[0]
-    for b in range(B):
-        c.crop(b, int(L0[b]))
+    c.crop_all(L0)
     rng = np.random.default_rng(seed + 7)
     accepts = rng.integers(0, bs + 1, size=(steps, B))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(steps):
         run_round(layer, c, hs, th, offs, accepts[r], out=out)
-        for b in range(B):
-            c.crop(b, int(L0[b]))
+        c.crop_all(L0)
     torch.cuda.synchronize()
     t_round = (time.perf_counter() - t0) / steps
     res = {

@@ -90,6 +90,14 @@ class KVCache:
     def crop(self, seq: int, new_len: int) -> None:
         check(_lib.lib().dflash_cache_crop(C.byref(self.desc), int(seq), int(new_len)), "dflash_cache_crop")
 
+    def crop_all(self, new_lengths) -> None:
+        """Crop every sequence at once (all checked before any changes)."""
+        arr = np.ascontiguousarray(new_lengths, dtype=np.int32)
+        if arr.shape != (self.batch,):
+            raise ValueError("one length per sequence")
+        check(_lib.lib().dflash_cache_crop_all(C.byref(self.desc), arr.ctypes.data_as(C.POINTER(C.c_int32))),
+              "dflash_cache_crop_all")
+
 
 class DFlashLayer:
     """One DFlash draft-attention layer over borrowed device weights.
@@ -396,6 +404,37 @@ def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float, out: Optional[torc
     return out
 
 
+class _PinnedUploads:
+    """Stream-ordered host-to-device copies of small int32 arrays through a
+    ring of pinned staging buffers. A copy from pageable memory would block the
+    host until the device caught up; here a buffer is only refilled once the
+    copy that last read it has completed (its event), so the host can enqueue
+    ahead of the device."""
+
+    def __init__(self, capacity: int, depth: int = 4):
+        self.capacity = int(capacity)
+        self._bufs = [torch.empty(self.capacity, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
+        self._events = [None] * depth
+        self._i = 0
+
+    def upload(self, src: np.ndarray, dst: torch.Tensor, stream=None) -> None:
+        src = np.ascontiguousarray(src, dtype=np.int32).reshape(-1)
+        if src.size > self.capacity or dst.numel() < src.size or dst.dtype != torch.int32:
+            raise ValueError("upload does not fit its staging buffer or destination")
+        i = self._i
+        self._i = (i + 1) % len(self._bufs)
+        if self._events[i] is not None:
+            self._events[i].synchronize()
+        buf = self._bufs[i][: src.size]
+        buf.numpy()[:] = src
+        s = torch.cuda.current_stream(dst.device) if stream is None else stream
+        with torch.cuda.stream(s):
+            dst.view(-1)[: src.size].copy_(buf, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(s)
+        self._events[i] = ev
+
+
 class PagedKVCache:
     """Draft KV cache of ``batch`` sequences in 64-row blocks (the paged layout
     of include/dflash.h): pools ``k [num_blocks, n_kv, 64, d]`` and ``v
@@ -424,6 +463,7 @@ class PagedKVCache:
                                      batch, self.capacity, self.table.data_ptr(),
                                      C.cast(self._tab, C.POINTER(C.c_int32)), max_blocks, num_blocks)
         self._dirty = False
+        self._uploads: Optional[_PinnedUploads] = None
 
     # ------------------------------------------------------------ blocks
     def blocks_of(self, seq: int) -> int:
@@ -448,10 +488,62 @@ class PagedKVCache:
             self.table_host[seq, i] = -1
             self._dirty = True
 
-    def sync(self) -> None:
-        """Copy the host table to the device table (stream-ordered before later steps)."""
+    def reserve_all(self, rows) -> None:
+        """``reserve`` for every sequence at once: back logical rows
+        [0, rows[b]) of each sequence b, taking blocks off the free list in the
+        order the per-sequence calls would (sequence 0 first)."""
+        rows = np.asarray(rows, dtype=np.int64)
+        need = -(-rows // self.BLOCK)
+        if (need > self.max_blocks).any():
+            raise ValueError(f"a sequence needs more than max_blocks {self.max_blocks} blocks")
+        have = np.count_nonzero(self.table_host >= 0, axis=1)
+        new = np.maximum(need - have, 0)
+        total = int(new.sum())
+        if total == 0:
+            return
+        if total > len(self.free):
+            raise MemoryError("no free cache block")
+        taken = np.asarray(self.free[-total:][::-1], dtype=np.int32)
+        del self.free[-total:]
+        seq = np.repeat(np.arange(self.batch), new)
+        first = np.repeat(np.cumsum(new) - new, new)
+        self.table_host[seq, have[seq] + np.arange(total) - first] = taken
+        self._dirty = True
+
+    def release_all(self, rows) -> None:
+        """``release`` for every sequence at once (blocks past logical row
+        rows[b] go back to the free list in the per-sequence calls' order)."""
+        keep = -(-np.asarray(rows, dtype=np.int64) // self.BLOCK)
+        cols = np.arange(self.max_blocks)
+        drop = (cols[None, :] >= keep[:, None]) & (self.table_host >= 0)
+        if not drop.any():
+            return
+        # sequence by sequence, last block first
+        self.free.extend(self.table_host[:, ::-1][drop[:, ::-1]].tolist())
+        self.table_host[drop] = -1
+        self._dirty = True
+
+    def crop_all(self, new_lengths) -> None:
+        """Crop every sequence at once (all checked before any changes) and
+        release the blocks the crops drop."""
+        arr = np.ascontiguousarray(new_lengths, dtype=np.int32)
+        if arr.shape != (self.batch,):
+            raise ValueError("one length per sequence")
+        check(_lib.lib().dflash_cache_crop_all(C.byref(self.desc), arr.ctypes.data_as(C.POINTER(C.c_int32))),
+              "dflash_cache_crop_all")
+        self.release_all(arr)
+
+    def sync(self, stream=None) -> None:
+        """Copy the host table to the device table, asynchronously and
+        stream-ordered before the steps enqueued after it (a pinned staging
+        copy of the table is taken now, so the host table may change at once)."""
         if self._dirty:
-            self.table.copy_(torch.from_numpy(self.table_host.copy()))
+            if self.table.device.type != "cuda":  # a host-resident cache (block accounting only)
+                self.table.copy_(torch.from_numpy(self.table_host))
+            else:
+                if self._uploads is None:
+                    self._uploads = _PinnedUploads(self.table_host.size)
+                self._uploads.upload(self.table_host, self.table, stream)
             self._dirty = False
 
     # ------------------------------------------------------------ rows
@@ -499,16 +591,24 @@ def run_round(model, cache, hidden_states: torch.Tensor, target_hidden: Optional
     B, bs = cache.batch, model.shape.block_size
     L = cache.lengths.astype(np.int64).copy()
     n = np.diff(np.asarray(ctx_offsets, dtype=np.int64))
+    acc = np.asarray(accept, dtype=np.int64)
+    if acc.shape != (B,) or (acc < 0).any() or (acc > bs).any():
+        raise ValueError("accepted counts: one per sequence, each in [0, block_size]")
     if isinstance(cache, PagedKVCache):
-        for b in range(B):
-            cache.reserve(b, int(L[b] + n[b] + bs))
-        cache.sync()
-    pos = np.concatenate([np.arange(L[b], L[b] + n[b] + bs) for b in range(B)]).astype(np.int32)
-    pos_d = torch.from_numpy(pos).to(hidden_states.device)
+        cache.reserve_all(L + n + bs)
+        cache.sync(stream)
+    cnt = n + bs  # positions L_b .. L_b + n_b + bs - 1 of every sequence
+    pos = (np.repeat(L, cnt) + np.arange(int(cnt.sum())) - np.repeat(np.cumsum(cnt) - cnt, cnt)).astype(np.int32)
+    # positions go up through a pinned ring kept on the cache, so the round
+    # never waits for the device
+    ring = getattr(cache, "_pos_uploads", None)
+    if ring is None or ring.capacity < pos.size:
+        ring = _PinnedUploads(max(pos.size, 4096))
+        cache._pos_uploads = ring
+    pos_d = torch.empty(pos.size, dtype=torch.int32, device=hidden_states.device)
+    if stream is not None:
+        pos_d.record_stream(stream)
+    ring.upload(pos, pos_d, stream)
     out = model.step(hidden_states, target_hidden, ctx_offsets, pos_d, cache, out=out, stream=stream)
-    for b in range(B):
-        a = int(accept[b])
-        if not 0 <= a <= bs:
-            raise ValueError("accepted count outside [0, block_size]")
-        cache.crop(b, int(L[b] + n[b] + a))
+    cache.crop_all(L + n + acc)
     return out

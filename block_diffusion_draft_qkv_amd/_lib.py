@@ -34,7 +34,7 @@ EXPORTS = (
     "dflash_layer_set_append_mode",
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
     "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
-    "dflash_ctxkv_create_mxfp8", "dflash_mxfp8_quantize",
+    "dflash_ctxkv_create_mxfp8", "dflash_mxfp8_quantize", "dflash_cache_crop_all",
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
 )
@@ -127,6 +127,8 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_create_mxfp8.restype = C.c_int
         h.dflash_mxfp8_quantize.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
         h.dflash_mxfp8_quantize.restype = C.c_int
+        h.dflash_cache_crop_all.argtypes = [C.POINTER(KVCacheDesc), C.POINTER(C.c_int32)]
+        h.dflash_cache_crop_all.restype = C.c_int
         h.dflash_ctxkv_destroy.argtypes = [C.c_void_p]
         h.dflash_ctxkv_destroy.restype = None
         h.dflash_ctxkv_workspace_bytes.argtypes = [C.c_void_p, C.c_int64]

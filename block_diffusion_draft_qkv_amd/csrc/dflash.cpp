@@ -526,6 +526,14 @@ int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len) {
   return DFLASH_OK;
 }
 
+int dflash_cache_crop_all(dflash_kv_cache* cache, const int32_t* new_len) {
+  if (!cache || !cache->len || !new_len || cache->batch < 0) return DFLASH_ERR_ARG;
+  for (int b = 0; b < cache->batch; ++b)
+    if (new_len[b] < 0 || new_len[b] > cache->len[b]) return DFLASH_ERR_RANGE;
+  for (int b = 0; b < cache->batch; ++b) cache->len[b] = new_len[b];
+  return DFLASH_OK;
+}
+
 int dflash_layer_poll_error(dflash_layer* L, void* stream) {
   if (!L) return DFLASH_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -191,6 +191,13 @@ int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
  * DFLASH_ERR_RANGE (new_len outside [0, len[seq]]: crop never grows). */
 int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len);
 
+/* dflash_cache_crop for every sequence at once (one draft round's accepted
+ * prefixes): new_len is a HOST array of cache->batch lengths. Every entry is
+ * checked before any length changes, so an error leaves them all as they were.
+ * Errors: DFLASH_ERR_ARG (null pointer), DFLASH_ERR_RANGE (an entry outside
+ * [0, len[b]]). */
+int dflash_cache_crop_all(dflash_kv_cache* cache, const int32_t* new_len);
+
 /* Synchronise `stream`, then return and clear the layer's sticky device-side
  * error (DFLASH_ERR_RANGE if a position fell outside the table since the last
  * poll), or DFLASH_OK. */

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from block_diffusion_draft_qkv_amd import PagedKVCache
+from block_diffusion_draft_qkv_amd import DFlashError, PagedKVCache
 
 
 def test_prefix_scatter_gather_roundtrip_and_block_accounting():
@@ -50,3 +50,41 @@ def test_reserve_release_and_limits():
     assert c.blocks_of(0) == 0 and len(c.free) == 3
     c.sync()
     assert torch.equal(c.table, torch.from_numpy(c.table_host))
+
+
+def test_batched_reserve_and_crop_match_the_per_sequence_calls():
+    """reserve_all / crop_all (one C call for every crop) leave the same table,
+    free list and lengths as the per-sequence reserve / crop, round after round."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    B = 6
+    a = PagedKVCache(B, 2, 16, 200, 12, torch.float32, device="cpu")
+    b = PagedKVCache(B, 2, 16, 200, 12, torch.float32, device="cpu")
+    order = list(range(200))
+    rng.shuffle(order)
+    a.free, b.free = list(order), list(order)
+    lens = rng.integers(0, 300, B)
+    a.set_lengths(lens)
+    b.set_lengths(lens)
+    for _ in range(25):
+        grow = a.lengths.astype(np.int64) + rng.integers(0, 90, B)
+        for s in range(B):
+            a.reserve(s, int(grow[s]))
+        b.reserve_all(grow)
+        assert np.array_equal(a.table_host, b.table_host) and a.free == b.free
+        a.set_lengths(grow)
+        b.set_lengths(grow)
+        new = (grow * rng.uniform(0.2, 1.0, B)).astype(np.int64)
+        for s in range(B):
+            a.crop(s, int(new[s]))
+        b.crop_all(new)
+        assert np.array_equal(a.table_host, b.table_host) and a.free == b.free
+        assert a.lengths.tolist() == b.lengths.tolist() == new.tolist()
+    # a crop that would grow one sequence changes nothing
+    bad = b.lengths.astype(np.int64).copy()
+    bad[2] += 1
+    before = (b.table_host.copy(), list(b.free), b.lengths.copy())
+    with pytest.raises(DFlashError):
+        b.crop_all(bad)
+    assert np.array_equal(b.table_host, before[0]) and b.free == before[1]
+    assert b.lengths.tolist() == before[2].tolist()
