@@ -25,6 +25,7 @@ from .mxfp8 import (  # noqa: F401
     e4m3_encode,
     e4m3_value,
     e8m0_value,
+    layer_step_mxfp8,
     mx_dequantize,
     mx_quantize,
     mxfp8_linear,

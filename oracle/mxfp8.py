@@ -36,6 +36,12 @@ Readings taken where the pages are silent:
   states' dtype before the projection.
 * The block products are exact, and this oracle sums them exactly enough
   (float64).
+* In that configuration the layer's own projections are MXFP8 too (the
+  precompute takes the MXFP8 path exactly when every layer's ``qkv_proj`` is
+  an MXFP8 linear; ``o_proj`` is taken to be one as well). The draft block's
+  rows and the new context rows (bf16 activations) are quantised once for the
+  fused q|k|v projection. The attention output, which the model holds in
+  bf16, is rounded to bf16 and quantised for ``o_proj``.
 """
 from __future__ import annotations
 
@@ -43,8 +49,10 @@ from typing import List, Sequence
 
 import numpy as np
 
+from types import SimpleNamespace
+
 from .context_kv import append_layer_kv
-from .ref_fp64 import OracleCache, _f64, linear, rms_norm
+from .ref_fp64 import OracleCache, _f64, layer_step, linear, rms_norm
 
 E4M3_MAX = 448.0
 E4M3_EMAX = 8          # exponent of the largest binade (448 = 1.75 * 2^8)
@@ -152,3 +160,25 @@ def context_kv_precompute_mxfp8(cfg, weights, caches: Sequence[OracleCache], con
                             linear(xq, mx_dequantize(weights.w_kv_codes[layer], weights.w_kv_scales[layer])),
                             weights.k_norm[layer], ctx_offsets, positions)
             for layer in range(Ln)]
+
+
+def _mx_rows(x):
+    """Rows as the MXFP8 linear sees them: quantised, then decoded."""
+    c, sc = mx_quantize(x)
+    return mx_dequantize(c, sc)
+
+
+def layer_step_mxfp8(cfg, weights, cache: OracleCache, hidden_states, target_hidden, ctx_offsets, positions):
+    """``layer_step`` with MXFP8 projections. ``weights`` has ``w_qkv_codes
+    [(nq+2nkv)*d, H]`` and ``w_qkv_scales [.., H/32]`` (rows q | k | v),
+    ``w_o_codes [H, nq*d]`` and ``w_o_scales [H, nq*d/32]`` (uint8), and
+    ``q_norm, k_norm [d]``."""
+    H, nq, nkv, d = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    wqkv = mx_dequantize(weights.w_qkv_codes, weights.w_qkv_scales)
+    plain = SimpleNamespace(w_q=wqkv[:nq * d], w_k=wqkv[nq * d:(nq + nkv) * d], w_v=wqkv[(nq + nkv) * d:],
+                            w_o=mx_dequantize(weights.w_o_codes, weights.w_o_scales),
+                            q_norm=weights.q_norm, k_norm=weights.k_norm)
+    X = _mx_rows(_f64(hidden_states).reshape(-1, H))
+    C = _mx_rows(_f64(target_hidden).reshape(-1, H)) if target_hidden is not None else None
+    return layer_step(cfg, plain, cache, X, C, ctx_offsets, positions,
+                      o_input=lambda o: _mx_rows(round_bf16(o)))

@@ -168,7 +168,7 @@ def crop(cache: OracleCache, seq: int, new_len: int) -> OracleCache:
 
 
 def layer_step(cfg, weights, cache: OracleCache, hidden_states, target_hidden,
-               ctx_offsets, positions):
+               ctx_offsets, positions, o_input=None):
     """One draft-attention layer step for a batch of sequences.
 
     ``cfg`` has ``hidden, n_q_heads, n_kv_heads, head_dim, block_size,
@@ -181,7 +181,9 @@ def layer_step(cfg, weights, cache: OracleCache, hidden_states, target_hidden,
     its window ``[new context | block]`` (``n_b + bs`` entries).
 
     Returns ``(out [B*bs, H], new_cache)``; the new cache has every new context
-    and block row appended (post-norm post-RoPE K, raw V)."""
+    and block row appended (post-norm post-RoPE K, raw V). ``o_input``, if
+    given, maps the attention output rows ``[bs, nq*d]`` to what ``o_proj``
+    multiplies (the identity when absent)."""
     H = cfg.hidden
     nq, nkv, d, bs = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
     if nq % nkv:
@@ -220,6 +222,7 @@ def layer_step(cfg, weights, cache: OracleCache, hidden_states, target_hidden,
         V = np.concatenate([new.v[b], v_new], axis=1)
         keep = window_keep(bs, K.shape[1], cfg.sliding_window)
         o = attention(q, K, V, keep, scaling)           # [nq, bs, d]
-        out[b * bs:(b + 1) * bs] = linear(o.transpose(1, 0, 2).reshape(bs, nq * d), weights.w_o)
+        o_rows = o.transpose(1, 0, 2).reshape(bs, nq * d)
+        out[b * bs:(b + 1) * bs] = linear(o_rows if o_input is None else o_input(o_rows), weights.w_o)
         new.k[b], new.v[b] = K, V
     return out, new

@@ -51,8 +51,9 @@ def rand_inputs(cfg, rng, lens, news):
 
 # ---------------------------------------------------------------- brute force
 
-def brute_step(cfg, w, cache, X, C, offs, pos):
-    """The whole layer step in pure-Python loops and the math module only."""
+def brute_step(cfg, w, cache, X, C, offs, pos, o_in=None):
+    """The whole layer step in pure-Python loops and the math module only
+    (``o_in``, if given, maps each attention output row before o_proj)."""
     H, nq, nkv, d, bs = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
     g, half, W = nq // nkv, d // 2, cfg.sliding_window
     B = len(offs) - 1
@@ -104,7 +105,7 @@ def brute_step(cfg, w, cache, X, C, offs, pos):
                 z = sum(e)
                 o = [sum(e[u] / z * Vb[j][t][c] for u, t in enumerate(vis)) for c in range(d)]
                 concat += o
-            out[b * bs + i] = lin(concat, w.w_o, range(H))
+            out[b * bs + i] = lin(o_in(concat) if o_in else concat, w.w_o, range(H))
         new_k.append(Kb)
         new_v.append(Vb)
     return np.array(out), new_k, new_v

@@ -251,3 +251,55 @@ def test_context_kv_precompute_mxfp8_matches_pure_python_brute_force():
         for b in range(2):
             np.testing.assert_array_equal(got[layer].k[b][:, :lens[b]], caches[layer].k[b])
             assert got[layer].lengths[b] == lens[b] + news[b]
+
+
+def test_layer_step_mxfp8_matches_pure_python_brute_force():
+    """The MXFP8 layer step against the pure-Python brute force of the layer
+    step fed what an MXFP8 linear multiplies: block and context rows
+    quantised by the code-table search, weights decoded from the field
+    definitions, and each attention output row rounded to bf16 and quantised
+    the same way before o_proj."""
+    from test_oracle_pins import brute_step, rand_inputs, tiny_cfg
+    cfg = tiny_cfg(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=8, block_size=3)
+    rng = np.random.default_rng(17)
+    H, nq, nkv, d = 64, 4, 2, 8
+    table = e4m3_table()
+    ok = np.flatnonzero(~np.isnan(np.array(table)))
+
+    class MW:
+        w_qkv_codes = rng.choice(ok, ((nq + 2 * nkv) * d, H)).astype(np.uint8)
+        w_qkv_scales = rng.integers(118, 124, ((nq + 2 * nkv) * d, H // 32)).astype(np.uint8)
+        w_o_codes = rng.choice(ok, (H, nq * d)).astype(np.uint8)
+        w_o_scales = rng.integers(118, 124, (H, nq * d // 32)).astype(np.uint8)
+        q_norm = rng.uniform(0.5, 1.5, d)
+        k_norm = rng.uniform(0.5, 1.5, d)
+
+    lens, news = [2, 0], [3, 1]
+    X, C, offs, pos, cache = rand_inputs(cfg, rng, lens, news)
+    got, got_cache = oracle.layer_step_mxfp8(cfg, MW, cache, X, C, offs, pos)
+
+    def dec(codes, scales):
+        return [[table[int(codes[r][c])] * 2.0 ** (int(scales[r][c // 32]) - 127) for c in range(codes.shape[1])]
+                for r in range(codes.shape[0])]
+
+    def qrow(v):
+        out = []
+        for blk in range(len(v) // 32):
+            codes, sbyte = brute_quantize_block([float(t) for t in v[32 * blk:32 * blk + 32]])
+            out += [table[c] * 2.0 ** (sbyte - 127) for c in codes]
+        return out
+
+    wq = dec(MW.w_qkv_codes, MW.w_qkv_scales)
+
+    class W:
+        w_q, w_k, w_v = wq[:nq * d], wq[nq * d:(nq + nkv) * d], wq[(nq + nkv) * d:]
+        w_o = dec(MW.w_o_codes, MW.w_o_scales)
+        q_norm, k_norm = MW.q_norm, MW.k_norm
+
+    Xq = np.array([qrow(r) for r in X])
+    Cq = np.array([qrow(r) for r in C])
+    want, want_k, want_v = brute_step(cfg, W, cache, Xq, Cq, offs, pos, o_in=lambda v: qrow([bf16_py(t) for t in v]))
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11)
+    for b in range(len(lens)):
+        np.testing.assert_allclose(got_cache.k[b], np.array(want_k[b]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got_cache.v[b], np.array(want_v[b]), rtol=1e-12, atol=1e-12)

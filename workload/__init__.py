@@ -18,7 +18,9 @@ from .ctxkv import (  # noqa: F401
     CtxKVConfig,
     CtxKVWeights,
     MXKVWeights,
+    MXLayerWeights,
     make_ctxkv_case,
     make_mxfp8_kv_weights,
+    make_mxfp8_layer_weights,
 )
 from .decoder import QWEN3_8B_INTERMEDIATE, MLPWeights, make_mlp_weights  # noqa: F401

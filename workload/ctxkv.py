@@ -135,19 +135,41 @@ def make_ctxkv_case(cfg: Union[str, CtxKVConfig], seed: int = 0) -> CtxKVCase:
                      L.astype(np.int32), ck, cv)
 
 
-def make_mxfp8_kv_weights(cfg: Union[str, CtxKVConfig], seed: int = 0) -> MXKVWeights:
-    """Seeded MXFP8 K/V weights of ``cfg``'s shape, drawn as bytes (recipe above)."""
-    if isinstance(cfg, str):
-        cfg = CTXKV_CONFIGS[cfg]
-    H, Ln, nkv, d = cfg.hidden, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
-    if H % 32:
-        raise ValueError("hidden must be a multiple of 32")
-    r = _rng(cfg, seed, 5)
-    shape = (Ln, 2 * nkv * d, H)
+def mx_bytes(r: np.random.Generator, shape):
+    """E4M3 codes of ``shape`` and E8M0 scale bytes of ``shape[:-1] + (shape[-1] // 32,)``,
+    drawn directly as bytes (recipe above)."""
+    if shape[-1] % 32:
+        raise ValueError("the reduction length must be a multiple of 32")
     sign = r.integers(0, 2, shape, dtype=np.int64)
     expo = np.clip(np.rint(r.normal(10.0, 1.2, shape)), 1, 15).astype(np.int64)
     mant = r.integers(0, 8, shape, dtype=np.int64)
     mant = np.where(expo == 15, np.minimum(mant, 6), mant)
     codes = ((sign << 7) | (expo << 3) | mant).astype(np.uint8)
-    scales = r.integers(116, 118, (Ln, 2 * nkv * d, H // 32)).astype(np.uint8)
-    return MXKVWeights(codes, scales)
+    scales = r.integers(116, 118, tuple(shape[:-1]) + (shape[-1] // 32,)).astype(np.uint8)
+    return codes, scales
+
+
+def make_mxfp8_kv_weights(cfg: Union[str, CtxKVConfig], seed: int = 0) -> MXKVWeights:
+    """Seeded MXFP8 K/V weights of ``cfg``'s shape, drawn as bytes (recipe above)."""
+    if isinstance(cfg, str):
+        cfg = CTXKV_CONFIGS[cfg]
+    H, Ln, nkv, d = cfg.hidden, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    return MXKVWeights(*mx_bytes(_rng(cfg, seed, 5), (Ln, 2 * nkv * d, H)))
+
+
+@dataclass
+class MXLayerWeights:
+    w_qkv_codes: np.ndarray   # [(nq + 2 nkv) d, H] uint8, rows q | k | v
+    w_qkv_scales: np.ndarray  # [(nq + 2 nkv) d, H / 32] uint8
+    w_o_codes: np.ndarray     # [H, nq d] uint8
+    w_o_scales: np.ndarray    # [H, nq d / 32] uint8
+
+
+def make_mxfp8_layer_weights(cfg, seed: int = 0) -> MXLayerWeights:
+    """Seeded MXFP8 q|k|v and o_proj weights of a layer config (a LayerConfig),
+    drawn as bytes by the same recipe; q_norm / k_norm stay the bf16 case's."""
+    H, nq, nkv, d = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.config_id, seed, 9])))
+    wq, sq = mx_bytes(r, ((nq + 2 * nkv) * d, H))
+    wo, so = mx_bytes(r, (H, nq * d))
+    return MXLayerWeights(wq, sq, wo, so)
