@@ -104,23 +104,43 @@ class DFlashLayer:
 
     ``w_qkv`` is ``[(nq + 2 nkv) d, H]`` (rows q heads, k heads, v heads),
     ``w_o`` ``[H, nq d]``, ``q_norm``/``k_norm`` ``[d]``, all in ``shape.dtype``
-    on the current device."""
+    on the current device.
+
+    With ``w_qkv_scale`` and ``w_o_scale`` the projections are MXFP8 (bf16
+    layers only): ``w_qkv`` and ``w_o`` hold E4M3 codes (uint8) and the scales
+    ``[rows, cols / 32]`` their E8M0 bytes."""
 
     def __init__(self, shape: LayerShape, w_qkv: torch.Tensor, w_o: torch.Tensor,
-                 q_norm: torch.Tensor, k_norm: torch.Tensor):
+                 q_norm: torch.Tensor, k_norm: torch.Tensor, w_qkv_scale: Optional[torch.Tensor] = None,
+                 w_o_scale: Optional[torch.Tensor] = None):
         self.shape = shape
+        self.mxfp8 = w_qkv_scale is not None or w_o_scale is not None
+        if self.mxfp8 and (w_qkv_scale is None or w_o_scale is None):
+            raise ValueError("MXFP8 layers need both scale tensors")
         self._weights = [t.contiguous() for t in (w_qkv, w_o, q_norm, k_norm)]
-        for t in self._weights:
-            if t.dtype != shape.dtype or not t.is_cuda:
-                raise ValueError("weights must be device tensors of the layer dtype")
+        for i, t in enumerate(self._weights):
+            want = torch.uint8 if (self.mxfp8 and i < 2) else shape.dtype
+            if t.dtype != want or not t.is_cuda:
+                raise ValueError("weights must be device tensors of the layer dtype (uint8 codes for MXFP8)")
         cfg = _lib.Config(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                           shape.block_size, shape.sliding_window, shape.max_position,
                           _DTYPES[shape.dtype], float(shape.rope_theta), float(shape.rms_eps))
-        w = _lib.Weights(*[t.data_ptr() for t in self._weights])
         handle = C.c_void_p()
         with torch.cuda.device(self._weights[0].device):
-            check(_lib.lib().dflash_layer_create(C.byref(cfg), C.byref(w), C.byref(handle)),
-                  "dflash_layer_create")
+            if self.mxfp8:
+                scales = [t.contiguous() for t in (w_qkv_scale, w_o_scale)]
+                if any(t.dtype != torch.uint8 or not t.is_cuda for t in scales):
+                    raise ValueError("scales must be uint8 device tensors")
+                self._weights += scales
+                wq, wo, qn, kn, sq, so = self._weights
+                w = _lib.MXFP8Weights(wq.data_ptr(), sq.data_ptr(), wo.data_ptr(), so.data_ptr(), qn.data_ptr(),
+                                      kn.data_ptr())
+                check(_lib.lib().dflash_layer_create_mxfp8(C.byref(cfg), C.byref(w), C.byref(handle)),
+                      "dflash_layer_create_mxfp8")
+            else:
+                w = _lib.Weights(*[t.data_ptr() for t in self._weights])
+                check(_lib.lib().dflash_layer_create(C.byref(cfg), C.byref(w), C.byref(handle)),
+                      "dflash_layer_create")
         self._h = handle
         self._ws: Optional[torch.Tensor] = None
 

@@ -35,6 +35,7 @@ EXPORTS = (
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
     "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
     "dflash_ctxkv_create_mxfp8", "dflash_mxfp8_quantize", "dflash_cache_crop_all",
+    "dflash_layer_create_mxfp8",
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
 )
@@ -50,6 +51,11 @@ class Config(C.Structure):
 class Weights(C.Structure):
     _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("q_norm", C.c_void_p),
                 ("k_norm", C.c_void_p)]
+
+
+class MXFP8Weights(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_qkv_scale", C.c_void_p), ("w_o", C.c_void_p),
+                ("w_o_scale", C.c_void_p), ("q_norm", C.c_void_p), ("k_norm", C.c_void_p)]
 
 
 class KVCacheDesc(C.Structure):
@@ -101,6 +107,8 @@ def lib() -> C.CDLL:
         h = C.CDLL(LIB_PATH)
         h.dflash_layer_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(C.c_void_p)]
         h.dflash_layer_create.restype = C.c_int
+        h.dflash_layer_create_mxfp8.argtypes = [C.POINTER(Config), C.POINTER(MXFP8Weights), C.POINTER(C.c_void_p)]
+        h.dflash_layer_create_mxfp8.restype = C.c_int
         h.dflash_layer_destroy.argtypes = [C.c_void_p]
         h.dflash_layer_destroy.restype = None
         h.dflash_workspace_bytes.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64]

@@ -35,7 +35,9 @@ struct Pending {
 
 // Workspace regions of one step (byte offsets from the workspace base).
 struct Carve {
-  size_t qkv, ctxkv, qpack, obuf, part_o, part_ml, total;
+  size_t qkv, ctxkv, qpack, obuf, part_o, part_ml;
+  size_t xq, xs, cq, cs, oq, os;  // MXFP8 rows and step-major scales of the block, context, attention output
+  size_t total;
 };
 
 }  // namespace
@@ -49,6 +51,9 @@ struct dflash_layer {
   int32_t* err = nullptr;
   bool profiling = false;
   int append_mode = DFLASH_APPEND_AUTO;
+  bool mx = false;                 // MXFP8 projections (dflash_layer_create_mxfp8): w holds E4M3 codes
+  uint8_t* wqkv_scale = nullptr;   // their scales, repacked step-major (owned)
+  uint8_t* wo_scale = nullptr;
   std::vector<Pending> pending;
   std::vector<hipEvent_t> event_pool;
   double ms[DFLASH_K_COUNT] = {};
@@ -100,6 +105,15 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
   w.part_o = off;  off += align_up(2 * gmax * kMaxQueryRows * d * 4);
   w.part_ml = off; off += align_up(2 * gmax * kMaxQueryRows * 2 * 4);
+  if (L->mx) {
+    const int64_t mc = std::max<int64_t>(total_ctx, 1), od = (int64_t)c.n_q_heads * d;
+    w.xq = off; off += align_up(mq * c.hidden);
+    w.xs = off; off += align_up(mq * c.hidden / 32);
+    w.cq = off; off += align_up(mc * c.hidden);
+    w.cs = off; off += align_up(mc * c.hidden / 32);
+    w.oq = off; off += align_up(mq * od);
+    w.os = off; off += align_up(mq * od / 32);
+  }
   w.total = off;
   return w;
 }
@@ -308,7 +322,44 @@ void dflash_layer_destroy(dflash_layer* L) {
   for (hipEvent_t e : L->event_pool) hipEventDestroy(e);
   hipFree(L->cos_sin);
   hipFree(L->err);
+  if (L->wqkv_scale) hipFree(L->wqkv_scale);
+  if (L->wo_scale) hipFree(L->wo_scale);
   delete L;
+}
+
+int dflash_layer_create_mxfp8(const dflash_config* cfg, const dflash_mxfp8_weights* weights,
+                              dflash_layer** out) {
+  if (!cfg || !weights || !out) return DFLASH_ERR_ARG;
+  *out = nullptr;
+  if (!weights->w_qkv_scale || !weights->w_o_scale) return DFLASH_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(weights->w_qkv_scale) % 4 || reinterpret_cast<uintptr_t>(weights->w_o_scale) % 4)
+    return DFLASH_ERR_ARG;
+  if (cfg->dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
+  if (cfg->hidden % 128 || ((int64_t)cfg->n_q_heads * cfg->head_dim) % 128) return DFLASH_ERR_SHAPE;
+  dflash_weights w;
+  w.w_qkv = weights->w_qkv;
+  w.w_o = weights->w_o;
+  w.q_norm = weights->q_norm;
+  w.k_norm = weights->k_norm;
+  dflash_layer* L = nullptr;
+  const int st = dflash_layer_create(cfg, &w, &L);
+  if (st != DFLASH_OK) return st;
+  L->mx = true;
+  const int64_t nqkv = (int64_t)(cfg->n_q_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+  const int64_t od = (int64_t)cfg->n_q_heads * cfg->head_dim;
+  const bool ok = hipMalloc(&L->wqkv_scale, (size_t)nqkv * cfg->hidden / 32) == hipSuccess &&
+                  hipMalloc(&L->wo_scale, (size_t)cfg->hidden * od / 32) == hipSuccess &&
+                  launch_scales_step_major(weights->w_qkv_scale, L->wqkv_scale, (int)nqkv, cfg->hidden, nullptr) ==
+                      hipSuccess &&
+                  launch_scales_step_major(weights->w_o_scale, L->wo_scale, cfg->hidden, (int)od, nullptr) ==
+                      hipSuccess &&
+                  hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    dflash_layer_destroy(L);
+    return DFLASH_ERR_HIP;
+  }
+  *out = L;
+  return DFLASH_OK;
 }
 
 size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t total_ctx,
@@ -363,6 +414,10 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     const int lst = check_layout(cache, rows);
     if (lst != DFLASH_OK) return lst;
   }
+  if (L->mx && L->append_mode == DFLASH_APPEND_SEPARATE) return DFLASH_ERR_UNSUPPORTED;
+  if (L->mx && (reinterpret_cast<uintptr_t>(hidden_states) % 16 ||
+                (Mc > 0 && reinterpret_cast<uintptr_t>(target_hidden) % 16)))
+    return DFLASH_ERR_ARG;
   if (!workspace) return DFLASH_ERR_WORKSPACE;
   const Carve wc = carve(L, B, Mc);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
@@ -384,7 +439,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   const int nt64 = ((Mq + 63) / 64) * (Nqkv / d) + (int)((Mc + 63) / 64) * (Nkv / d);
   const int nt128 = ((Mq + 127) / 128) * (Nqkv / d) + (int)((Mc + 127) / 128) * (Nkv / d);
   const int target = L->num_cus * 3 / 4;
-  const bool fused = L->append_mode == DFLASH_APPEND_FUSED ||
+  const bool fused = L->mx || L->append_mode == DFLASH_APPEND_FUSED ||
                      (L->append_mode == DFLASH_APPEND_AUTO && nt64 >= target);
   const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, nt128 >= target ? nt128 : nt64, 1}
                               : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
@@ -425,7 +480,32 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   na.seq = seq;
   hipEvent_t ev;
   record(L, &ev, s);
-  if (fused) {
+  if (L->mx) {
+    // MXFP8: the block and context rows quantised once (scales step-major,
+    // planes of their own rows), then the block-scaled q|k|v + context k|v
+    // projection with the same epilogue. The weight's scale planes hold all
+    // its q|k|v rows; the context problem starts at its k rows.
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + wc.xq);
+    uint8_t* xs = reinterpret_cast<uint8_t*>(ws + wc.xs);
+    uint8_t* cq = reinterpret_cast<uint8_t*>(ws + wc.cq);
+    uint8_t* cs = reinterpret_cast<uint8_t*>(ws + wc.cs);
+    if (launch_rms_rows_mx(hidden_states, nullptr, xq, xs, Mq, H, 0.f, Mq, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (Mc > 0 && launch_rms_rows_mx(target_hidden, nullptr, cq, cs, (int)Mc, H, 0.f, (int)Mc, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    ga.p[0].a = xq;
+    ga.p[0].sa = xs;
+    ga.p[0].sb = L->wqkv_scale;
+    ga.p[0].sb_plane = (int64_t)Nqkv * 4;
+    if (Mc > 0) {
+      ga.p[1].a = cq;
+      ga.p[1].b = static_cast<const char*>(L->w.w_qkv) + (size_t)nq * d * H;
+      ga.p[1].sa = cs;
+      ga.p[1].sb = L->wqkv_scale + (size_t)nq * d * 4;
+      ga.p[1].sb_plane = (int64_t)Nqkv * 4;
+    }
+    if (launch_gemm_append_mx(d, ga, na, tq.tiles, tq.bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+    record_end(L, DFLASH_K_GEMM_QKV, ev, s);
+  } else if (fused) {
     if (launch_gemm_append(c.dtype, d, ga, na, tq.tiles, tq.bm, s) != hipSuccess) return DFLASH_ERR_HIP;
     record_end(L, DFLASH_K_GEMM_QKV, ev, s);
   } else {
@@ -505,7 +585,18 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   go.nprob = 1;
   go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + to.bn - 1) / to.bn, 0, 0};
   record(L, &ev, s);
-  if (launch_gemm(c.dtype, false, go, to.tiles, to.bm, to.bn, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
+  if (L->mx) {
+    // the attention output (bf16) quantised per row, then the block-scaled o_proj
+    uint8_t* oq = reinterpret_cast<uint8_t*>(ws + wc.oq);
+    uint8_t* os = reinterpret_cast<uint8_t*>(ws + wc.os);
+    if (launch_rms_rows_mx(obuf, nullptr, oq, os, Mq, nq * d, 0.f, Mq, s) != hipSuccess) return DFLASH_ERR_HIP;
+    go.p[0].a = oq;
+    go.p[0].sa = os;
+    go.p[0].sb = L->wo_scale;
+    if (launch_gemm_mx(go, to.tiles, to.bm, to.bn, s) != hipSuccess) return DFLASH_ERR_HIP;
+  } else if (launch_gemm(c.dtype, false, go, to.tiles, to.bm, to.bn, 1, s) != hipSuccess) {
+    return DFLASH_ERR_HIP;
+  }
   record_end(L, DFLASH_K_GEMM_O, ev, s);
 
   for (int b = 0; b < B; ++b) cache->len[b] += (ctx_offsets[b + 1] - ctx_offsets[b]) + bs;

@@ -305,8 +305,8 @@ __device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, in
 #pragma unroll
       for (int i = 0; i < BPP; ++i)
         lds_dma16(boff[i], bb, sl + A_BYTES + (uint32_t)(i * kGemmProducers + pw) * 1024u);
-      const void* sab = uniform_ptr(P.sa + (size_t)step * P.m * 4);
-      const void* sbb = uniform_ptr(P.sb + (size_t)step * P.n * 4);
+      const void* sab = uniform_ptr(P.sa + (size_t)step * (P.sa_plane ? P.sa_plane : (int64_t)P.m * 4));
+      const void* sbb = uniform_ptr(P.sb + (size_t)step * (P.sb_plane ? P.sb_plane : (int64_t)P.n * 4));
 #pragma unroll
       for (int i = 0; i < (SL + 1) / 2; ++i) {
         const int u = 2 * i + pw;
@@ -409,18 +409,23 @@ __device__ __forceinline__ bool gemm_core_mx(const TileJob& J, uint32_t lds0, in
   return true;
 }
 
-template <typename T, typename OutT, int BM, int BN>
+// With MX the operands are MXFP8 (gemm_core_mx, no k split): o_proj of the
+// layer in its MXFP8 configuration.
+template <typename T, typename OutT, int BM, int BN, bool MX = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
-  using Sh = GemmShape<BM, BN>;
+  using Sh = std::conditional_t<MX, GemmShapeMX<BM, BN>, GemmShape<BM, BN>>;
   constexpr int WM = Sh::WM, WN = Sh::WN, MI = Sh::MI, NI = Sh::NI;
   __shared__ u32x4 lds[Sh::S * Sh::STAGE / 16];
   TileJob J = tile_job<BM, BN>(args);
   const int ksl = gridDim.y;                                      // k slices
-  const int nk_all = J.P.k / (8 * (16 / (int)sizeof(T)));         // 128-byte k steps
+  const int nk_all = MX ? J.P.k / 128 : J.P.k / (8 * (16 / (int)sizeof(T)));  // 128-byte k steps
   J.k_first = (int)(((int64_t)nk_all * blockIdx.y) / ksl);
   J.nk = (int)(((int64_t)nk_all * (blockIdx.y + 1)) / ksl) - J.k_first;
   f32x4 acc[NI][MI];
-  if (!gemm_core<T, BM, BN>(J, lds_base(lds), 0, acc)) return;
+  bool consumer;
+  if constexpr (MX) consumer = gemm_core_mx<BM, BN>(J, lds_base(lds), 0, acc);
+  else consumer = gemm_core<T, BM, BN>(J, lds_base(lds), 0, acc);
+  if (!consumer) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
@@ -783,6 +788,20 @@ hipError_t launch_append_t(const GemmArgs& args, const NormRopeArgs& nr, int tot
 }
 
 }  // namespace
+
+hipError_t launch_gemm_mx(const GemmArgs& args, int total_tiles, int bm, int bn, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  const dim3 grid(total_tiles), block(kGemmThreads);
+  if (bm == 128 && bn == 128)
+    hipLaunchKernelGGL((gemm_kernel<__bf16, __bf16, 128, 128, true>), grid, block, 0, s, args);
+  else if (bm == 128 && bn == 64)
+    hipLaunchKernelGGL((gemm_kernel<__bf16, __bf16, 128, 64, true>), grid, block, 0, s, args);
+  else if (bm == 64 && bn == 128)
+    hipLaunchKernelGGL((gemm_kernel<__bf16, __bf16, 64, 128, true>), grid, block, 0, s, args);
+  else
+    hipLaunchKernelGGL((gemm_kernel<__bf16, __bf16, 64, 64, true>), grid, block, 0, s, args);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormRopeArgs& nr, int total_tiles,
                                  int bm, hipStream_t s) {

@@ -30,9 +30,13 @@ struct GemmProblem {
   int32_t b_pair = 0;
   // MXFP8 operands (gemm_append with the MX flag): a and b hold E4M3 codes
   // ([m][lda], [n][ldb] bytes) and sa / sb their E8M0 scales, one byte per 32
-  // consecutive k, step-major: [k / 128][m or n rows][4 bytes].
+  // consecutive k, step-major: [k / 128][plane rows][4 bytes], the problem's
+  // rows at the start of each plane; sa_plane / sb_plane are the bytes between
+  // planes (0: 4 m and 4 n, planes of exactly the problem's rows).
   const uint8_t* sa = nullptr;
   const uint8_t* sb = nullptr;
+  int64_t sa_plane = 0;
+  int64_t sb_plane = 0;
 };
 struct GemmArgs {
   GemmProblem p[2];
@@ -130,6 +134,9 @@ hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, 
 // The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
 // head_dim, no k split) doing the work of launch_norm_rope in its epilogue
 // (nr's qkv, ctxkv and kslices fields are unused).
+// The plain GEMM over MXFP8 operands (sa / sb set, k % 128 == 0, no k split),
+// bf16 output: C = A W^T (+ R).
+hipError_t launch_gemm_mx(const GemmArgs& args, int total_tiles, int bm, int bn, hipStream_t stream);
 // gemm_append over MXFP8 operands (GemmProblem sa / sb set, k % 128 == 0);
 // the caches and gains are bf16.
 hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormRopeArgs& nr, int total_tiles,

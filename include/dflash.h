@@ -28,14 +28,16 @@
  *   - Device pointers are borrowed: the caller allocates and frees every buffer
  *     passed in and keeps weights alive for the layer's lifetime. The library
  *     allocates only each handle's own cos/sin table and error flag (at
- *     create), and an MXFP8 precompute handle its repacked weight scales.
+ *     create), and an MXFP8 layer or precompute handle its repacked weight
+ *     scales.
  *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream) and the calls return without synchronising,
  *     except dflash_layer_poll_error, dflash_layer_kernel_times and
  *     dflash_ctxkv_poll_error.
  *   - Element type of every activation, weight and cache buffer is the
  *     config's dtype (fp32 or bf16), except the MXFP8 weights of
- *     dflash_ctxkv_create_mxfp8; accumulation is fp32.
+ *     dflash_layer_create_mxfp8 and dflash_ctxkv_create_mxfp8; accumulation
+ *     is fp32.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -139,6 +141,36 @@ typedef struct dflash_layer dflash_layer; /* opaque */
  * (limits above), DFLASH_ERR_HIP (allocation or copy failed). */
 int dflash_layer_create(const dflash_config* cfg, const dflash_weights* weights,
                         dflash_layer** out);
+
+/* MXFP8 weights of a layer (the configuration in which the vLLM page
+ * "qwen3_dflash" builds its MXFP8 context K/V projection: every layer's
+ * qkv_proj is an MXFP8 linear; o_proj is taken to be one as well). Format as
+ * for dflash_ctxkv_mxfp8_weights: E4M3 codes and one E8M0 scale per 32
+ * consecutive elements of a row. */
+typedef struct {
+    const void* w_qkv;        /* [(nq + 2 nkv) d, H] E4M3, rows q | k | v; 16-byte aligned */
+    const void* w_qkv_scale;  /* [(nq + 2 nkv) d, H / 32] E8M0; 4-byte aligned          */
+    const void* w_o;          /* [H, nq d] E4M3; 16-byte aligned                         */
+    const void* w_o_scale;    /* [H, nq d / 32] E8M0; 4-byte aligned                     */
+    const void* q_norm;       /* [d] bf16                                                */
+    const void* k_norm;       /* [d] bf16                                                */
+} dflash_mxfp8_weights;
+
+/* A layer handle whose projections are MXFP8. Each step quantises the draft
+ * block rows and the new context rows once (dflash_mxfp8_quantize's rule) for
+ * the block-scaled q|k|v + context k|v projection (16x16x128 scaled FP8
+ * MFMA, fp32 sums, the same norm / RoPE / append epilogue), runs the attention
+ * as in bf16, and quantises the bf16 attention output for the block-scaled
+ * o_proj. Everything else (arguments, workspace query, crop, errors) is as for
+ * dflash_layer_create; hidden_states and target_hidden must be 16-byte
+ * aligned, and DFLASH_APPEND_SEPARATE is not supported (the step then returns
+ * DFLASH_ERR_UNSUPPORTED). create reads the scale arrays once and repacks them
+ * into buffers of its own ([k / 128][rows][4]), freed by destroy.
+ * Errors: those of dflash_layer_create; DFLASH_ERR_UNSUPPORTED (dtype not
+ * bf16); DFLASH_ERR_SHAPE (hidden or nq d not a multiple of 128);
+ * DFLASH_ERR_ARG (a missing or misaligned scale pointer). */
+int dflash_layer_create_mxfp8(const dflash_config* cfg, const dflash_mxfp8_weights* weights,
+                              dflash_layer** out);
 
 /* Release the handle's own table and flag. Waits for the device to finish
  * work that may still read them. NULL is a no-op. */
