@@ -59,6 +59,8 @@ def parse():
                     help="timed steps of the whole draft decoder layer at C3 (0: skip)")
     ap.add_argument("--paged-steps", type=int, default=50,
                     help="timed C3 steps on the paged cache, and as many driver rounds (0: skip)")
+    ap.add_argument("--mxfp8-steps", type=int, default=50,
+                    help="timed C3 steps of the layer with MXFP8 projections (0: skip)")
     ap.add_argument("--decoder-only", action="store_true",
                     help="only time the draft decoder layer (for profiling)")
     ap.add_argument("--context-kv-only", default=None, choices=("P3", "P4"),
@@ -292,6 +294,77 @@ def bench_decoder(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     return res
 
 
+def bench_mxfp8_layer(steps: int, warmup: int, seed: int = 0, copies: int = 3):
+    """The C3 layer step with MXFP8 projections (E4M3 weights with E8M0 block
+    scales, activations quantised on the fly): `steps` steps with the crops,
+    lengths rewound on the host, on `copies` rotating cache copies; then the
+    same steps with per-kernel HIP events (the q|k|v and o_proj figures
+    include their activation quantisation)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import DFlashLayer, KVCache, LayerShape
+    from workload import make_case, make_mxfp8_layer_weights
+
+    case = make_case("C3", seed=seed)
+    cfg = case.cfg
+    dt = torch.bfloat16
+    B, bs, H = case.batch, cfg.block_size, cfg.hidden
+
+    def dev(x, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+    def u8(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    mw = make_mxfp8_layer_weights(cfg, 0)
+    layer = DFlashLayer(LayerShape(H, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, bs, dt, cfg.rope_theta,
+                                   cfg.rms_eps, cfg.sliding_window, cfg.max_position),
+                        u8(mw.w_qkv_codes), u8(mw.w_o_codes), dev(case.weights.q_norm), dev(case.weights.k_norm),
+                        w_qkv_scale=u8(mw.w_qkv_scales), w_o_scale=u8(mw.w_o_scales))
+    caches = []
+    for i in range(copies):
+        c = KVCache(B, cfg.n_kv_heads, cfg.head_dim, case.capacity(), dt)
+        for b in range(B):
+            c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
+        caches.append(c)
+    hs, th, pos = dev(case.hidden_states), dev(case.target_hidden), dev(case.positions, torch.int32)
+    offs = [int(o) for o in case.ctx_offsets]
+    out = torch.empty((B * bs, H), dtype=dt, device="cuda")
+    ws = layer.workspace(B, offs[-1])
+    L0 = case.cached_len.copy()
+    accepted = (case.cached_len + case.new_ctx + case.accept).tolist()
+
+    def one(i):
+        c = caches[i % copies]
+        layer.step(hs, th, offs, pos, c, out=out, workspace=ws)
+        c.crop_all(accepted)
+        c.set_lengths(L0)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(warmup + i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    layer.set_profiling(True)
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    kt = layer.kernel_times()
+    layer.set_profiling(False)
+    if layer.poll_error() != 0:
+        raise RuntimeError("position outside the RoPE table")
+    return {
+        "workload": "C3 layer step with MXFP8 q|k|v and o_proj (E4M3, E8M0 scale per 32), B=32, block 16",
+        "ms_per_step": round(t_step * 1e3, 4),
+        "tokens_per_s": round(B * bs / t_step, 1),
+        "kernel_mean_us": {k: round(v[0] * 1e3 / v[1], 2) if v[1] else 0.0 for k, v in kt.items()},
+    }
+
+
 def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     """The C3 layer step on the paged cache (64-row blocks handed out in a
     shuffled order): `steps` steps with lengths rewound on the host, HIP
@@ -449,8 +522,7 @@ def main():
     def one_step(i):
         cache = caches[i % a.copies]
         layer.step(hs, th, offs, pos, cache, out=out, workspace=ws)
-        for b in range(B):
-            cache.crop(b, accepted[b])
+        cache.crop_all(accepted)
         cache.set_lengths(L0)  # rewind for the next use of this copy (not part of the step)
 
     for i in range(a.warmup):
@@ -550,6 +622,8 @@ def main():
         line["decoder_layer"] = bench_decoder(a.decoder_steps, 5)
     if a.paged_steps > 0:
         line["paged"] = bench_paged(a.paged_steps, 10)
+    if a.mxfp8_steps > 0:
+        line["mxfp8_layer_step"] = bench_mxfp8_layer(a.mxfp8_steps, 10)
     print(json.dumps(line), flush=True)
 
 
