@@ -61,6 +61,8 @@ def parse():
                     help="timed C3 steps on the paged cache, and as many driver rounds (0: skip)")
     ap.add_argument("--mxfp8-steps", type=int, default=50,
                     help="timed C3 steps of the layer with MXFP8 projections (0: skip)")
+    ap.add_argument("--mxfp8-only", action="store_true",
+                    help="only time the C3 layer step with MXFP8 projections (for profiling)")
     ap.add_argument("--decoder-only", action="store_true",
                     help="only time the draft decoder layer (for profiling)")
     ap.add_argument("--context-kv-only", default=None, choices=("P3", "P4"),
@@ -470,6 +472,9 @@ def main():
         return
     if a.decoder_only:
         print(json.dumps({"decoder_layer": bench_decoder(a.decoder_steps, 5)}), flush=True)
+        return
+    if a.mxfp8_only:
+        print(json.dumps({"mxfp8_layer_step": bench_mxfp8_layer(a.mxfp8_steps, 10)}), flush=True)
         return
     if a.context_kv_only:
         print(json.dumps({"context_kv_precompute": bench_context_kv(a.ctxkv_steps, 5, (a.context_kv_only,))}),

@@ -489,8 +489,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     uint8_t* xs = reinterpret_cast<uint8_t*>(ws + wc.xs);
     uint8_t* cq = reinterpret_cast<uint8_t*>(ws + wc.cq);
     uint8_t* cs = reinterpret_cast<uint8_t*>(ws + wc.cs);
-    if (launch_rms_rows_mx(hidden_states, nullptr, xq, xs, Mq, H, 0.f, Mq, s) != hipSuccess) return DFLASH_ERR_HIP;
-    if (Mc > 0 && launch_rms_rows_mx(target_hidden, nullptr, cq, cs, (int)Mc, H, 0.f, (int)Mc, s) != hipSuccess)
+    if (launch_rows_mx2(hidden_states, xq, xs, Mq, target_hidden, cq, cs, (int)Mc, H, s) != hipSuccess)
       return DFLASH_ERR_HIP;
     ga.p[0].a = xq;
     ga.p[0].sa = xs;

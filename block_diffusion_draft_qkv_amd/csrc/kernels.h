@@ -147,6 +147,10 @@ hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormR
 // [h / 128][step_rows][4] when step_rows > 0 (step_rows >= rows).
 hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
                               float eps, int step_rows, hipStream_t stream);
+// Two bf16 row sets [rows1][h], [rows2][h] quantised (no norm) in one launch,
+// each with step-major scales [h / 128][rows_i][4].
+hipError_t launch_rows_mx2(const void* x1, uint8_t* c1, uint8_t* s1, int rows1, const void* x2, uint8_t* c2,
+                           uint8_t* s2, int rows2, int h, hipStream_t stream);
 // E8M0 scales [n][k / 32] (4-byte aligned) -> step-major [k / 128][n][4].
 hipError_t launch_scales_step_major(const void* src, void* dst, int n, int k, hipStream_t stream);
 hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, const NormRopeArgs& nr,

@@ -123,16 +123,14 @@ __global__ __launch_bounds__(256) void rms_rows_kernel(const T* __restrict__ x, 
 // go out row-major [rows][h / 32], or, with step_rows > 0, step-major
 // [h / 128][step_rows][4] (a row's four blocks of a 128-wide k step together,
 // the rows of one step contiguous), the layout the MXFP8 GEMM streams.
-__global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restrict__ x,
-                                                          const __bf16* __restrict__ g,
-                                                          uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales, int h, float eps,
-                                                          int step_rows) {
+__device__ __forceinline__ void mx_row(const __bf16* __restrict__ x, const __bf16* __restrict__ g,
+                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int r, int h,
+                                       float eps, int step_rows) {
   constexpr int V = 8;
   __shared__ float part[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunk = h / V;  // a multiple of 16: a block's four chunks are in one pass
-  const size_t roff = (size_t)blockIdx.x * h;
+  const size_t roff = (size_t)r * h;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + roff);
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
   uint2* out = reinterpret_cast<uint2*>(codes + roff);
@@ -190,8 +188,8 @@ __global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restri
     packed.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], (int)packed.y, true);
     out[c] = packed;
     if ((tid & 3) == 0) {
-      const size_t at = step_rows > 0 ? ((size_t)(c / 16) * step_rows + blockIdx.x) * 4 + (c / 4) % 4
-                                      : (size_t)blockIdx.x * (h / 32) + c / 4;
+      const size_t at = step_rows > 0 ? ((size_t)(c / 16) * step_rows + r) * 4 + (c / 4) % 4
+                                      : (size_t)r * (h / 32) + c / 4;
       scales[at] = (uint8_t)sbyte;
     }
   };
@@ -201,6 +199,25 @@ __global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restri
     if (c < nchunk) put(c, keep[k]);
   }
   for (int c = tid + kChunks * 256; c < nchunk; c += 256) put(c, row[c]);  // longer rows: from L2
+}
+
+__global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restrict__ x,
+                                                          const __bf16* __restrict__ g,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, int h, float eps,
+                                                          int step_rows) {
+  mx_row(x, g, codes, scales, blockIdx.x, h, eps, step_rows);
+}
+
+// Two row sets quantised (no norm) in one launch, each with step-major scale
+// planes of its own rows: a layer step's draft block and new context rows.
+__global__ __launch_bounds__(256) void rows_mx2_kernel(const __bf16* __restrict__ x1, uint8_t* __restrict__ c1,
+                                                       uint8_t* __restrict__ s1, int rows1,
+                                                       const __bf16* __restrict__ x2, uint8_t* __restrict__ c2,
+                                                       uint8_t* __restrict__ s2, int rows2, int h) {
+  const int r = blockIdx.x;
+  if (r < rows1) mx_row(x1, nullptr, c1, s1, r, h, 0.f, rows1);
+  else mx_row(x2, nullptr, c2, s2, r - rows1, h, 0.f, rows2);
 }
 
 // Row-major E8M0 scales [n][k / 32] -> step-major [k / 128][n][4]: one
@@ -220,6 +237,14 @@ hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rms_rows_mx_kernel, dim3(rows), dim3(256), 0, stream, static_cast<const __bf16*>(x),
                      static_cast<const __bf16*>(g), codes, scales, h, eps, step_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_mx2(const void* x1, uint8_t* c1, uint8_t* s1, int rows1, const void* x2, uint8_t* c2,
+                           uint8_t* s2, int rows2, int h, hipStream_t stream) {
+  if (rows1 + rows2 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_mx2_kernel, dim3(rows1 + rows2), dim3(256), 0, stream, static_cast<const __bf16*>(x1), c1,
+                     s1, rows1, static_cast<const __bf16*>(x2), c2, s2, rows2, h);
   return hipGetLastError();
 }
 
