@@ -196,9 +196,32 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4"), formats=("bf16
             raise RuntimeError("context position outside the RoPE table")
         us = e0.elapsed_time(e1) * 1e3 / steps
         rows = offs[-1]
+        es = 2 if c.dtype == "bf16" else 4
+        fc = None
+        if not mx:
+            # the optional fc projection before it (three target layers' features)
+            from workload import make_fc_inputs
+            aux, w_fc = make_fc_inputs(c, rows, seed=0)
+            pre.set_fc(dev(w_fc))
+            aux_d = dev(aux)
+            ctx_fc = torch.empty((rows, c.hidden), dtype=dt, device="cuda")
+            for _ in range(warmup):
+                pre.combine(aux_d, out=ctx_fc)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                pre.combine(aux_d, out=ctx_fc)
+            e1.record()
+            torch.cuda.synchronize()
+            fc_us = e0.elapsed_time(e1) * 1e3 / steps
+            fc_flops = 2.0 * rows * c.hidden * aux.shape[1]
+            fc = {"us_per_run": round(fc_us, 2), "fc_in": int(aux.shape[1]),
+                  "tflops": round(fc_flops / (fc_us * 1e-6) / 1e12, 1),
+                  "floor_us": {"mfma": round(fc_flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+                               "hbm": round((w_fc.size + aux.size + rows * c.hidden) * es / (HBM_PEAK_GBS * 1e9) * 1e6,
+                                            2)}}
         n_out = c.n_layers * 2 * c.n_kv_heads * c.head_dim
         flops = 2.0 * rows * n_out * c.hidden
-        es = 2 if c.dtype == "bf16" else 4
         weight_bytes = n_out * c.hidden * es if not mx else n_out * c.hidden * 33 // 32   # codes + scales
         io_bytes = rows * c.hidden * es + rows * n_out * es   # states in, K/V rows out
         peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
@@ -213,6 +236,8 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4"), formats=("bf16
             "floor_us": {"mfma": round(flops / (peak * 1e12) * 1e6, 2),
                          "hbm": round((weight_bytes + io_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
         }
+        if fc is not None:
+            res[name]["fc_combine"] = fc
         pre.close()
         del caches
         torch.cuda.empty_cache()

@@ -289,6 +289,37 @@ class ContextKV:
                                             _ptr(workspace), workspace.numel(), _stream_handle(stream))
         check(st, "dflash_ctxkv_append")
 
+    def set_fc(self, w_fc: Optional[torch.Tensor]) -> None:
+        """Register the fc weight ``[H, fc_in]`` (the dtype, device) used by
+        ``combine``; None removes it."""
+        if w_fc is None:
+            self._fc = None
+            check(_lib.lib().dflash_ctxkv_set_fc(self._h, None, 0), "dflash_ctxkv_set_fc")
+            return
+        w = w_fc.contiguous()
+        if w.dtype != self.shape.dtype or not w.is_cuda or w.dim() != 2 or w.shape[0] != self.shape.hidden:
+            raise ValueError("fc weight must be a [hidden, fc_in] device tensor of the dtype")
+        check(_lib.lib().dflash_ctxkv_set_fc(self._h, w.data_ptr(), w.shape[1]), "dflash_ctxkv_set_fc")
+        self._fc = w
+
+    def combine(self, aux_states: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """The fc projection of concatenated target-layer features
+        ``[rows, fc_in]`` -> context states ``[rows, H]`` for ``append``."""
+        if getattr(self, "_fc", None) is None:
+            raise ValueError("no fc weight set")
+        a = aux_states.contiguous()
+        if a.dtype != self.shape.dtype or a.dim() != 2 or a.shape[1] != self._fc.shape[1]:
+            raise ValueError("aux_states must be [rows, fc_in] in the dtype")
+        if out is None:
+            out = torch.empty((a.shape[0], self.shape.hidden), dtype=a.dtype, device=a.device)
+        need = int(_lib.lib().dflash_ctxkv_combine_workspace_bytes(self._h, a.shape[0]))
+        if getattr(self, "_fc_ws", None) is None or self._fc_ws.numel() < need:
+            self._fc_ws = torch.empty(need, dtype=torch.uint8, device=a.device)
+        check(_lib.lib().dflash_ctxkv_combine(self._h, _ptr(a), a.shape[0], _ptr(out), _ptr(self._fc_ws),
+                                              self._fc_ws.numel(), _stream_handle(stream)),
+              "dflash_ctxkv_combine")
+        return out
+
     def set_append_mode(self, mode: str) -> None:
         """``"auto"`` (default), ``"fused"`` (projection epilogue) or ``"separate"``."""
         check(_lib.lib().dflash_ctxkv_set_append_mode(self._h, _lib.APPEND_MODES[mode]), "set_append_mode")

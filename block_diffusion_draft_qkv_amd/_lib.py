@@ -35,7 +35,8 @@ EXPORTS = (
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
     "dflash_ctxkv_append", "dflash_ctxkv_poll_error", "dflash_ctxkv_set_append_mode",
     "dflash_ctxkv_create_mxfp8", "dflash_mxfp8_quantize", "dflash_cache_crop_all",
-    "dflash_layer_create_mxfp8",
+    "dflash_layer_create_mxfp8", "dflash_ctxkv_set_fc", "dflash_ctxkv_combine",
+    "dflash_ctxkv_combine_workspace_bytes",
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
 )
@@ -135,6 +136,13 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_create_mxfp8.restype = C.c_int
         h.dflash_mxfp8_quantize.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
         h.dflash_mxfp8_quantize.restype = C.c_int
+        h.dflash_ctxkv_set_fc.argtypes = [C.c_void_p, C.c_void_p, C.c_int32]
+        h.dflash_ctxkv_set_fc.restype = C.c_int
+        h.dflash_ctxkv_combine.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                           C.c_size_t, C.c_void_p]
+        h.dflash_ctxkv_combine.restype = C.c_int
+        h.dflash_ctxkv_combine_workspace_bytes.argtypes = [C.c_void_p, C.c_int64]
+        h.dflash_ctxkv_combine_workspace_bytes.restype = C.c_size_t
         h.dflash_cache_crop_all.argtypes = [C.POINTER(KVCacheDesc), C.POINTER(C.c_int32)]
         h.dflash_cache_crop_all.restype = C.c_int
         h.dflash_ctxkv_destroy.argtypes = [C.c_void_p]

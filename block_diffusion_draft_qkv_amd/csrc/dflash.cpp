@@ -72,6 +72,8 @@ struct dflash_ctxkv {
   dflash_ctxkv_weights w;      // with mx, w.w_kv holds E4M3 codes
   bool mx = false;             // MXFP8 weights (dflash_ctxkv_create_mxfp8)
   uint8_t* w_scale = nullptr;  // their scales, repacked step-major (owned)
+  const void* w_fc = nullptr;  // optional fc weight [hidden][fc_in] (borrowed)
+  int32_t fc_in = 0;
   int num_cus = 256;
   int append_mode = DFLASH_APPEND_AUTO;
   float* cos_sin = nullptr;
@@ -735,6 +737,61 @@ int dflash_ctxkv_create_mxfp8(const dflash_ctxkv_config* cfg, const dflash_ctxkv
   w.w_kv = weights->w_kv;
   w.k_norm = weights->k_norm;
   return ctxkv_create_impl(cfg, &w, static_cast<const uint8_t*>(weights->w_kv_scale), true, out);
+}
+
+int dflash_ctxkv_set_fc(dflash_ctxkv* h, const void* w_fc, int32_t fc_in) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (!w_fc) {
+    h->w_fc = nullptr;
+    h->fc_in = 0;
+    return DFLASH_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(w_fc) % 16) return DFLASH_ERR_ARG;
+  if (fc_in <= 0 || fc_in % 64) return DFLASH_ERR_SHAPE;
+  h->w_fc = w_fc;
+  h->fc_in = fc_in;
+  return DFLASH_OK;
+}
+
+size_t dflash_ctxkv_combine_workspace_bytes(const dflash_ctxkv* h, int64_t rows) {
+  if (!h || rows < 0) return 0;
+  return align_up((size_t)kMaxKSlices * (size_t)std::max<int64_t>(rows, 1) * h->cfg.hidden * 4);
+}
+
+int dflash_ctxkv_combine(dflash_ctxkv* h, const void* aux_states, int64_t rows, void* context_states,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (rows < 0 || rows > INT32_MAX) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!h->w_fc || !aux_states || !context_states) return DFLASH_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(aux_states) % 16 || reinterpret_cast<uintptr_t>(context_states) % 16)
+    return DFLASH_ERR_ARG;
+  const dflash_ctxkv_config& c = h->cfg;
+  const int H = c.hidden, K = h->fc_in;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Few rows and a long k: split k over fp32 slices in the workspace and sum
+  // them (one rounding to the dtype); otherwise the GEMM rounds directly.
+  const TileChoice t = choose_tiles(h->num_cus, (int)rows, H, 0, 0, true);
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.nprob = 1;
+  const int64_t slice = rows * (int64_t)H;
+  if (t.kslices == 1) {
+    ga.p[0] = {aux_states, h->w_fc, context_states, (int32_t)rows, H, K, K, K, H, (H + t.bn - 1) / t.bn, 0, 0};
+    if (launch_gemm(c.dtype, c.dtype == DFLASH_F32, ga, t.tiles, t.bm, t.bn, 1, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    return DFLASH_OK;
+  }
+  if (!workspace) return DFLASH_ERR_WORKSPACE;
+  if (workspace_bytes < (size_t)t.kslices * slice * 4 || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return DFLASH_ERR_WORKSPACE;
+  float* part = static_cast<float*>(workspace);
+  ga.p[0] = {aux_states, h->w_fc, part, (int32_t)rows, H, K, K, K, H, (H + t.bn - 1) / t.bn, 0, slice};
+  if (launch_gemm(c.dtype, true, ga, t.tiles, t.bm, t.bn, t.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
+  if (launch_sum_slices(c.dtype == DFLASH_BF16 ? 1 : 0, part, t.kslices, slice, context_states, slice, s) !=
+      hipSuccess)
+    return DFLASH_ERR_HIP;
+  return DFLASH_OK;
 }
 
 int dflash_mxfp8_quantize(const void* x, int64_t rows, int32_t cols, void* codes, void* scales, void* stream) {

@@ -350,6 +350,34 @@ int dflash_ctxkv_create_mxfp8(const dflash_ctxkv_config* cfg, const dflash_ctxkv
 /* Release the handle (waits for the device). NULL is a no-op. */
 void dflash_ctxkv_destroy(dflash_ctxkv* h);
 
+/* The optional fc projection before the precompute (vLLM page
+ * "qwen3_dflash": the model's fc, a ReplicatedLinear with no bias, and
+ * combine_hidden_states): the features of the selected target layers,
+ * concatenated per row, projected to the draft's hidden size. The result is
+ * the context_states that dflash_ctxkv_append takes.
+ * set_fc registers the weight w_fc: device [hidden, fc_in] in the config
+ * dtype, 16-byte aligned, borrowed (it must outlive the handle or the next
+ * set_fc); fc_in > 0 and a multiple of 64. NULL w_fc removes it.
+ * Errors: DFLASH_ERR_ARG (null handle, misaligned weight), DFLASH_ERR_SHAPE
+ * (fc_in). */
+int dflash_ctxkv_set_fc(dflash_ctxkv* h, const void* w_fc, int32_t fc_in);
+
+/* Device workspace bytes dflash_ctxkv_combine may need for `rows` rows (fp32
+ * partial sums of a k split); 0 on bad input. */
+size_t dflash_ctxkv_combine_workspace_bytes(const dflash_ctxkv* h, int64_t rows);
+
+/* context_states [rows, hidden] = aux_states [rows, fc_in] . w_fc^T, with fp32
+ * sums rounded once to the dtype (for few rows the k axis is split over fp32
+ * slices in the workspace and summed afterwards). Both device buffers are
+ * 16-byte aligned and in the config dtype; the workspace (256-byte aligned,
+ * at least dflash_ctxkv_combine_workspace_bytes) is scratch for the call;
+ * enqueued on `stream`. rows == 0 is a no-op.
+ * Errors: DFLASH_ERR_ARG (null handle or pointers, misaligned buffers, no fc
+ * weight set), DFLASH_ERR_SHAPE (rows < 0 or > 2^31 - 1),
+ * DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP. */
+int dflash_ctxkv_combine(dflash_ctxkv* h, const void* aux_states, int64_t rows, void* context_states,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace bytes for up to `total_ctx` context rows; 0 on bad input. */
 size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx);
 

@@ -18,7 +18,7 @@ from .ref_fp64 import (  # noqa: F401
     rope_inv_freq,
     window_keep,
 )
-from .context_kv import context_kv_precompute  # noqa: F401
+from .context_kv import combine_hidden_states, context_kv_precompute  # noqa: F401
 from .decoder import decoder_layer_step, draft_forward, mlp, silu  # noqa: F401
 from .mxfp8 import (  # noqa: F401
     context_kv_precompute_mxfp8,

@@ -11,7 +11,11 @@ What it computes is the vLLM page "qwen3_dflash",
 ``_normalize_context_k``: the new context rows of every draft layer are made
 at once instead of inside each layer's forward.
 
-* The raw context states (the fc output) are RMS-normalised over ``hidden``
+* The raw context states are the ``fc`` output (``combine_hidden_states``):
+  the features of the selected target layers, concatenated per row, times
+  the ``fc`` weight (a ``ReplicatedLinear`` with no bias, from
+  ``n_target_layers * target_hidden`` to ``hidden``).
+* The raw context states are RMS-normalised over ``hidden``
   with the model's ``hidden_norm`` gain (``_normalize_context_states``).
 * One projection with the K/V rows of every layer's fused q|k|v weight gives
   each layer's context K and V (``_build_context_kv_buffers`` stacks the rows
@@ -32,6 +36,12 @@ from typing import List, Sequence
 import numpy as np
 
 from .ref_fp64 import OracleCache, _f64, linear, rms_norm, rope
+
+
+def combine_hidden_states(aux_states, w_fc):
+    """The ``fc`` projection of the concatenated target-layer features:
+    ``aux_states [rows, fc_in] . w_fc^T`` with ``w_fc [hidden, fc_in]``."""
+    return linear(_f64(aux_states), _f64(w_fc))
 
 
 def context_kv_precompute(cfg, weights, caches: Sequence[OracleCache], context_states, ctx_offsets,

@@ -196,3 +196,53 @@ def test_position_out_of_range_is_latched():
     pre.append(dev(case.context_states, torch.bfloat16), case.ctx_offsets, torch.from_numpy(bad).cuda(), caches)
     assert pre.poll_error() != 0
     assert pre.poll_error() == 0  # cleared once reported
+
+
+@pytest.mark.parametrize("name", ["P3", "P4"])
+def test_fc_combine_matches_oracle(name):
+    """The fc projection of three target layers' concatenated features
+    (fc_in = 3 H) at the workload's row count, against the oracle; P4's 4096
+    rows are checked on a sample of rows (each row is independent)."""
+    from workload import make_fc_inputs
+    case = make_ctxkv_case(name, seed=0)
+    rows = int(case.ctx_offsets[-1])
+    aux, w_fc = make_fc_inputs(case.cfg, rows, seed=0)
+    pre = make_precompute(case)
+    pre.set_fc(dev(w_fc, torch.bfloat16))
+    out = pre.combine(dev(aux, torch.bfloat16))
+    torch.cuda.synchronize()
+    pick = np.arange(rows) if rows <= 512 else np.random.default_rng(2).choice(rows, 64, replace=False)
+    ref = oracle.combine_hidden_states(aux[pick], w_fc)
+    e = assert_close_stored(to64(out[torch.from_numpy(pick).cuda()]), ref, "bf16", f"{name} fc")
+    print(f"[fc {name}] rows {rows} max abs {e[0]:.3e} rel-RMS {e[1]:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["P1", "small_bf16"])
+def test_fc_then_precompute_matches_oracle(name):
+    """combine, then append: the caches follow the oracle's precompute of the
+    oracle's combined rows."""
+    from workload import make_fc_inputs
+    case = {"P1": lambda: make_ctxkv_case("P1", seed=3),
+            "small_bf16": lambda: make_ctxkv_case(small(config_id=52), seed=3)}[name]()
+    dt = torch_dt(case)
+    rows = int(case.ctx_offsets[-1])
+    aux, w_fc = make_fc_inputs(case.cfg, rows, seed=1)
+    pre = make_precompute(case)
+    pre.set_fc(dev(w_fc, dt))
+    caches = make_caches(case)
+    ctx = pre.combine(dev(aux, dt))
+    pre.append(ctx, case.ctx_offsets, torch.from_numpy(case.positions.astype(np.int32)).cuda(), caches)
+    torch.cuda.synchronize()
+    assert pre.poll_error() == 0
+    ref = oracle.context_kv_precompute(case.cfg, case.weights, oracle_caches(case),
+                                       oracle.combine_hidden_states(aux, w_fc), case.ctx_offsets, case.positions)
+    L, n = case.cached_len, case.new_ctx
+    for layer, kv in enumerate(caches):
+        assert kv.lengths.tolist() == (L + n).tolist()
+        for b in range(case.batch):
+            lb, tb = int(L[b]), int(L[b] + n[b])
+            if tb > lb:
+                assert_close_stored(to64(kv.k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], case.cfg.dtype,
+                                    f"layer {layer} K seq {b}")
+                assert_close_stored(to64(kv.v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                                    case.cfg.dtype, f"layer {layer} V seq {b}")

@@ -607,3 +607,22 @@ def test_draft_stack_is_layers_in_order_then_final_norm():
     np.testing.assert_array_equal(new[1].k[0], c2.k[0])
     swapped, _ = oracle.draft_forward(cfg, layers[::-1], [cache, cache.copy()], X, C, offs, pos, fin)
     assert np.abs(swapped - got).max() > 1e-3
+
+
+def test_combine_hidden_states_matches_pure_python_and_feeds_the_precompute():
+    """The fc projection of concatenated target features: a pure-Python dot
+    product per output, and the precompute of the combined rows equals the
+    precompute handed those rows."""
+    rng = np.random.default_rng(31)
+    rows, fc_in, H = 4, 3 * 10, 10
+    aux = rng.standard_normal((rows, fc_in))
+    w_fc = rng.standard_normal((H, fc_in)) * 0.2
+    got = oracle.combine_hidden_states(aux, w_fc)
+    for r in range(rows):
+        for o in range(H):
+            want = sum(float(aux[r][c]) * float(w_fc[o][c]) for c in range(fc_in))
+            assert abs(got[r][o] - want) <= 1e-12 * (1 + abs(want))
+    # the layers' features are concatenated per row: permuting whole layer
+    # chunks of the input together with the weight's columns changes nothing
+    perm = np.concatenate([np.arange(20, 30), np.arange(0, 10), np.arange(10, 20)])
+    np.testing.assert_allclose(oracle.combine_hidden_states(aux[:, perm], w_fc[:, perm]), got, rtol=1e-12, atol=1e-12)

@@ -20,6 +20,7 @@ from .ctxkv import (  # noqa: F401
     MXKVWeights,
     MXLayerWeights,
     make_ctxkv_case,
+    make_fc_inputs,
     make_mxfp8_kv_weights,
     make_mxfp8_layer_weights,
 )

@@ -173,3 +173,19 @@ def make_mxfp8_layer_weights(cfg, seed: int = 0) -> MXLayerWeights:
     wq, sq = mx_bytes(r, ((nq + 2 * nkv) * d, H))
     wo, so = mx_bytes(r, (H, nq * d))
     return MXLayerWeights(wq, sq, wo, so)
+
+
+def make_fc_inputs(cfg: Union[str, CtxKVConfig], rows: int, seed: int = 0, target_layers: int = 3):
+    """Inputs of the fc projection for ``rows`` context rows: the concatenated
+    features of ``target_layers`` target layers ``[rows, target_layers * H]``
+    ~ N(0, 1) and the fc weight ``[H, target_layers * H]`` ~ N(0, 0.02^2)
+    (a target with the draft's hidden size, three extracted layers as in the
+    pages' config example), rounded to the config dtype."""
+    if isinstance(cfg, str):
+        cfg = CTXKV_CONFIGS[cfg]
+    rnd = round_bf16 if cfg.dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    r = _rng(cfg, seed, 6)
+    fc_in = target_layers * cfg.hidden
+    w_fc = rnd(r.standard_normal((cfg.hidden, fc_in), dtype=np.float32) * np.float32(0.02))
+    aux = rnd(r.standard_normal((rows, fc_in), dtype=np.float32))
+    return aux, w_fc
