@@ -147,11 +147,11 @@ def test_steps_with_crop_match_oracle_rounds():
     out2 = layer.step(hs2, th2, case2.ctx_offsets, torch.from_numpy(pos2).cuda(), cache)
     ref2, ref_cache2 = oracle.layer_step(cfg, case.weights, ref_cache, case2.hidden_states,
                                          case2.target_hidden, case2.ctx_offsets, pos2)
-    assert_close(to64(out2), ref2, "bf16", "round 2 out")
+    assert_close(to64(out2), ref2, "bf16", "second step out")
     for b in range(case.batch):
         k, v = cache.read(b)
-        assert_close(to64(k), ref_cache2.k[b], "bf16", f"round 2 cache K {b}")
-        assert_close(to64(v), ref_cache2.v[b], "bf16", f"round 2 cache V {b}")
+        assert_close(to64(k), ref_cache2.k[b], "bf16", f"second step cache K {b}")
+        assert_close(to64(v), ref_cache2.v[b], "bf16", f"second step cache V {b}")
 
 
 def test_crop_semantics_bit_exact():
