@@ -177,6 +177,37 @@ __device__ inline u32x4 pack_p_bf16(const f32x4& p0, const f32x4& p1) {
 }
 
 // Four consecutive outputs of one row as one 16-byte (fp32) or 8-byte (bf16) store.
+// MXFP8 output helpers (the same rule as the activation quantiser: values
+// rounded to bf16, shared exponent floor(log2 amax) - 8 clamped to
+// [-127, 127], elements x / 2^exponent clamped to +-448 and converted by the
+// packed FP8 instruction, round to nearest even).
+__device__ inline f32x4 round_bf16x4(const f32x4& v) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (float)(__bf16)v[i];
+  return r;
+}
+__device__ inline float absmax4(const f32x4& v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+// Scale byte of a block maximum and the power of two that maps the block.
+__device__ inline int mx_scale_byte(float amax, float& mul) {
+  const int sbyte = min(max((int)((__float_as_uint(amax) >> 23) & 0xff) - 8, 0), 254);
+  mul = __uint_as_float((uint32_t)(254 - sbyte) << 23);
+  return sbyte;
+}
+__device__ inline uint32_t mx_codes4(const f32x4& y, float mul) {
+  f32x4 t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = fminf(fmaxf(y[i] * mul, -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], lo, true);
+}
+// Scale byte of 32-column block `cb` of row `m` in the step-major layout.
+__device__ inline size_t mx_scale_at(const MxOut& mo, int m, int cb) {
+  return ((size_t)(cb >> 2) * mo.rows + m) * 4 + (cb & 3);
+}
+
 template <typename T> __device__ inline void store4(T* p, const f32x4& v);
 template <> __device__ inline void store4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
@@ -494,10 +525,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
           if (full) {
             const float inv = 1.0f / lt;
             const int i = qrow / g, hh = qrow % g;
-            T* orow = static_cast<T*>(a.o) +
-                      ((size_t)(cur.b * a.bs + i) * a.nq + (size_t)(cur.j * g + hh)) * D;
+            if (a.mxo.codes != nullptr) {
+              // MXFP8 o_proj input: a 32-column block is slices 2k, 2k+1 of the
+              // four lanes (q = 0..3) that hold this row.
+              const int m = cur.b * a.bs + i, col0 = (cur.j * g + hh) * D;
+              uint8_t* crow = a.mxo.codes + (size_t)m * a.mxo.ld + col0;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) store4<T>(orow + db * 16 + 4 * q, acc[db] * inv);
+              for (int k = 0; k < D / 32; ++k) {
+                const f32x4 y0 = round_bf16x4(acc[2 * k] * inv), y1 = round_bf16x4(acc[2 * k + 1] * inv);
+                float am = fmaxf(absmax4(y0), absmax4(y1));
+                am = fmaxf(am, __shfl_xor(am, 16, 64));
+                am = fmaxf(am, __shfl_xor(am, 32, 64));
+                float mul;
+                const int sb = mx_scale_byte(am, mul);
+                *reinterpret_cast<uint32_t*>(crow + (2 * k) * 16 + 4 * q) = mx_codes4(y0, mul);
+                *reinterpret_cast<uint32_t*>(crow + (2 * k + 1) * 16 + 4 * q) = mx_codes4(y1, mul);
+                if (q == 0) a.mxo.scales[mx_scale_at(a.mxo, m, col0 / 32 + k)] = (uint8_t)sb;
+              }
+            } else {
+              T* orow = static_cast<T*>(a.o) +
+                        ((size_t)(cur.b * a.bs + i) * a.nq + (size_t)(cur.j * g + hh)) * D;
+#pragma unroll
+              for (int db = 0; db < DB; ++db) store4<T>(orow + db * 16 + 4 * q, acc[db] * inv);
+            }
           } else {
             const int slot = 2 * (int)w + (seg_start_flat == 0 ? 0 : 1);
             float* po = a.part_o + ((size_t)slot * kMaxQueryRows + qrow) * D;
@@ -564,6 +614,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   }
   const int g = a.nq / a.nkv, b = pair / a.nkv, j = pair % a.nkv;
   const int i = row / g, hh = row % g;
+  if (a.mxo.codes != nullptr) {
+    // MXFP8 o_proj input: a 32-column block is 8 neighbouring threads of the row
+    const int m = b * a.bs + i, col0 = (j * g + hh) * D;
+    const f32x4 y = round_bf16x4(num * (1.0f / den));
+    float am = absmax4(y);
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    am = fmaxf(am, __shfl_xor(am, 4, 64));
+    float mul;
+    const int sb = mx_scale_byte(am, mul);
+    *reinterpret_cast<uint32_t*>(a.mxo.codes + (size_t)m * a.mxo.ld + col0 + d4) = mx_codes4(y, mul);
+    if (d4 % 32 == 0) a.mxo.scales[mx_scale_at(a.mxo, m, (col0 + d4) / 32)] = (uint8_t)sb;
+    return;
+  }
   T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.bs + i) * a.nq + (size_t)(j * g + hh)) * D;
   store4<T>(orow + d4, num * (1.0f / den));
 }

@@ -533,6 +533,9 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   aa.window = c.sliding_window >= cache->capacity ? 0 : c.sliding_window;
   aa.total_tiles = n_tiles;
   aa.G = (int32_t)attn_groups(L, n_tiles);
+  // an MXFP8 layer's attention writes o_proj's MXFP8 input directly
+  aa.mxo = L->mx ? MxOut{reinterpret_cast<uint8_t*>(ws + wc.oq), reinterpret_cast<uint8_t*>(ws + wc.os), nq * d, Mq}
+                 : MxOut{nullptr, nullptr, 0, 0};
   aa.map = cache_map(cache, nkv);
   aa.seq = seq;
   // Each work-group's first (pair, tile): walk the pairs in flat order.
@@ -556,6 +559,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   ma.part_o = aa.part_o;
   ma.part_ml = aa.part_ml;
   ma.o = obuf;
+  ma.mxo = aa.mxo;
   ma.nq = nq; ma.nkv = nkv; ma.bs = bs; ma.R = R;
   ma.n_split = 0;
   {
@@ -587,12 +591,9 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   go.p[0] = {obuf, L->w.w_o, out, Mq, H, nq * d, nq * d, nq * d, H, (H + to.bn - 1) / to.bn, 0, 0};
   record(L, &ev, s);
   if (L->mx) {
-    // the attention output (bf16) quantised per row, then the block-scaled o_proj
-    uint8_t* oq = reinterpret_cast<uint8_t*>(ws + wc.oq);
-    uint8_t* os = reinterpret_cast<uint8_t*>(ws + wc.os);
-    if (launch_rms_rows_mx(obuf, nullptr, oq, os, Mq, nq * d, 0.f, Mq, s) != hipSuccess) return DFLASH_ERR_HIP;
-    go.p[0].a = oq;
-    go.p[0].sa = os;
+    // the attention and merge wrote the MXFP8 rows of its output (aa.mxo)
+    go.p[0].a = aa.mxo.codes;
+    go.p[0].sa = aa.mxo.scales;
     go.p[0].sb = L->wo_scale;
     if (launch_gemm_mx(go, to.tiles, to.bm, to.bn, s) != hipSuccess) return DFLASH_ERR_HIP;
   } else if (launch_gemm(c.dtype, false, go, to.tiles, to.bm, to.bn, 1, s) != hipSuccess) {

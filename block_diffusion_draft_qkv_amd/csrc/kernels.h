@@ -161,6 +161,15 @@ hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, con
                               int total_tiles, int bm, hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
+// MXFP8 form of the attention output (the o_proj input of a layer whose
+// projections are MXFP8): codes [rows][ld] E4M3 bytes, scales step-major
+// [ld / 128][rows][4] E8M0 bytes. codes == nullptr: write O in the dtype.
+struct MxOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  int32_t ld, rows;
+};
+
 // Flattened work: pairs (b, j) in b-major order, each owning the 64-key tiles
 // [lo_b, hi_b) of sequence b (lo_b > 0 only under a sliding window). Work-group
 // w takes flat tiles [floor(w N / G), floor((w+1) N / G)).
@@ -172,6 +181,7 @@ struct AttnArgs {
   float* part_o;           // [2G][64][d] un-normalised partial outputs
   float* part_ml;          // [2G][64][2] running max (log2 domain) and sum
   int32_t nq, nkv, bs, R, cap, window, G;
+  MxOut mxo;
   int64_t total_tiles;
   CacheMap map;            // cache layout
   SeqTable seq;
@@ -191,11 +201,14 @@ struct MergeArgs {
   const float* part_o;
   const float* part_ml;
   void* o;
+  MxOut mxo;
   int32_t nq, nkv, bs, R, n_split;
   int32_t pair[kMaxGroups];        // b * nkv + j
   int16_t first_slot[kMaxGroups];  // slot of the pair's first part
   int16_t nparts[kMaxGroups];      // parts (work-group ranges) of the pair
 };
+// kernel arguments are passed by value: both must fit the 4 KB argument block
+static_assert(sizeof(AttnArgs) <= 4096 && sizeof(MergeArgs) <= 4096, "kernel arguments exceed 4 KB");
 hipError_t launch_merge(int dtype, int head_dim, const MergeArgs& args, hipStream_t stream);
 
 // Host-side mirror of the kernels' partition (used to size and skip launches).

@@ -160,8 +160,9 @@ typedef struct {
  * block rows and the new context rows once (dflash_mxfp8_quantize's rule) for
  * the block-scaled q|k|v + context k|v projection (16x16x128 scaled FP8
  * MFMA, fp32 sums, the same norm / RoPE / append epilogue), runs the attention
- * as in bf16, and quantises the bf16 attention output for the block-scaled
- * o_proj. Everything else (arguments, workspace query, crop, errors) is as for
+ * as in bf16 with the attention output (rounded to bf16, then quantised by
+ * the same rule) written as MXFP8 by the attention and merge kernels, and
+ * feeds that to the block-scaled o_proj. Everything else (arguments, workspace query, crop, errors) is as for
  * dflash_layer_create; hidden_states and target_hidden must be 16-byte
  * aligned, and DFLASH_APPEND_SEPARATE is not supported (the step then returns
  * DFLASH_ERR_UNSUPPORTED). create reads the scale arrays once and repacks them
