@@ -54,22 +54,37 @@ class LayerShape:
 
 
 class KVCache:
-    """Draft KV cache of ``batch`` sequences in device memory.
+    """Draft KV cache of ``batch`` sequences in device memory, block-major.
 
-    ``k`` is ``[batch, n_kv, capacity, head_dim]``; ``v`` is stored transposed,
-    ``[batch, n_kv, head_dim, capacity]``. ``lengths`` is the host array of
-    valid rows that the library reads and updates."""
+    Rows come in blocks of 64; block ``i`` of sequence ``b`` holds rows
+    ``64 i .. 64 i + 63`` of every KV head: ``k`` is ``[batch, capacity / 64,
+    n_kv, 64, head_dim]`` and ``v``, transposed within the block, is ``[batch,
+    capacity / 64, n_kv, head_dim, 64]`` (the paged pools' layout with the
+    blocks of a sequence in order). ``k_rows()`` and ``vt_rows()`` return
+    row-major copies. ``lengths`` is the host array of valid rows that the
+    library reads and updates."""
 
     def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int,
                  dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        if capacity <= 0 or capacity % 64:
+            raise ValueError("capacity must be a positive multiple of 64")
         self.batch, self.n_kv_heads, self.head_dim, self.capacity = batch, n_kv_heads, head_dim, capacity
         self.dtype = dtype
-        self.k = torch.empty((batch, n_kv_heads, capacity, head_dim), dtype=dtype, device=device)
-        self.v = torch.empty((batch, n_kv_heads, head_dim, capacity), dtype=dtype, device=device)
+        nb = capacity // 64
+        self.k = torch.empty((batch, nb, n_kv_heads, 64, head_dim), dtype=dtype, device=device)
+        self.v = torch.empty((batch, nb, n_kv_heads, head_dim, 64), dtype=dtype, device=device)
         self._len = (C.c_int32 * max(batch, 1))()
         self.lengths = np.ctypeslib.as_array(self._len)[:batch]
         self.desc = _lib.KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(),
                                      C.cast(self._len, C.POINTER(C.c_int32)), batch, capacity)
+
+    def k_rows(self) -> torch.Tensor:
+        """K as ``[batch, n_kv, capacity, head_dim]`` (a copy)."""
+        return self.k.permute(0, 2, 1, 3, 4).reshape(self.batch, self.n_kv_heads, self.capacity, self.head_dim)
+
+    def vt_rows(self) -> torch.Tensor:
+        """V transposed, ``[batch, n_kv, head_dim, capacity]`` (a copy)."""
+        return self.v.permute(0, 2, 3, 1, 4).reshape(self.batch, self.n_kv_heads, self.head_dim, self.capacity)
 
     def set_lengths(self, lengths: Sequence[int]) -> None:
         self.lengths[:] = np.asarray(lengths, dtype=np.int32)
@@ -78,14 +93,28 @@ class KVCache:
         """Place rows ``[0, L)`` of sequence ``seq`` (``k``, ``v``: ``[n_kv, L, d]``)
         and set its length to L."""
         L = k.shape[1]
-        self.k[seq, :, :L].copy_(k)
-        self.v[seq, :, :, :L].copy_(v.transpose(1, 2))
+        if L > self.capacity:
+            raise ValueError("prefix longer than the capacity")
+        full, rest = divmod(L, 64)
+        nkv, d = self.n_kv_heads, self.head_dim
+        if full:
+            kb = k[:, :full * 64].reshape(nkv, full, 64, d)
+            vb = v[:, :full * 64].reshape(nkv, full, 64, d)
+            self.k[seq, :full].copy_(kb.transpose(0, 1))
+            self.v[seq, :full].copy_(vb.permute(1, 0, 3, 2))
+        if rest:
+            self.k[seq, full, :, :rest].copy_(k[:, full * 64:])
+            self.v[seq, full, :, :, :rest].copy_(v[:, full * 64:].transpose(1, 2))
         self.lengths[seq] = L
 
     def read(self, seq: int):
-        """Valid rows of sequence ``seq`` as ``(k, v)``, each ``[n_kv, len, d]``."""
+        """Valid rows of sequence ``seq`` as ``(k, v)``, each ``[n_kv, len, d]`` (copies)."""
         L = int(self.lengths[seq])
-        return self.k[seq, :, :L], self.v[seq, :, :, :L].transpose(1, 2)
+        nb = -(-L // 64)
+        nkv, d = self.n_kv_heads, self.head_dim
+        k = self.k[seq, :nb].transpose(0, 1).reshape(nkv, nb * 64, d)[:, :L]
+        v = self.v[seq, :nb].permute(1, 0, 3, 2).reshape(nkv, nb * 64, d)[:, :L]
+        return k, v
 
     def crop(self, seq: int, new_len: int) -> None:
         check(_lib.lib().dflash_cache_crop(C.byref(self.desc), int(seq), int(new_len)), "dflash_cache_crop")

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
       const int c = (lane % CPR) ^ kswz<T, CPR>(row);
       kdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
     }
-    const int vstride = a.map.vstride();  // elements between V^T rows (cap, or 64 in a paged pool)
+    const int vstride = a.map.vstride();  // elements between V^T rows of a 64-row block
 #pragma unroll
     for (int i = 0; i < KPP; ++i) {
       const int blk = i * kProducerWaves + pw, row = blk * (64 / VCPR) + lane / VCPR;
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
       const uint32_t sl = lds0 + (uint32_t)(n % S) * TILE;
       const void* kt;
       const void* vt;
-      if (!paged) {
-        kt = uniform_ptr(Kc + (pair * a.cap + (size_t)cur.tile * KT) * D * sizeof(T));
-        vt = uniform_ptr(Vc + (pair * D * a.cap + (size_t)cur.tile * KT) * sizeof(T));
-      } else {
-        const size_t blk = (size_t)a.map.clamp_block(phys) * nkv + cur.j, off = (size_t)(cur.tile * KT) % kKeyTile;
+      {
+        // the tile's 64-row block (CacheMap::block_of; the table entry was loaded ahead)
+        const size_t pb = paged ? (size_t)a.map.clamp_block(phys)
+                                : (size_t)cur.b * (a.cap / kKeyTile) + (size_t)(cur.tile * KT) / kKeyTile;
+        const size_t blk = pb * nkv + cur.j, off = (size_t)(cur.tile * KT) % kKeyTile;
         kt = uniform_ptr(Kc + (blk * kKeyTile + off) * D * sizeof(T));
         vt = uniform_ptr(Vc + (blk * D * kKeyTile + off) * sizeof(T));
       }

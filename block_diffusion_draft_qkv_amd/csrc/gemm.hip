@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
   // before the main loop (nothing waits for them until the epilogue).
   constexpr int MH = MI / 2;
   int sb[MI], win[MI], crow[MI], pos[MH];  // sequence, window row, cache row; positions
-  int blk[MI];                             // physical block of the row (paged cache)
+  int blk[MI];                             // the row's 64-row cache block (CacheMap::block_of)
   bool ok[MI];
   if (wave < kGemmConsumers) {
     // The sequences a wave's rows touch are few and found with wave-uniform
@@ -625,11 +625,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
         pos[u] = a.positions[pi];
       }
     }
-    // A paged cache's physical block of each row, loaded with the positions.
-    if (a.map.bt != nullptr) {
+    // The cache block of each row (a paged cache's from its table, loaded with the positions).
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) blk[mi] = ok[mi] ? a.map.phys(sb[mi], crow[mi]) : 0;
-    }
+    for (int mi = 0; mi < MI; ++mi) blk[mi] = ok[mi] ? (int)a.map.block_of(sb[mi], crow[mi]) : 0;
   }
 
   f32x4 acc[NI][MI];
@@ -651,10 +649,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!ok[mi]) continue;
-      const int b = sb[mi];
-      const size_t col = a.map.bt == nullptr
-                             ? (size_t)(b * nkv + j) * D * a.cap + crow[mi]
-                             : ((size_t)blk[mi] * nkv + j) * D * kKeyTile + crow[mi] % kKeyTile;
+      const size_t col = ((size_t)blk[mi] * nkv + j) * D * kKeyTile + crow[mi] % kKeyTile;
       const size_t col0 = col + (size_t)(wn * HALF) * vs;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
@@ -736,9 +731,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
         const int i = (J.m0 + wm * WM + mi * 16 + r16) % bs;
         dst = static_cast<T*>(a.qpack) + ((size_t)(b * nkv + j) * R + i * g + hh) * D;
       } else {
-        dst = kc + (a.map.bt == nullptr
-                        ? ((size_t)(b * nkv + j) * a.cap + crow[mi]) * D
-                        : (((size_t)blk[mi] * nkv + j) * kKeyTile + crow[mi] % kKeyTile) * D);
+        dst = kc + (((size_t)blk[mi] * nkv + j) * kKeyTile + crow[mi] % kKeyTile) * D;
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {

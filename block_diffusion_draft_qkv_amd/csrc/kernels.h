@@ -49,13 +49,13 @@ hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_
                        int kslices, hipStream_t stream);
 
 // ------------------------------------------------------------- cache layout
-// Where cache row `row` of sequence b, KV head j lives. Contiguous: K
-// [B][nkv][cap][d], V transposed [B][nkv][d][cap]. Paged (bt != nullptr):
-// 64-row blocks; logical block i of sequence b is physical block
-// bt[b * bt_stride + i] of the pools K [blocks][nkv][64][d] and V
-// [blocks][nkv][d][64]. Table entries are clamped into [0, num_blocks) (the
-// host checks its mirror of the table; the clamp keeps a stale device table
-// inside the pools).
+// Where cache row `row` of sequence b, KV head j lives. Rows come in 64-row
+// blocks of every head, K [blocks][nkv][64][d] and V transposed within the
+// block [blocks][nkv][d][64]. Contiguous: sequence b owns blocks
+// b * (cap / 64) ... in order. Paged (bt != nullptr): logical block i of
+// sequence b is physical block bt[b * bt_stride + i]; table entries are
+// clamped into [0, num_blocks) (the host checks its mirror of the table; the
+// clamp keeps a stale device table inside the pools).
 struct CacheMap {
   const int32_t* bt;
   int32_t bt_stride, num_blocks, cap, nkv;
@@ -74,17 +74,23 @@ struct CacheMap {
     using ctab = const __attribute__((address_space(4))) int32_t;
     return ((ctab*)bt)[(size_t)b * bt_stride + row / kKeyTile];
   }
+  // Both layouts are block-major: block p holds rows of every KV head,
+  // K [p][nkv][64][d] and V^T [p][nkv][d][64]. A paged cache's block comes
+  // from its table; a contiguous cache's row `row` of sequence b is in block
+  // b * (cap / 64) + row / 64.
+  __device__ inline size_t block_of(int b, int row) const {
+    if (bt) return (size_t)phys(b, row);
+    return (size_t)b * (cap / kKeyTile) + row / kKeyTile;
+  }
   // element offset of K row `row`
   __device__ inline size_t k_row(int b, int j, int row, int d) const {
-    if (!bt) return ((size_t)(b * nkv + j) * cap + row) * d;
-    return (((size_t)phys(b, row) * nkv + j) * kKeyTile + row % kKeyTile) * d;
+    return ((block_of(b, row) * nkv + j) * kKeyTile + row % kKeyTile) * d;
   }
   // element offset of V^T (dim 0, row `row`); dim dd adds dd * vstride()
   __device__ inline size_t v_col(int b, int j, int row, int d) const {
-    if (!bt) return (size_t)(b * nkv + j) * d * cap + row;
-    return ((size_t)phys(b, row) * nkv + j) * d * kKeyTile + row % kKeyTile;
+    return (block_of(b, row) * nkv + j) * d * kKeyTile + row % kKeyTile;
   }
-  __device__ inline int vstride() const { return bt ? kKeyTile : cap; }
+  __device__ static constexpr int vstride() { return kKeyTile; }
 };
 
 // ------------------------------------------------- norm + RoPE + append + Q
@@ -98,8 +104,8 @@ struct NormRopeArgs {
   const void* q_norm;
   const void* k_norm;
   void* qpack;             // [B*nkv][R][d]: R = bs*g rows ordered (i, hh)
-  void* kc;                // cache K [B][nkv][cap][d]
-  void* vc;                // cache V [B][nkv][d][cap]
+  void* kc;                // cache K (CacheMap layout)
+  void* vc;                // cache V^T (CacheMap layout)
   int32_t* err;
   int32_t nq, nkv, bs, cap, max_pos;
   float eps, qscale;

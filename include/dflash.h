@@ -95,10 +95,17 @@ typedef struct {
 } dflash_weights;
 
 /* Draft KV cache of `batch` sequences, device memory owned by the caller.
- *   k: [batch][n_kv][capacity][head_dim]   K rows, key-major
- *   v: [batch][n_kv][head_dim][capacity]   V stored transposed (key index
- *                                          contiguous), so that the P*V
- *                                          contraction streams it directly
+ * Rows come in blocks of 64 (capacity / 64 blocks per sequence); block i of
+ * sequence b holds rows 64 i .. 64 i + 63 of every KV head:
+ *   k: [batch][capacity / 64][n_kv][64][head_dim]   K rows, key-major
+ *   v: [batch][capacity / 64][n_kv][head_dim][64]   V transposed within the
+ *                                          block (key index contiguous), so
+ *                                          that the P*V contraction streams
+ *                                          it directly
+ * Every 64-key tile of one head is one contiguous piece of K and one of V, at
+ * the same offsets whatever the capacity. (Row-major [batch][n_kv][capacity]
+ * slabs put every sequence and head a capacity-dependent stride apart, and
+ * some strides made the streams of concurrent work-groups collide in HBM.)
  *   len: HOST array [batch], the valid rows of each sequence; it is the
  *        authoritative length (kernels receive it by value).
  * K holds post-norm, post-RoPE keys; V holds raw values. Rows at or past len
@@ -109,7 +116,7 @@ typedef struct {
  * "qwen3_dflash", whose cache update writes each row to the slot its
  * slot_mapping names): rows come in blocks of 64; logical block i of sequence
  * b (rows 64 i .. 64 i + 63) is physical block block_table[b * max_blocks + i]
- * of the pools
+ * of the pools (the contiguous layout with the blocks taken from a table)
  *   k: [num_blocks][n_kv][64][head_dim]
  *   v: [num_blocks][n_kv][head_dim][64]    (transposed within the block)
  * and capacity must equal 64 * max_blocks. block_table (device) is what the

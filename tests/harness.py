@@ -121,20 +121,27 @@ def raw_bits(t: torch.Tensor) -> np.ndarray:
     return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).cpu().numpy()
 
 
+def cache_bits(cache):
+    """Raw bits of a contiguous cache in row-major form: K ``[B, nkv, cap, d]``
+    and V transposed ``[B, nkv, d, cap]``."""
+    return raw_bits(cache.k_rows()), raw_bits(cache.vt_rows())
+
+
 def check_cache_after_step(case: Case, cache, before_k, before_v, new_cache: oracle.OracleCache):
     """New rows [L_b, T_b) match the oracle; every other row of K and V (the
     dead ones past T_b hold a NaN canary) is bit-identical to what it was;
     lengths equal T_b exactly."""
     L, T = case.cached_len, case.total_len
     assert cache.lengths.tolist() == T.tolist()
-    k_bits, v_bits = raw_bits(cache.k), raw_bits(cache.v)
+    k_bits, v_bits = cache_bits(cache)
+    k_rows, vt_rows = cache.k_rows(), cache.vt_rows()
     for b in range(case.batch):
         lb, tb = int(L[b]), int(T[b])
         np.testing.assert_array_equal(k_bits[b, :, :lb], before_k[b, :, :lb])
         np.testing.assert_array_equal(k_bits[b, :, tb:], before_k[b, :, tb:])
         np.testing.assert_array_equal(v_bits[b, :, :, :lb], before_v[b, :, :, :lb])
         np.testing.assert_array_equal(v_bits[b, :, :, tb:], before_v[b, :, :, tb:])
-        k_new = to64(cache.k[b, :, lb:tb])
-        v_new = to64(cache.v[b, :, :, lb:tb].transpose(1, 2))
+        k_new = to64(k_rows[b, :, lb:tb])
+        v_new = to64(vt_rows[b, :, :, lb:tb].transpose(1, 2))
         assert_close(k_new, new_cache.k[b][:, lb:tb], case.cfg.dtype, f"cache K seq {b}")
         assert_close(v_new, new_cache.v[b][:, lb:tb], case.cfg.dtype, f"cache V seq {b}")

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from harness import assert_close, assert_close_stored, dev, fill_canary, raw_bits, to64
+from harness import assert_close, assert_close_stored, cache_bits, dev, fill_canary, raw_bits, to64
 from workload import CTXKV_CONFIGS, make_ctxkv_case
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
@@ -60,7 +60,7 @@ def run_and_check(case, capacity=None, mode=None):
     if mode is not None:
         pre.set_append_mode(mode)
     caches = make_caches(case, capacity)
-    before = [(raw_bits(c.k), raw_bits(c.v)) for c in caches]
+    before = [cache_bits(c) for c in caches]
     dt = torch_dt(case)
     ctx = dev(case.context_states, dt)
     pos = torch.from_numpy(case.positions.astype(np.int32)).cuda()
@@ -73,7 +73,7 @@ def run_and_check(case, capacity=None, mode=None):
     worst = (0.0, 0.0)
     for layer, kv in enumerate(caches):
         assert kv.lengths.tolist() == (L + n).tolist()
-        kb, vb = raw_bits(kv.k), raw_bits(kv.v)
+        kb, vb = cache_bits(kv)
         bk, bv = before[layer]
         for b in range(case.batch):
             lb, tb = int(L[b]), int(L[b] + n[b])
@@ -82,9 +82,9 @@ def run_and_check(case, capacity=None, mode=None):
             np.testing.assert_array_equal(vb[b, :, :, :lb], bv[b, :, :, :lb])
             np.testing.assert_array_equal(vb[b, :, :, tb:], bv[b, :, :, tb:])
             if tb > lb:
-                e1 = assert_close_stored(to64(kv.k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], case.cfg.dtype,
+                e1 = assert_close_stored(to64(kv.k_rows()[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], case.cfg.dtype,
                                          f"layer {layer} K seq {b}")
-                e2 = assert_close_stored(to64(kv.v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                e2 = assert_close_stored(to64(kv.vt_rows()[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
                                          case.cfg.dtype, f"layer {layer} V seq {b}")
                 worst = (max(worst[0], e1[0], e2[0]), max(worst[1], e1[1], e2[1]))
     return pre, caches, ref, worst
@@ -126,8 +126,8 @@ def test_context_kv_prefill_rows_sampled():
     for layer, kv in enumerate(caches):
         assert kv.lengths.tolist() == [4096]
         for i, r in enumerate(rows):
-            assert_close_stored(to64(kv.k[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
-            assert_close_stored(to64(kv.v[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
+            assert_close_stored(to64(kv.k_rows()[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
+            assert_close_stored(to64(kv.vt_rows()[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
                                 f"layer {layer} V row {r}")
 
 
@@ -242,7 +242,7 @@ def test_fc_then_precompute_matches_oracle(name):
         for b in range(case.batch):
             lb, tb = int(L[b]), int(L[b] + n[b])
             if tb > lb:
-                assert_close_stored(to64(kv.k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], case.cfg.dtype,
+                assert_close_stored(to64(kv.k_rows()[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], case.cfg.dtype,
                                     f"layer {layer} K seq {b}")
-                assert_close_stored(to64(kv.v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                assert_close_stored(to64(kv.vt_rows()[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
                                     case.cfg.dtype, f"layer {layer} V seq {b}")

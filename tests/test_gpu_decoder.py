@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from harness import (check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64,
+from harness import (cache_bits, check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64,
                      torch_dtype)
 from workload import LayerConfig, make_case, make_mlp_weights
 
@@ -69,7 +69,7 @@ def test_decoder_layer_matches_oracle(name):
     print(f"[{name}] batch {case.batch}, keys {int(case.total_len.sum())}, intermediate {inter}", flush=True)
     dec = make_decoder(case, mw)
     cache = make_cache(case)
-    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    bk, bv = cache_bits(cache)
     x, th, pos = step_inputs(case)
     out = dec.step(x, th, case.ctx_offsets, pos, cache)
     torch.cuda.synchronize()

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import (assert_close, check_cache_after_step, make_cache, make_layer, raw_bits,
+from harness import (assert_close, cache_bits, check_cache_after_step, make_cache, make_layer, raw_bits,
                      run_oracle, step_inputs, to64)
 from workload import make_case
 
@@ -23,7 +23,7 @@ def test_full_config_step_and_crop(name):
     print(f"[{name}] batch {case.batch}, keys {int(case.total_len.sum())}", flush=True)
     layer = make_layer(case)
     cache = make_cache(case)
-    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    bk, bv = cache_bits(cache)
     hs, th, pos = step_inputs(case)
     out = layer.step(hs, th, case.ctx_offsets, pos, cache)
     torch.cuda.synchronize()

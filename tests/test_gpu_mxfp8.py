@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from harness import assert_close_stored, dev, raw_bits, to64
+from harness import assert_close_stored, cache_bits, dev, raw_bits, to64
 from test_gpu_context_kv import make_caches, oracle_caches
 from workload import make_ctxkv_case, make_mxfp8_kv_weights, round_bf16
 
@@ -82,7 +82,7 @@ def run_mx(case, seed):
     mx = make_mxfp8_kv_weights(case.cfg, seed)
     pre = make_mx_precompute(case, mx)
     caches = make_caches(case)
-    before = [(raw_bits(c.k), raw_bits(c.v)) for c in caches]
+    before = [cache_bits(c) for c in caches]
     pos = torch.from_numpy(case.positions.astype(np.int32)).cuda()
     pre.append(dev(case.context_states, torch.bfloat16), case.ctx_offsets, pos, caches)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def test_mxfp8_precompute_matches_oracle(name):
     worst = (0.0, 0.0)
     for layer, kv in enumerate(caches):
         assert kv.lengths.tolist() == (L + n).tolist()
-        kb, vb = raw_bits(kv.k), raw_bits(kv.v)
+        kb, vb = cache_bits(kv)
         bk, bv = before[layer]
         for b in range(case.batch):
             lb, tb = int(L[b]), int(L[b] + n[b])
@@ -110,9 +110,9 @@ def test_mxfp8_precompute_matches_oracle(name):
             np.testing.assert_array_equal(vb[b, :, :, :lb], bv[b, :, :, :lb])
             np.testing.assert_array_equal(vb[b, :, :, tb:], bv[b, :, :, tb:])
             if tb > lb:
-                e1 = assert_close_stored(to64(kv.k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], "bf16",
+                e1 = assert_close_stored(to64(kv.k_rows()[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], "bf16",
                                          f"layer {layer} K seq {b}")
-                e2 = assert_close_stored(to64(kv.v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                e2 = assert_close_stored(to64(kv.vt_rows()[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
                                          "bf16", f"layer {layer} V seq {b}")
                 worst = (max(worst[0], e1[0], e2[0]), max(worst[1], e1[1], e2[1]))
     print(f"[mxfp8 {name}] max abs {worst[0]:.3e} rel-RMS {worst[1]:.3e}", flush=True)
@@ -133,8 +133,8 @@ def test_mxfp8_prefill_rows_sampled():
     for layer, kv in enumerate(caches):
         assert kv.lengths.tolist() == [4096]
         for i, r in enumerate(rows):
-            assert_close_stored(to64(kv.k[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
-            assert_close_stored(to64(kv.v[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
+            assert_close_stored(to64(kv.k_rows()[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
+            assert_close_stored(to64(kv.vt_rows()[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
                                 f"layer {layer} V row {r}")
 
 

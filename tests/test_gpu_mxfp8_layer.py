@@ -25,7 +25,7 @@ import pytest
 import torch
 
 import oracle
-from harness import check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64
+from harness import cache_bits, check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64
 from workload import LayerConfig, make_case, make_mxfp8_layer_weights
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
@@ -62,7 +62,7 @@ def run_mx(case, seed=0):
     mw = make_mxfp8_layer_weights(case.cfg, seed)
     layer = mx_layer(case, mw)
     cache = make_cache(case)
-    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    bk, bv = cache_bits(cache)
     hs, th, pos = step_inputs(case)
     print(f"[mxfp8 step {case.cfg.name}] B={case.batch} keys={int(case.total_len.sum())}", flush=True)
     out = layer.step(hs, th, case.ctx_offsets, pos, cache)
@@ -124,3 +124,58 @@ def test_mxfp8_layer_rejects_what_it_does_not_support():
         DFlashLayer(f32, torch.from_numpy(mw.w_qkv_codes).cuda(), torch.from_numpy(mw.w_o_codes).cuda(),
                     dev(case.weights.q_norm, torch.float32), dev(case.weights.k_norm, torch.float32),
                     w_qkv_scale=u8, w_o_scale=u8)
+
+
+def test_mxfp8_layer_step_paged_matches_oracle():
+    """The MXFP8 step on a paged cache with shuffled blocks and a NaN canary:
+    output to the bound above, new rows to the stored-value bound, every other
+    slot untouched."""
+    from test_gpu_paged import check_paged_after, make_paged
+    case = make_case(small(batch=4, config_id=87), seed=4)
+    mw = make_mxfp8_layer_weights(case.cfg, 3)
+    layer = mx_layer(case, mw)
+    cache = make_paged(case, seed=6)
+    for b in range(case.batch):
+        cache.reserve(b, int(case.total_len[b]))
+    cache.sync()
+    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    hs, th, pos = step_inputs(case)
+    out = layer.step(hs, th, case.ctx_offsets, pos, cache)
+    torch.cuda.synchronize()
+    assert layer.poll_error() == 0
+    args = (case.cfg, MXLayerOracleWeights(mw, case.weights), oracle.OracleCache.from_arrays(case.cache_k, case.cache_v),
+            case.hidden_states, case.target_hidden if case.target_hidden.size else None, case.ctx_offsets,
+            case.positions)
+    ref, new = oracle.layer_step_mxfp8(*args)
+    ref_noq, _ = oracle.layer_step_mxfp8(*args, quantise_o=False)
+    max_abs, rel = errors(to64(out), ref)
+    _, rel_noq = errors(ref_noq, ref)
+    print(f"[mxfp8 paged step] max abs {max_abs:.3e} rel-RMS {rel:.3e} (unquantised: {rel_noq:.3e})", flush=True)
+    assert max_abs <= 5e-2 and rel <= 3e-2 and rel <= 0.5 * rel_noq, (max_abs, rel, rel_noq)
+    assert cache.lengths.tolist() == case.total_len.tolist()
+    check_paged_after(cache, bk, bv, case.cached_len, case.total_len, new, "bf16", "mxfp8 paged")
+
+
+def test_mxfp8_layer_step_c3_paged_is_bit_identical_to_contiguous():
+    """Same tiles and the same order of every sum on either cache layout."""
+    case = make_case("C3", seed=1)
+    mw = make_mxfp8_layer_weights(case.cfg, 1)
+    layer = mx_layer(case, mw)
+    hs, th, pos = step_inputs(case)
+    from test_gpu_paged import make_paged
+    flat = make_cache(case)
+    print("[mxfp8 C3 contiguous vs paged]", flush=True)
+    out_flat = layer.step(hs, th, case.ctx_offsets, pos, flat).clone()
+    cache = make_paged(case, seed=8)
+    for b in range(case.batch):
+        cache.reserve(b, int(case.total_len[b]))
+    cache.sync()
+    out = layer.step(hs, th, case.ctx_offsets, pos, cache)
+    torch.cuda.synchronize()
+    assert layer.poll_error() == 0
+    assert torch.equal(out.view(torch.int16), out_flat.view(torch.int16))
+    for b in (0, 13, 31):
+        k, v = cache.read(b)
+        kf, vf = flat.read(b)
+        assert torch.equal(k.contiguous().view(torch.int16), kf.contiguous().view(torch.int16))
+        assert torch.equal(v.contiguous().view(torch.int16), vf.contiguous().view(torch.int16))

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from harness import (assert_close, check_cache_after_step, make_cache, make_layer, raw_bits,
+from harness import (assert_close, cache_bits, check_cache_after_step, make_cache, make_layer, raw_bits,
                      run_oracle, step_inputs, to64)
 from workload import CONFIGS, LayerConfig, make_case
 
@@ -25,7 +25,7 @@ def run_and_check(case, capacity=None, append_mode=None):
     if append_mode is not None:
         layer.set_append_mode(append_mode)
     cache = make_cache(case, capacity)
-    bk, bv = raw_bits(cache.k), raw_bits(cache.v)
+    bk, bv = cache_bits(cache)
     hs, th, pos = step_inputs(case)
     out = layer.step(hs, th, case.ctx_offsets, pos, cache)
     torch.cuda.synchronize()
