@@ -38,7 +38,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_splitkv_c3_traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", "attention.hip")
+# every source the attention kernel is compiled from
+ATTN_SOURCES = [os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", f)
+                for f in ("attention.hip", "kernels.h", "common.h", "lds_dma.h")]
 
 
 def parse():
@@ -61,6 +63,8 @@ def parse():
                     help="timed C3 steps on the paged cache, and as many driver rounds (0: skip)")
     ap.add_argument("--mxfp8-steps", type=int, default=50,
                     help="timed C3 steps of the layer with MXFP8 projections (0: skip)")
+    ap.add_argument("--other-steps", type=int, default=30,
+                    help="steps of the C4 and C5 layer step measurements (0 skips them)")
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="only time the C3 layer step with MXFP8 projections (for profiling)")
     ap.add_argument("--decoder-only", action="store_true",
@@ -72,18 +76,24 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload: str):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
+    None when there is none, it covers another workload, or the kernel's
+    sources changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+    if not rec.get("workload", "").startswith(workload):
+        return None
+    if rec.get("attention_source_sha256_16") != source_hash(ATTN_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -318,6 +328,95 @@ def bench_decoder(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     dec.close()
     del caches
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_other_configs(names, steps: int, warmup: int, seed: int = 0, copies: int = 2):
+    """The layer step at the other full-size workloads (C4 long context, C5
+    sliding window): wall-clock step time, then the same steps with HIP
+    events for the attention kernel against its algorithmic bytes (in-band
+    keys only under the window)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_draft_qkv_amd import DFlashLayer, KVCache, LayerShape
+    from workload import make_case
+
+    res = {}
+    for name in names:
+        case = make_case(name, seed=seed)
+        cfg = case.cfg
+        B, bs, H = case.batch, cfg.block_size, cfg.hidden
+        nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        es = 2 if cfg.dtype == "bf16" else 4
+
+        def dev(x, dtype=dt):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+        w = case.weights
+        layer = DFlashLayer(LayerShape(H, nq, nkv, d, bs, dt, cfg.rope_theta, cfg.rms_eps, cfg.sliding_window,
+                                       cfg.max_position), dev(w.w_qkv), dev(w.w_o), dev(w.q_norm), dev(w.k_norm))
+        caches = []
+        for i in range(copies):
+            c = KVCache(B, nkv, d, case.capacity(), dt)
+            if i == 0:
+                for b in range(B):
+                    c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
+            else:
+                c.k.copy_(caches[0].k)
+                c.v.copy_(caches[0].v)
+                c.set_lengths(case.cached_len)
+            caches.append(c)
+        hs = dev(case.hidden_states)
+        th = dev(case.target_hidden) if case.target_hidden.size else None
+        pos = dev(case.positions, torch.int32)
+        offs = [int(o) for o in case.ctx_offsets]
+        out = torch.empty((B * bs, H), dtype=dt, device="cuda")
+        ws = layer.workspace(B, offs[-1])
+        L0 = case.cached_len.copy()
+        accepted = (case.cached_len + case.new_ctx + case.accept).tolist()
+
+        def one(i):
+            c = caches[i % copies]
+            layer.step(hs, th, offs, pos, c, out=out, workspace=ws)
+            c.crop_all(accepted)
+            c.set_lengths(L0)
+
+        for i in range(warmup):
+            one(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one(warmup + i)
+        torch.cuda.synchronize()
+        t_step = (time.perf_counter() - t0) / steps
+        layer.set_profiling(True)
+        for i in range(steps):
+            one(i)
+        torch.cuda.synchronize()
+        kt = layer.kernel_times()
+        layer.set_profiling(False)
+        if layer.poll_error() != 0:
+            raise RuntimeError(f"{name}: device-side error")
+        T = case.total_len.astype(np.int64)
+        keys = np.minimum(T, cfg.sliding_window + bs - 1) if cfg.sliding_window else T
+        attn_bytes = int(keys.sum()) * nkv * d * 2 * es + 2 * B * bs * nq * d * es
+        ms, n = kt["attn"]
+        t_attn = ms * 1e3 / n
+        res[name] = {
+            "workload": (f"B={B}, cached ctx {cfg.cached_len}, new ctx {cfg.new_ctx}, block {bs}, "
+                         f"window {cfg.sliding_window or 'none'}"),
+            "ms_per_step": round(t_step * 1e3, 4),
+            "tokens_per_s": round(B * bs / t_step, 1),
+            "attn_us": round(t_attn, 2),
+            "attn_algorithmic_bytes": attn_bytes,
+            "attn_hbm_frac": round(attn_bytes / (t_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_mean_us": {k: round(v[0] * 1e3 / v[1], 2) for k, v in kt.items() if v[1]},
+        }
+        layer.close()
+        del caches
+        torch.cuda.empty_cache()
     return res
 
 
@@ -596,7 +695,7 @@ def main():
     t_merge = mean_us("merge")
     t_proj = mean_us("gemm_qkv") + mean_us("gemm_o")
     achieved = attn_bytes / (t_attn * 1e-6) / 1e9
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(f"{cfg.name}: ") if a.seed == 0 else None
 
     line = {
         "metric": METRIC,
@@ -625,7 +724,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attn_splitkv_kernel<bf16,128>",
+            "kernel": f"attn_splitkv_kernel<{cfg.dtype},{d}>",
             "algorithmic_bytes_per_launch": attn_bytes,
             "mean_launch_us": round(t_attn, 2),
         },
@@ -654,6 +753,8 @@ def main():
         line["paged"] = bench_paged(a.paged_steps, 10)
     if a.mxfp8_steps > 0:
         line["mxfp8_layer_step"] = bench_mxfp8_layer(a.mxfp8_steps, 10)
+    if a.other_steps > 0:
+        line["other_configs"] = bench_other_configs(("C4", "C5"), a.other_steps, 5)
     print(json.dumps(line), flush=True)
 
 
