@@ -117,6 +117,30 @@ def test_capacity_exactly_full():
     run_and_check(case, capacity=cap)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_capacity_changes_addresses_only(dtype):
+    """The same step on caches of three capacities: the output and every
+    valid cache row bit-identical (the capacity moves where a sequence's
+    blocks start, nothing else)."""
+    case = make_case(small(dtype=dtype, batch=4, config_id=25), seed=1)
+    layer = make_layer(case)
+    hs, th, pos = step_inputs(case)
+    base = case.capacity()
+    outs, rows = [], []
+    for cap in (base, base + 64, base + 192):
+        cache = make_cache(case, cap)
+        print(f"[capacity {cap}]", flush=True)
+        outs.append(layer.step(hs, th, case.ctx_offsets, pos, cache).clone())
+        torch.cuda.synchronize()
+        rows.append([cache.read(b) for b in range(case.batch)])
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    for o, r in zip(outs[1:], rows[1:]):
+        assert torch.equal(o.view(bits), outs[0].view(bits))
+        for (k, v), (k0, v0) in zip(r, rows[0]):
+            assert torch.equal(k.contiguous().view(bits), k0.contiguous().view(bits))
+            assert torch.equal(v.contiguous().view(bits), v0.contiguous().view(bits))
+
+
 def test_max_batch():
     cfg = small(batch=256, hidden=128, n_q_heads=2, n_kv_heads=1, head_dim=64, block_size=4,
                 cached_len=(0, 130), new_ctx=(0, 3), config_id=19)
