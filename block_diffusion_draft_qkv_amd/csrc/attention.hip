@@ -12,9 +12,15 @@
 // tile of up to 64 rows; consumer wave w (0-3) of the work-group owns rows
 // 16w .. 16w+15. Every (sequence b, KV head j) pair owns the key tiles
 // [lo_b, hi_b) (lo_b > 0 only under a sliding window); all tiles of all pairs
-// are flattened b-major and cut into G equal ranges, one per work-group, so
-// every work-group streams the same number of key tiles whatever the ragged
-// lengths. A range crosses pair boundaries; the part of a pair inside a range
+// are flattened head-major (j, then b, then tile) and cut into G equal ranges,
+// one per work-group, so every work-group streams the same number of key
+// tiles whatever the ragged lengths. With G a multiple of nkv every head's
+// tiles split at the same places, and the host deals the ranges so that the
+// nkv work-groups covering the same tiles of all heads run on one XCD: they
+// read neighbouring pieces of the same cache blocks together (measured at C3:
+// 95 us against 108 us for b-major ranges dealt in contiguous runs of w,
+// whose concurrent reads scatter over the cache whenever lengths are ragged).
+// A range crosses pair boundaries; the part of a pair inside a range
 // is a segment. A segment that is a whole pair writes the output directly; a
 // pair cut by a range boundary leaves fp32 partials (un-normalised O, exponent
 // offset, sum) in slot 2w (the range's first segment) or 2w+1 (its last),
@@ -102,14 +108,6 @@ __device__ inline void seq_tiles(const AttnArgs& a, int b, int kt, int& lo, int&
 __device__ inline int64_t bound_of(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
 __device__ inline int64_t owner_of(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
 
-// Range handled by work-group `bid`. Work-groups are dealt to the 8 XCDs
-// round-robin (bid % 8); giving each XCD a contiguous block of ranges spreads
-// every KV head and sequence over all XCDs instead of pinning XCD x to the
-// ranges x, x+8, ..., which measured up to 5 % slower on some XCDs.
-__device__ inline int range_of_block(int bid, int G) {
-  const int x = bid % 8, per = G / 8, extra = G % 8;
-  return x * per + (x < extra ? x : extra) + bid / 8;
-}
 
 // Which key each lane's S^T accumulator row stands for (see the file comment).
 template <typename T> __device__ inline int key_of(int kb, int m);
@@ -238,7 +236,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkv = a.nkv, R = a.R;
-  const int64_t N = a.total_tiles, G = a.G, w = range_of_block(blockIdx.x, (int)G);
+  const int64_t N = a.total_tiles, G = a.G, w = a.range_of[blockIdx.x];
   const int total = (int)(bound_of(w + 1, N, G) - bound_of(w, N, G));
   const uint32_t lds0 = lds_base(lds);
   const uint32_t qlds0 = lds0 + S * TILE;
@@ -259,15 +257,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
   }
   auto advance = [&](Cursor& c) {
     if (++c.tile == c.hi) {
-      if (++c.j == nkv) {
-        c.j = 0;
-        if (++c.b < a.seq.batch) {  // past the last pair the cursor is never used
-          int lo, cnt;
-          seq_tiles(a, c.b, KT, lo, cnt);
-          c.lo = lo;
-          c.hi = lo + cnt;
-        }
+      if (++c.b == a.seq.batch) {  // past the last pair the cursor is never used
+        c.b = 0;
+        ++c.j;
       }
+      int lo, cnt;
+      seq_tiles(a, c.b, KT, lo, cnt);
+      c.lo = lo;
+      c.hi = lo + cnt;
       c.tile = c.lo;
     }
   };

@@ -89,8 +89,33 @@ int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
   int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
   cap = std::min<int64_t>(cap, kMaxGroups);
-  return std::max<int64_t>(1, std::min<int64_t>(cap, n_tiles));
+  // a multiple of nkv when there are enough, so every head gets the same ranges
+  int64_t g = std::min<int64_t>(cap, n_tiles);
+  if (g >= L->cfg.n_kv_heads) g -= g % L->cfg.n_kv_heads;
+  return std::max<int64_t>(1, g);
 }
+
+}  // namespace
+
+void dflash::attn_range_map(int G, int nkv, uint16_t* range_of) {
+  // The ranges in the order the XCDs take them: (i, j) when every head has
+  // G / nkv ranges, else plain order.
+  int order[kMaxGroups];
+  int n = 0;
+  if (nkv > 1 && G % nkv == 0) {
+    const int per = G / nkv;
+    for (int i = 0; i < per; ++i)
+      for (int j = 0; j < nkv; ++j) order[n++] = j * per + i;
+  } else {
+    for (int w = 0; w < G; ++w) order[n++] = w;
+  }
+  // The 8 XCDs take work-groups round-robin: XCD x runs bid = x, x + 8, ...
+  int next = 0;
+  for (int x = 0; x < 8; ++x)
+    for (int bid = x; bid < G; bid += 8) range_of[bid] = (uint16_t)order[next++];
+}
+
+namespace {
 
 Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
   const dflash_config& c = L->cfg;
@@ -538,12 +563,13 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
                  : MxOut{nullptr, nullptr, 0, 0};
   aa.map = cache_map(cache, nkv);
   aa.seq = seq;
+  attn_range_map(aa.G, nkv, aa.range_of);
   // Each work-group's first (pair, tile): walk the pairs in flat order.
   {
     int64_t f = 0;
     int w = 0;
-    for (int b = 0; b < B && w < aa.G; ++b)
-      for (int j = 0; j < nkv && w < aa.G; ++j) {
+    for (int j = 0; j < nkv && w < aa.G; ++j)
+      for (int b = 0; b < B && w < aa.G; ++b) {
         const int64_t end = f + tile_cnt[b];
         for (int64_t fw; w < aa.G && (fw = part_bound(w, n_tiles, aa.G)) < end; ++w)
           aa.start[w] = (uint32_t)(b * nkv + j) | ((uint32_t)(tile_lo[b] + (fw - f)) << 16);
@@ -564,8 +590,8 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   ma.n_split = 0;
   {
     int64_t f = 0;
-    for (int b = 0; b < B; ++b)
-      for (int j = 0; j < nkv; ++j) {
+    for (int j = 0; j < nkv; ++j)
+      for (int b = 0; b < B; ++b) {
         const int64_t e = f + tile_cnt[b];
         const int64_t w0 = part_owner(f, n_tiles, aa.G), w1 = part_owner(e - 1, n_tiles, aa.G);
         if (w0 != w1) {

@@ -176,9 +176,12 @@ struct MxOut {
   int32_t ld, rows;
 };
 
-// Flattened work: pairs (b, j) in b-major order, each owning the 64-key tiles
-// [lo_b, hi_b) of sequence b (lo_b > 0 only under a sliding window). Work-group
-// w takes flat tiles [floor(w N / G), floor((w+1) N / G)).
+// Flattened work: pairs (b, j) in head-major order (j outer, b inner), each
+// owning the 64-key tiles [lo_b, hi_b) of sequence b (lo_b > 0 only under a
+// sliding window). Range w takes flat tiles [floor(w N / G), floor((w+1) N / G)).
+// With G a multiple of nkv, ranges w = j (G / nkv) + i of every head j cover
+// the same sequences and tiles, so the nkv work-groups of one i read the nkv
+// neighbouring 16 KB pieces of the same cache blocks at about the same time.
 struct AttnArgs {
   const void* q;           // qpack
   const void* kc;
@@ -191,10 +194,16 @@ struct AttnArgs {
   int64_t total_tiles;
   CacheMap map;            // cache layout
   SeqTable seq;
-  // Start of work-group w's range: pair b * nkv + j in bits 0..15, absolute key
-  // tile in bits 16..31 (filled by the host, which knows every length).
+  // Start of range w: pair b * nkv + j in bits 0..15, absolute key tile in
+  // bits 16..31 (filled by the host, which knows every length).
   uint32_t start[kMaxGroups];
+  // Range of work-group `bid` (a permutation of [0, G)); see attn_range_map.
+  uint16_t range_of[kMaxGroups];
 };
+// Deals the G ranges to work-groups. Work-groups go to the 8 XCDs round-robin
+// (bid % 8); each XCD gets a contiguous run of the ranges in (i, j) order, so
+// the nkv heads of one i share an XCD and its L2.
+void attn_range_map(int G, int nkv, uint16_t* range_of);
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream);
 // Attention work-groups one CU holds at once (bounded by the kernel's LDS ring)
 // and the keys per attention tile.
