@@ -109,10 +109,12 @@ void dflash::attn_range_map(int G, int nkv, uint16_t* range_of) {
   } else {
     for (int w = 0; w < G; ++w) order[n++] = w;
   }
-  // The 8 XCDs take work-groups round-robin: XCD x runs bid = x, x + 8, ...
+  // The XCDs take work-groups round-robin: XCD x runs bid = x, x + kXcds, ...
+  // (only locality depends on kXcds; any value gives a permutation)
+  constexpr int kXcds = 8;  // MI355X
   int next = 0;
-  for (int x = 0; x < 8; ++x)
-    for (int bid = x; bid < G; bid += 8) range_of[bid] = (uint16_t)order[next++];
+  for (int x = 0; x < kXcds; ++x)
+    for (int bid = x; bid < G; bid += kXcds) range_of[bid] = (uint16_t)order[next++];
 }
 
 namespace {
