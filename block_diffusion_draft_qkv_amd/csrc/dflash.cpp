@@ -611,8 +611,15 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     record_end(L, DFLASH_K_MERGE, ev, s);
   }
 
-  // HK1: o_proj
-  const TileChoice to = choose_tiles(L, Mq, H, 0, 0, false);
+  // HK1: o_proj. Too few rows for the CUs (a small batch) and a weight large
+  // enough that streaming it dominates (>= 4 MB; below that the extra launch
+  // costs more): k split over fp32 slices in the q|k|v region of the workspace
+  // (its contents are consumed by now), summed into out with one rounding.
+  const bool o_big = (int64_t)H * nq * d * elem_size(c) >= (4 << 20);
+  const TileChoice to = choose_tiles(L, Mq, H, 0, 0, !L->mx && o_big);
+  const int64_t o_slice = (int64_t)Mq * H;
+  const bool o_split = to.kslices > 1 && (size_t)to.kslices * o_slice * 4 <=
+                                             (size_t)kMaxKSlices * Mq * (nq + 2 * nkv) * d * 4;
   GemmArgs go;
   std::memset(&go, 0, sizeof(go));
   go.nprob = 1;
@@ -624,6 +631,13 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     go.p[0].sa = aa.mxo.scales;
     go.p[0].sb = L->wo_scale;
     if (launch_gemm_mx(go, to.tiles, to.bm, to.bn, s) != hipSuccess) return DFLASH_ERR_HIP;
+  } else if (o_split) {
+    float* part = reinterpret_cast<float*>(ws + wc.qkv);
+    go.p[0].c = part;
+    go.p[0].slice_stride = o_slice;
+    if (launch_gemm(c.dtype, true, go, to.tiles, to.bm, to.bn, to.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (launch_sum_slices(c.dtype == DFLASH_BF16 ? 1 : 0, part, to.kslices, o_slice, out, o_slice, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
   } else if (launch_gemm(c.dtype, false, go, to.tiles, to.bm, to.bn, 1, s) != hipSuccess) {
     return DFLASH_ERR_HIP;
   }
