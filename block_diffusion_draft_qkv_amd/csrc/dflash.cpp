@@ -85,12 +85,17 @@ namespace {
 int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Attention work-groups for N flat tiles: as many as the CUs hold at once
-// (the kernel's LDS ring bounds that), never more than there are tiles.
+// (the kernel's LDS ring bounds that), fewer when the tiles are few.
 int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
   int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
   cap = std::min<int64_t>(cap, kMaxGroups);
-  // a multiple of nkv when there are enough, so every head gets the same ranges
-  int64_t g = std::min<int64_t>(cap, n_tiles);
+  // At least 4 tiles a range: a range of one or two tiles is mostly its own
+  // ramp, and every range a pair is cut into is one more part for the merge
+  // (one sequence at 2080 keys: step 0.0524 ms with 1 tile a range, 0.0476 with
+  // 4, 0.0493 with 8). Then a multiple of nkv when there are enough, so every
+  // head gets the same ranges.
+  constexpr int64_t kMinTilesPerRange = 4;
+  int64_t g = std::min<int64_t>(cap, std::max<int64_t>(n_tiles / kMinTilesPerRange, 1));
   if (g >= L->cfg.n_kv_heads) g -= g % L->cfg.n_kv_heads;
   return std::max<int64_t>(1, g);
 }
