@@ -86,16 +86,18 @@ int elem_size(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Attention work-groups for N flat tiles: as many as the CUs hold at once
 // (the kernel's LDS ring bounds that), fewer when the tiles are few.
-int64_t attn_groups(const dflash_layer* L, int64_t n_tiles) {
+int64_t attn_groups(const dflash_layer* L, int64_t n_tiles, int64_t n_pairs) {
   int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
   cap = std::min<int64_t>(cap, kMaxGroups);
   // At least 4 tiles a range: a range of one or two tiles is mostly its own
   // ramp, and every range a pair is cut into is one more part for the merge
   // (one sequence at 2080 keys: step 0.0524 ms with 1 tile a range, 0.0476 with
-  // 4, 0.0493 with 8). Then a multiple of nkv when there are enough, so every
-  // head gets the same ranges.
+  // 4, 0.0493 with 8), but never fewer ranges than pairs while there are tiles
+  // for them (a few short pairs on one range would run one after another). Then
+  // a multiple of nkv when there are enough, so every head gets the same ranges.
   constexpr int64_t kMinTilesPerRange = 4;
-  int64_t g = std::min<int64_t>(cap, std::max<int64_t>(n_tiles / kMinTilesPerRange, 1));
+  int64_t g = std::max<int64_t>(n_tiles / kMinTilesPerRange, std::min<int64_t>(n_tiles, n_pairs));
+  g = std::min<int64_t>(cap, std::max<int64_t>(g, 1));
   if (g >= L->cfg.n_kv_heads) g -= g % L->cfg.n_kv_heads;
   return std::max<int64_t>(1, g);
 }
@@ -473,8 +475,10 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   const int nt64 = ((Mq + 63) / 64) * (Nqkv / d) + (int)((Mc + 63) / 64) * (Nkv / d);
   const int nt128 = ((Mq + 127) / 128) * (Nqkv / d) + (int)((Mc + 127) / 128) * (Nkv / d);
   const int target = L->num_cus * 3 / 4;
-  const bool fused = L->mx || L->append_mode == DFLASH_APPEND_FUSED ||
-                     (L->append_mode == DFLASH_APPEND_AUTO && nt64 >= target);
+  // AUTO fuses at every size: with few rows the separate path's k split and
+  // its norm / RoPE / append launch cost more than the fused tiles save (one
+  // sequence: 0.0484 against 0.0470 ms; C1 0.0392 against 0.0362 ms).
+  const bool fused = L->mx || L->append_mode != DFLASH_APPEND_SEPARATE;
   const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, nt128 >= target ? nt128 : nt64, 1}
                               : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
   GemmArgs ga;
@@ -564,7 +568,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   // A window at least the capacity keeps every key (|query - key| < T_b <= capacity).
   aa.window = c.sliding_window >= cache->capacity ? 0 : c.sliding_window;
   aa.total_tiles = n_tiles;
-  aa.G = (int32_t)attn_groups(L, n_tiles);
+  aa.G = (int32_t)attn_groups(L, n_tiles, (int64_t)B * nkv);
   // an MXFP8 layer's attention writes o_proj's MXFP8 input directly
   aa.mxo = L->mx ? MxOut{reinterpret_cast<uint8_t*>(ws + wc.oq), reinterpret_cast<uint8_t*>(ws + wc.os), nq * d, Mq}
                  : MxOut{nullptr, nullptr, 0, 0};
