@@ -39,6 +39,75 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream or None
 
 
+def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device: torch.device) -> None:
+    """The C ABI takes bare pointers and no sizes, so everything the kernels
+    assume about a tensor is checked here: exact shape, dtype, contiguity and
+    the layer's device (a host tensor would be dereferenced by a kernel)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_workspace(ws: torch.Tensor, device: torch.device) -> None:
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+
+
+def _ctx_offsets(ctx_offsets, batch: int) -> np.ndarray:
+    offs = np.asarray([int(o) for o in ctx_offsets], dtype=np.int64)
+    if offs.shape != (batch + 1,):
+        raise ValueError("ctx_offsets must have batch + 1 entries")
+    if offs[0] != 0 or (np.diff(offs) < 0).any() or offs[-1] > np.iinfo(np.int32).max:
+        raise ValueError("ctx_offsets must start at 0 and be non-decreasing")
+    return offs
+
+
+def _check_cache(cache, shape: "LayerShape", device: torch.device, n_kv_heads: int, head_dim: int) -> None:
+    if not isinstance(cache, (KVCache, PagedKVCache)):
+        raise ValueError("cache must be a KVCache or PagedKVCache")
+    if cache.dtype != shape.dtype or cache.n_kv_heads != n_kv_heads or cache.head_dim != head_dim:
+        raise ValueError("cache dtype, KV heads and head_dim must match the layer")
+    if cache.k.device != device:
+        raise ValueError(f"cache must be on {device}, got {cache.k.device}")
+    if isinstance(cache, PagedKVCache) and cache.table.device != device:
+        raise ValueError(f"the block table must be on {device}")
+
+
+def _check_step_args(shape: "LayerShape", device: torch.device, act_dtype: torch.dtype, x: torch.Tensor,
+                     target_hidden: Optional[torch.Tensor], ctx_offsets, positions: torch.Tensor, cache,
+                     out: Optional[torch.Tensor], workspace: Optional[torch.Tensor], x_name: str):
+    """Host checks of a layer (or decoder) step's arguments; returns the
+    offsets and the target rows to pass (None when there are none)."""
+    _check_cache(cache, shape, device, shape.n_kv_heads, shape.head_dim)
+    B, bs, H = cache.batch, shape.block_size, shape.hidden
+    offs = _ctx_offsets(ctx_offsets, B)
+    mc = int(offs[-1])
+    _check_tensor(x, x_name, act_dtype, (B * bs, H), device)
+    if target_hidden is not None and target_hidden.numel() == 0 and mc == 0:
+        target_hidden = None
+    if mc > 0 or target_hidden is not None:
+        if target_hidden is None:
+            raise ValueError(f"target_hidden is required for {mc} new context rows")
+        _check_tensor(target_hidden, "target_hidden", act_dtype, (mc, H), device)
+    _check_tensor(positions, "positions", torch.int32, (mc + B * bs,), device)
+    if out is not None:
+        _check_tensor(out, "out", act_dtype, (B * bs, H), device)
+        if out.data_ptr() == x.data_ptr():
+            raise ValueError(f"out must not alias {x_name}")
+    if workspace is not None:
+        _check_workspace(workspace, device)
+    return offs, target_hidden
+
+
 @dataclass(frozen=True)
 class LayerShape:
     hidden: int
@@ -171,6 +240,7 @@ class DFlashLayer:
                 check(_lib.lib().dflash_layer_create(C.byref(cfg), C.byref(w), C.byref(handle)),
                       "dflash_layer_create")
         self._h = handle
+        self.device = self._weights[0].device
         self._ws: Optional[torch.Tensor] = None
 
     # ------------------------------------------------------------------ api
@@ -180,7 +250,7 @@ class DFlashLayer:
     def workspace(self, batch: int, total_ctx: int) -> torch.Tensor:
         need = self.workspace_bytes(batch, total_ctx)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def step(self, hidden_states: torch.Tensor, target_hidden: Optional[torch.Tensor],
@@ -188,23 +258,14 @@ class DFlashLayer:
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
         s = self.shape
-        if len(ctx_offsets) != cache.batch + 1:
-            raise ValueError("ctx_offsets must have batch + 1 entries")
-        offs = (C.c_int32 * (cache.batch + 1))(*[int(o) for o in ctx_offsets])
-        if hidden_states.dtype != s.dtype or not hidden_states.is_contiguous():
-            raise ValueError("hidden_states must be contiguous in the layer dtype")
-        if positions.dtype != torch.int32 or not positions.is_contiguous():
-            raise ValueError("positions must be a contiguous int32 device tensor")
-        if target_hidden is not None and target_hidden.numel() == 0:
-            target_hidden = None
-        if target_hidden is not None and (target_hidden.dtype != s.dtype or not target_hidden.is_contiguous()):
-            raise ValueError("target_hidden must be contiguous in the layer dtype")
+        offs, target_hidden = _check_step_args(s, self.device, s.dtype, hidden_states, target_hidden, ctx_offsets,
+                                               positions, cache, out, workspace, "hidden_states")
+        c_offs = (C.c_int32 * (cache.batch + 1))(*offs.tolist())
         if out is None:
-            out = torch.empty((cache.batch * s.block_size, s.hidden), dtype=s.dtype,
-                              device=hidden_states.device)
+            out = torch.empty((cache.batch * s.block_size, s.hidden), dtype=s.dtype, device=self.device)
         if workspace is None:
-            workspace = self.workspace(cache.batch, int(ctx_offsets[-1]))
-        st = _lib.lib().dflash_attn_step(self._h, _ptr(hidden_states), _ptr(target_hidden), offs,
+            workspace = self.workspace(cache.batch, int(offs[-1]))
+        st = _lib.lib().dflash_attn_step(self._h, _ptr(hidden_states), _ptr(target_hidden), c_offs,
                                          _ptr(positions), C.byref(cache.desc), _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream_handle(stream))
         check(st, "dflash_attn_step")
@@ -289,12 +350,13 @@ class ContextKV:
                 check(_lib.lib().dflash_ctxkv_create(C.byref(cfg), C.byref(w), C.byref(handle)),
                       "dflash_ctxkv_create")
         self._h = handle
+        self.device = self._weights[0].device
         self._ws: Optional[torch.Tensor] = None
 
     def workspace(self, total_ctx: int) -> torch.Tensor:
         need = int(_lib.lib().dflash_ctxkv_workspace_bytes(self._h, int(total_ctx)))
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def append(self, context_states: torch.Tensor, ctx_offsets, positions: torch.Tensor,
@@ -304,13 +366,18 @@ class ContextKV:
         if len(caches) != s.n_layers:
             raise ValueError("one cache per layer")
         B = caches[0].batch
-        if len(ctx_offsets) != B + 1:
-            raise ValueError("ctx_offsets must have batch + 1 entries")
-        if context_states.dtype != s.dtype or not context_states.is_contiguous():
-            raise ValueError("context_states must be contiguous in the dtype")
-        if positions.dtype != torch.int32 or not positions.is_contiguous():
-            raise ValueError("positions must be a contiguous int32 device tensor")
-        offs = (C.c_int32 * (B + 1))(*[int(o) for o in ctx_offsets])
+        for c in caches:
+            _check_cache(c, LayerShape(s.hidden, 1, s.n_kv_heads, s.head_dim, 1, s.dtype), self.device,
+                         s.n_kv_heads, s.head_dim)
+            if c.batch != B:
+                raise ValueError("every layer's cache must hold the same sequences")
+        offs = _ctx_offsets(ctx_offsets, B)
+        mc = int(offs[-1])
+        _check_tensor(context_states, "context_states", s.dtype, (mc, s.hidden), self.device)
+        _check_tensor(positions, "positions", torch.int32, (mc,), self.device)
+        if workspace is not None:
+            _check_workspace(workspace, self.device)
+        offs = (C.c_int32 * (B + 1))(*offs.tolist())
         descs = (C.POINTER(_lib.KVCacheDesc) * s.n_layers)(*[C.pointer(c.desc) for c in caches])
         if workspace is None:
             workspace = self.workspace(int(ctx_offsets[-1]))
@@ -337,10 +404,12 @@ class ContextKV:
         if getattr(self, "_fc", None) is None:
             raise ValueError("no fc weight set")
         a = aux_states.contiguous()
-        if a.dtype != self.shape.dtype or a.dim() != 2 or a.shape[1] != self._fc.shape[1]:
+        if a.dim() != 2:
             raise ValueError("aux_states must be [rows, fc_in] in the dtype")
+        _check_tensor(a, "aux_states", self.shape.dtype, (a.shape[0], self._fc.shape[1]), self.device)
         if out is None:
             out = torch.empty((a.shape[0], self.shape.hidden), dtype=a.dtype, device=a.device)
+        _check_tensor(out, "out", self.shape.dtype, (a.shape[0], self.shape.hidden), self.device)
         need = int(_lib.lib().dflash_ctxkv_combine_workspace_bytes(self._h, a.shape[0]))
         if getattr(self, "_fc_ws", None) is None or self._fc_ws.numel() < need:
             self._fc_ws = torch.empty(need, dtype=torch.uint8, device=a.device)
@@ -386,10 +455,11 @@ def mxfp8_quantize(x: torch.Tensor, stream=None):
 class _BorrowedLayer(DFlashLayer):
     """The attention layer a decoder owns (no destroy of its own)."""
 
-    def __init__(self, shape: LayerShape, handle):
+    def __init__(self, shape: LayerShape, handle, device: torch.device):
         self.shape = shape
         self._h = handle
         self._weights = []
+        self.device = device
         self._ws = None
 
     def close(self) -> None:
@@ -421,35 +491,29 @@ class DFlashDecoder:
             check(_lib.lib().dflash_decoder_create(C.byref(cfg), C.byref(w), C.byref(handle)),
                   "dflash_decoder_create")
         self._h = handle
+        self.device = self._weights[0].device
         self._ws: Optional[torch.Tensor] = None
-        self.attention = _BorrowedLayer(shape, C.c_void_p(_lib.lib().dflash_decoder_attention(handle)))
+        self.attention = _BorrowedLayer(shape, C.c_void_p(_lib.lib().dflash_decoder_attention(handle)),
+                                        self.device)
 
     def workspace(self, batch: int, total_ctx: int) -> torch.Tensor:
         need = int(_lib.lib().dflash_decoder_workspace_bytes(self._h, int(batch), int(total_ctx)))
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self._weights[0].device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def step(self, x: torch.Tensor, target_hidden: Optional[torch.Tensor], ctx_offsets, positions: torch.Tensor,
              cache: KVCache, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
         s = self.shape
-        if len(ctx_offsets) != cache.batch + 1:
-            raise ValueError("ctx_offsets must have batch + 1 entries")
-        if x.dtype != s.dtype or not x.is_contiguous():
-            raise ValueError("x must be contiguous in the layer dtype")
-        if positions.dtype != torch.int32 or not positions.is_contiguous():
-            raise ValueError("positions must be a contiguous int32 device tensor")
-        if target_hidden is not None and target_hidden.numel() == 0:
-            target_hidden = None
-        if target_hidden is not None and (target_hidden.dtype != s.dtype or not target_hidden.is_contiguous()):
-            raise ValueError("target_hidden must be contiguous in the layer dtype")
-        offs = (C.c_int32 * (cache.batch + 1))(*[int(o) for o in ctx_offsets])
+        offs, target_hidden = _check_step_args(s, self.device, s.dtype, x, target_hidden, ctx_offsets, positions,
+                                               cache, out, workspace, "x")
+        c_offs = (C.c_int32 * (cache.batch + 1))(*offs.tolist())
         if out is None:
             out = torch.empty_like(x)
         if workspace is None:
-            workspace = self.workspace(cache.batch, int(ctx_offsets[-1]))
-        st = _lib.lib().dflash_decoder_step(self._h, _ptr(x), _ptr(target_hidden), offs, _ptr(positions),
+            workspace = self.workspace(cache.batch, int(offs[-1]))
+        st = _lib.lib().dflash_decoder_step(self._h, _ptr(x), _ptr(target_hidden), c_offs, _ptr(positions),
                                             C.byref(cache.desc), _ptr(out), _ptr(workspace), workspace.numel(),
                                             _stream_handle(stream))
         check(st, "dflash_decoder_step")
@@ -473,11 +537,14 @@ class DFlashDecoder:
 def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float, out: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
     """Row RMSNorm (the draft model's final norm) of a contiguous [rows, H] tensor."""
-    if x.dtype not in _DTYPES or gain.dtype != x.dtype or not x.is_contiguous() or not gain.is_contiguous():
-        raise ValueError("x and gain must be contiguous fp32 or bf16 tensors of one dtype")
+    if x.dtype not in _DTYPES or x.dim() not in (1, 2):
+        raise ValueError("x must be a contiguous [rows, H] (or [H]) fp32 or bf16 tensor")
+    rows, h = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.shape[0])
+    _check_tensor(x, "x", x.dtype, tuple(x.shape), x.device)
+    _check_tensor(gain, "gain", x.dtype, (h,), x.device)
     if out is None:
         out = torch.empty_like(x)
-    rows, h = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.shape[0])
+    _check_tensor(out, "out", x.dtype, tuple(x.shape), x.device)
     st = _lib.lib().dflash_rms_norm(_ptr(x), _ptr(gain), _ptr(out), int(rows), int(h), float(eps), _DTYPES[x.dtype],
                                     _stream_handle(stream))
     check(st, "dflash_rms_norm")

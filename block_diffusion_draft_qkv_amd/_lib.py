@@ -8,9 +8,8 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-# DFLASH_LIB may point at another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                        "libdflash.so")
+# The in-tree build only: nothing in the environment can substitute another library.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
 
 DFLASH_OK = 0
 DFLASH_ERR_ARG = 1

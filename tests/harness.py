@@ -10,6 +10,11 @@ Tolerances (against the float64 oracle):
   that: |err| <= 2e-2 + 2^-8 |ref| (fp32: 1e-4 + 2^-20 |ref|), with the same
   rel-RMS bound.
 Cache indexing, lengths and untouched rows: bit-exact.
+
+Every handle the tests make has its workspace refilled with 0xFF bytes (NaN as
+fp32 and as bf16) each time a step asks for it (poison_workspaces), so a kernel
+that read scratch it had not written in the same step (a stale split partial,
+say) would turn the result non-finite.
 """
 from __future__ import annotations
 
@@ -31,13 +36,31 @@ def dev(a, dtype, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dtype)
 
 
+WORKSPACE_POISON = 0xFF
+
+
+def poison_workspaces(handle):
+    """Make ``handle.workspace(...)`` (used by step/append when no workspace is
+    passed) return its buffer refilled with NaN bytes on every call."""
+    orig = handle.workspace
+
+    def workspace(*args, **kw):
+        ws = orig(*args, **kw)
+        ws.fill_(WORKSPACE_POISON)
+        return ws
+
+    handle.workspace = workspace
+    return handle
+
+
 def make_layer(case: Case):
     from block_diffusion_draft_qkv_amd import DFlashLayer, LayerShape
     cfg, w = case.cfg, case.weights
     dt = torch_dtype(case)
     shape = LayerShape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, dt,
                        cfg.rope_theta, cfg.rms_eps, cfg.sliding_window, cfg.max_position)
-    return DFlashLayer(shape, dev(w.w_qkv, dt), dev(w.w_o, dt), dev(w.q_norm, dt), dev(w.k_norm, dt))
+    return poison_workspaces(DFlashLayer(shape, dev(w.w_qkv, dt), dev(w.w_o, dt), dev(w.q_norm, dt),
+                                         dev(w.k_norm, dt)))
 
 
 def fill_canary(t: torch.Tensor):

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from harness import assert_close, assert_close_stored, cache_bits, dev, fill_canary, raw_bits, to64
+from harness import (assert_close, assert_close_stored, cache_bits, dev, fill_canary, poison_workspaces, raw_bits,
+                     to64)
 from workload import CTXKV_CONFIGS, make_ctxkv_case
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
@@ -31,8 +32,8 @@ def make_precompute(case):
     c, w, dt = case.cfg, case.weights, torch_dt(case)
     shape = ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt, c.rope_theta, c.rms_eps,
                            c.max_position)
-    return ContextKV(shape, dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt),
-                     dev(w.k_norm, dt))
+    return poison_workspaces(ContextKV(shape, dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt),
+                                       dev(w.k_norm, dt)))
 
 
 def make_caches(case, capacity=None):
@@ -176,10 +177,16 @@ def test_empty_context_changes_nothing_and_bad_calls_are_rejected():
         pre.append(ctx, case.ctx_offsets, pos, caches)
     caches[1].lengths[0] -= 1
     # a step past the capacity: rejected
-    big = case.ctx_offsets.copy()
-    big[1:] += case.capacity()
-    with pytest.raises(DFlashError):
-        pre.append(ctx, big, pos, caches)
+    for c in caches:
+        c.lengths[0] = case.capacity() - 1
+    with pytest.raises(DFlashError) as e:
+        pre.append(ctx, case.ctx_offsets, pos, caches)
+    assert e.value.status == 3
+    for c, (_, _, ln) in zip(caches, before):
+        c.set_lengths(ln)
+    # offsets that disagree with the rows given: refused by the binding
+    with pytest.raises(ValueError):
+        pre.append(ctx[:-1], case.ctx_offsets, pos, caches)
     torch.cuda.synchronize()
     for c, (k, v, ln) in zip(caches, before):
         np.testing.assert_array_equal(raw_bits(c.k), k)

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from harness import poison_workspaces  # noqa: E402
 from harness import (cache_bits, check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64,
                      torch_dtype)
 from workload import LayerConfig, make_case, make_mlp_weights
@@ -39,9 +40,9 @@ def make_decoder(case, mw):
     cfg, w, dt = case.cfg, case.weights, torch_dtype(case)
     shape = LayerShape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, dt,
                        cfg.rope_theta, cfg.rms_eps, cfg.sliding_window, cfg.max_position)
-    return DFlashDecoder(shape, mw.w_down.shape[1], dev(w.w_qkv, dt), dev(w.w_o, dt), dev(w.q_norm, dt),
-                         dev(w.k_norm, dt), dev(mw.input_norm, dt), dev(mw.post_norm, dt), dev(mw.w_gate_up, dt),
-                         dev(mw.w_down, dt))
+    return poison_workspaces(DFlashDecoder(shape, mw.w_down.shape[1], dev(w.w_qkv, dt), dev(w.w_o, dt),
+                                           dev(w.q_norm, dt), dev(w.k_norm, dt), dev(mw.input_norm, dt),
+                                           dev(mw.post_norm, dt), dev(mw.w_gate_up, dt), dev(mw.w_down, dt)))
 
 
 def small(**kw):

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+from harness import poison_workspaces  # noqa: E402
 from harness import assert_close_stored, cache_bits, dev, raw_bits, to64
 from test_gpu_context_kv import make_caches, oracle_caches
 from workload import make_ctxkv_case, make_mxfp8_kv_weights, round_bf16
@@ -74,8 +75,8 @@ def make_mx_precompute(case, mx):
                            c.rms_eps, c.max_position)
     codes = torch.from_numpy(mx.w_kv_codes.reshape(-1, c.hidden)).cuda()
     scales = torch.from_numpy(mx.w_kv_scales.reshape(-1, c.hidden // 32)).cuda()
-    return ContextKV(shape, dev(w.hidden_norm, torch.bfloat16), codes, dev(w.k_norm, torch.bfloat16),
-                     w_kv_scale=scales)
+    return poison_workspaces(ContextKV(shape, dev(w.hidden_norm, torch.bfloat16), codes,
+                                       dev(w.k_norm, torch.bfloat16), w_kv_scale=scales))
 
 
 def run_mx(case, seed):

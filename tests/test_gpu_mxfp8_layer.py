@@ -25,6 +25,7 @@ import pytest
 import torch
 
 import oracle
+from harness import poison_workspaces  # noqa: E402
 from harness import cache_bits, check_cache_after_step, dev, errors, make_cache, raw_bits, step_inputs, to64
 from workload import LayerConfig, make_case, make_mxfp8_layer_weights
 
@@ -54,8 +55,9 @@ def mx_layer(case, mw):
     def u8(a):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    return DFlashLayer(shape, u8(mw.w_qkv_codes), u8(mw.w_o_codes), dev(case.weights.q_norm, dt),
-                       dev(case.weights.k_norm, dt), w_qkv_scale=u8(mw.w_qkv_scales), w_o_scale=u8(mw.w_o_scales))
+    return poison_workspaces(DFlashLayer(shape, u8(mw.w_qkv_codes), u8(mw.w_o_codes), dev(case.weights.q_norm, dt),
+                                         dev(case.weights.k_norm, dt), w_qkv_scale=u8(mw.w_qkv_scales),
+                                         w_o_scale=u8(mw.w_o_scales)))
 
 
 def run_mx(case, seed=0):

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from harness import poison_workspaces  # noqa: E402
 from harness import (CANARY_BF16, CANARY_F32, assert_close, assert_close_stored, dev, fill_canary, make_cache,
                      make_layer, raw_bits, run_oracle, step_inputs, to64, torch_dtype)
 from workload import CTXKV_CONFIGS, LayerConfig, make_case, make_ctxkv_case
@@ -159,9 +160,10 @@ def test_context_precompute_into_paged_stack():
                                      config_id=77)
     case = make_ctxkv_case(pc, seed=6)
     c, w, dt = case.cfg, case.weights, torch.bfloat16
-    pre = ContextKV(ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt, c.rope_theta, c.rms_eps,
-                                   c.max_position),
-                    dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt), dev(w.k_norm, dt))
+    pre = poison_workspaces(ContextKV(ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt,
+                                                     c.rope_theta, c.rms_eps, c.max_position),
+                                      dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt),
+                                      dev(w.k_norm, dt)))
     tot = case.cached_len + case.new_ctx
     need = [-(-int(t) // 64) for t in tot]
     caches = [PagedKVCache(case.batch, c.n_kv_heads, c.head_dim, sum(need) + 4, max(need) + 1, dt)

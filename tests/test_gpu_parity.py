@@ -1,6 +1,8 @@
 """GPU parity of the HIP layer step against the float64 oracle on small seeded
 cases that still span several key tiles, ragged tails, splits and the edge
 cases of the method (empty cache, no new context, window bands, crop)."""
+import ctypes as C
+
 import numpy as np
 import pytest
 import torch
@@ -212,7 +214,7 @@ def test_position_out_of_range_is_latched():
 
 
 def test_invalid_steps_change_nothing():
-    from block_diffusion_draft_qkv_amd import DFlashError
+    from block_diffusion_draft_qkv_amd import DFlashError, _lib
     case = make_case(small(batch=2, config_id=23), seed=0)
     layer = make_layer(case)
     cache = make_cache(case)
@@ -221,16 +223,21 @@ def test_invalid_steps_change_nothing():
     out = torch.zeros((2 * 16, 512), dtype=torch.bfloat16, device="cuda")
     bad_offsets = list(case.ctx_offsets)
     bad_offsets[1] = bad_offsets[2] + 1   # decreasing
-    cases = [
-        dict(ctx_offsets=bad_offsets, expect=2),
-        dict(workspace=torch.empty(64, dtype=torch.uint8, device="cuda"), expect=7),
-    ]
-    for c in cases:
-        with pytest.raises(DFlashError) as e:
-            layer.step(hs, th, c.get("ctx_offsets", case.ctx_offsets), pos, cache, out=out,
-                       workspace=c.get("workspace"))
-        assert e.value.status == c["expect"]
-        assert cache.lengths.tolist() == lens.tolist()
+    # decreasing offsets: the binding refuses them, and so does the library
+    # when called directly through the C ABI
+    with pytest.raises(ValueError):
+        layer.step(hs, th, bad_offsets, pos, cache, out=out)
+    ws = layer.workspace(case.batch, int(case.ctx_offsets[-1]))
+    c_offs = (C.c_int32 * 3)(*[int(o) for o in bad_offsets])
+    st = _lib.lib().dflash_attn_step(layer._h, hs.data_ptr(), th.data_ptr(), c_offs, pos.data_ptr(),
+                                     C.byref(cache.desc), out.data_ptr(), ws.data_ptr(), ws.numel(), None)
+    assert st == _lib.DFLASH_ERR_SHAPE
+    assert cache.lengths.tolist() == lens.tolist()
+    with pytest.raises(DFlashError) as e:
+        layer.step(hs, th, case.ctx_offsets, pos, cache, out=out,
+                   workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == _lib.DFLASH_ERR_WORKSPACE
+    assert cache.lengths.tolist() == lens.tolist()
     # a step that would pass the capacity
     cache.lengths[0] = cache.capacity - 16
     with pytest.raises(DFlashError) as e:
