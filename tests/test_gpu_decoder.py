@@ -111,9 +111,16 @@ def test_decoder_rejects_bad_steps_before_enqueueing():
     x, th, pos = step_inputs(case)
     out = torch.full_like(x, 7.0)
     lens = cache.lengths.copy()
+    # a step past the capacity: the library refuses it before the first launch
+    cache.lengths[0] = cache.capacity - 1
+    with pytest.raises(DFlashError) as e:
+        dec.step(x, th, case.ctx_offsets, pos, cache, out=out)
+    assert e.value.status == 3
+    cache.set_lengths(lens)
+    # offsets that disagree with the rows given: refused by the binding
     big = case.ctx_offsets.copy()
     big[1:] += cache.capacity
-    with pytest.raises(DFlashError):
+    with pytest.raises(ValueError):
         dec.step(x, th, big, pos, cache, out=out)
     torch.cuda.synchronize()
     assert cache.lengths.tolist() == lens.tolist()
