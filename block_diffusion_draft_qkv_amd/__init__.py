@@ -271,6 +271,23 @@ class DFlashLayer:
         check(st, "dflash_attn_step")
         return out
 
+    def step_noalloc(self, hidden_states: torch.Tensor, target_hidden: Optional[torch.Tensor], ctx_offsets,
+                     positions: torch.Tensor, cache: KVCache, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """``step`` for callers that cannot allocate: no workspace, the
+        library's per-device scratch instead (``out`` must be given; calls on
+        one device must not overlap)."""
+        s = self.shape
+        if out is None:
+            raise ValueError("step_noalloc writes a caller-given out")
+        offs, target_hidden = _check_step_args(s, self.device, s.dtype, hidden_states, target_hidden, ctx_offsets,
+                                               positions, cache, out, None, "hidden_states")
+        c_offs = (C.c_int32 * (cache.batch + 1))(*offs.tolist())
+        st = _lib.lib().dflash_attn_step_noalloc(self._h, _ptr(hidden_states), _ptr(target_hidden), c_offs,
+                                                 _ptr(positions), C.byref(cache.desc), _ptr(out),
+                                                 _stream_handle(stream))
+        check(st, "dflash_attn_step_noalloc")
+        return out
+
     def poll_error(self, stream=None) -> int:
         return int(_lib.lib().dflash_layer_poll_error(self._h, _stream_handle(stream)))
 

@@ -22,13 +22,14 @@ DFLASH_ERR_WORKSPACE = 7
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
 DFLASH_MAX_BATCH = 256
+DFLASH_NOALLOC_SCRATCH_BYTES = 64 << 20
 APPEND_MODES = {"auto": 0, "fused": 1, "separate": 2}
 KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o")
 
 # Every symbol include/dflash.h declares.
 EXPORTS = (
     "dflash_layer_create", "dflash_layer_destroy", "dflash_workspace_bytes",
-    "dflash_attn_step", "dflash_cache_crop", "dflash_layer_poll_error",
+    "dflash_attn_step", "dflash_attn_step_noalloc", "dflash_cache_crop", "dflash_layer_poll_error",
     "dflash_layer_set_profiling", "dflash_layer_kernel_times", "dflash_status_string",
     "dflash_layer_set_append_mode",
     "dflash_ctxkv_create", "dflash_ctxkv_destroy", "dflash_ctxkv_workspace_bytes",
@@ -117,6 +118,9 @@ def lib() -> C.CDLL:
                                        C.c_void_p, C.POINTER(KVCacheDesc), C.c_void_p, C.c_void_p,
                                        C.c_size_t, C.c_void_p]
         h.dflash_attn_step.restype = C.c_int
+        h.dflash_attn_step_noalloc.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32),
+                                               C.c_void_p, C.POINTER(KVCacheDesc), C.c_void_p, C.c_void_p]
+        h.dflash_attn_step_noalloc.restype = C.c_int
         h.dflash_cache_crop.argtypes = [C.POINTER(KVCacheDesc), C.c_int32, C.c_int32]
         h.dflash_cache_crop.restype = C.c_int
         h.dflash_layer_poll_error.argtypes = [C.c_void_p, C.c_void_p]

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -39,6 +40,43 @@ struct Carve {
   size_t xq, xs, cq, cs, oq, os;  // MXFP8 rows and step-major scales of the block, context, attention output
   size_t total;
 };
+
+}  // namespace
+
+// Scratch of dflash_attn_step_noalloc: a file-scope device array, one copy on
+// every device the library runs on, held until the process ends. In host code
+// its name is only a host-side stand-in: its device address on each device
+// comes from hipGetSymbolAddress (taken once per device, with that device
+// current, when a layer is created there) and only that address is used.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = DFLASH_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Resolve `scratch` on the current device (`device`) once; a failure leaves
+// the no-allocation step unavailable there and clears HIP's sticky error so
+// that it is not reported by a later, unrelated launch.
+void resolve_noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) {
+    g_scratch_ptr[device] = p;
+  } else {
+    (void)hipGetLastError();
+  }
+}
+
+void* noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 }  // namespace
 
@@ -126,16 +164,32 @@ void dflash::attn_range_map(int G, int nkv, uint16_t* range_of) {
 
 namespace {
 
-Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx) {
+// What one step runs, as far as its scratch depends on it: the projection's
+// form (fused epilogue or fp32 slices for the separate kernel), the attention
+// work-groups and o_proj's k slices.
+struct StepPlan {
+  bool fused;
+  int qkv_kslices, groups, o_kslices;
+};
+
+// Without a plan: a bound for any step of `batch` sequences and `total_ctx`
+// context rows (what dflash_workspace_bytes reports). With one: exactly the
+// regions that step uses (the scratch of dflash_attn_step_noalloc).
+Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx, const StepPlan* plan = nullptr) {
   const dflash_config& c = L->cfg;
   const int64_t d = c.head_dim, g = c.n_q_heads / c.n_kv_heads;
   const int64_t mq = batch * c.block_size, es = elem_size(c);
-  const int64_t gmax =
-      std::min<int64_t>((int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim), kMaxGroups);
+  const int64_t nqkv = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * d, nkv2 = 2 * (int64_t)c.n_kv_heads * d;
+  const int64_t gmax = plan ? plan->groups
+                            : std::min<int64_t>((int64_t)L->num_cus * attn_wgs_per_cu(c.dtype, c.head_dim), kMaxGroups);
+  const int64_t ks = plan ? (plan->fused ? 0 : plan->qkv_kslices) : kMaxKSlices;
+  // fp32 q|k|v slices of the separate path; o_proj's k slices reuse the region
+  int64_t qkv_bytes = ks * mq * nqkv * 4;
+  if (plan && plan->o_kslices > 1) qkv_bytes = std::max<int64_t>(qkv_bytes, plan->o_kslices * mq * c.hidden * 4);
   Carve w{};
   size_t off = 0;
-  w.qkv = off;     off += align_up(kMaxKSlices * mq * (c.n_q_heads + 2 * c.n_kv_heads) * d * 4);
-  w.ctxkv = off;   off += align_up(kMaxKSlices * std::max<int64_t>(total_ctx, 1) * 2 * c.n_kv_heads * d * 4);
+  w.qkv = off;     off += align_up(qkv_bytes);
+  w.ctxkv = off;   off += align_up(ks * (plan ? total_ctx : std::max<int64_t>(total_ctx, 1)) * nkv2 * 4);
   // The attention kernel fetches whole 64-row query tiles: slack past the end.
   w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es + kMaxQueryRows * d * 4);
   w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
@@ -335,6 +389,7 @@ int dflash_layer_create(const dflash_config* cfg, const dflash_weights* weights,
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
     L->num_cus = cus;
+  resolve_noalloc_scratch(L->device);
 
   if (!upload_rope_table(cfg->max_position, cfg->head_dim, cfg->rope_theta, &L->cos_sin) ||
       hipMalloc(&L->err, sizeof(int32_t)) != hipSuccess ||
@@ -406,10 +461,12 @@ size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t tota
 
 // The layer step; with validate_only it returns after the host-side checks,
 // having enqueued nothing (the decoder layer checks before its first launch).
+// With noalloc the scratch is the library's per-device buffer (exactly what
+// this step uses, refused past its size) instead of the caller's workspace.
 static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void* target_hidden,
                           const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
                           void* out, void* workspace, size_t workspace_bytes, void* stream,
-                          bool validate_only) {
+                          bool validate_only, bool noalloc = false) {
   if (!L || !hidden_states || !ctx_offsets || !positions || !cache || !out) return DFLASH_ERR_ARG;
   if (!cache->k || !cache->v || !cache->len) return DFLASH_ERR_ARG;
   const dflash_config& c = L->cfg;
@@ -454,22 +511,11 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   if (L->mx && (reinterpret_cast<uintptr_t>(hidden_states) % 16 ||
                 (Mc > 0 && reinterpret_cast<uintptr_t>(target_hidden) % 16)))
     return DFLASH_ERR_ARG;
-  if (!workspace) return DFLASH_ERR_WORKSPACE;
-  const Carve wc = carve(L, B, Mc);
-  if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return DFLASH_ERR_WORKSPACE;
-  if (validate_only) return DFLASH_OK;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* qkv = reinterpret_cast<float*>(ws + wc.qkv);
-  float* ctxkv = reinterpret_cast<float*>(ws + wc.ctxkv);
-  void* qpack = ws + wc.qpack;
-  void* obuf = ws + wc.obuf;
+  // What the step runs: host decisions that also size its scratch.
   const int es = elem_size(c);
   const int Mq = B * bs, H = c.hidden;
   const int Nqkv = (nq + 2 * nkv) * d, Nkv = 2 * nkv * d;
-
   // HK1: block q|k|v and context k|v in one launch; with the append fused into
   // its epilogue (one head per tile, no k split) it also does HK2's work.
   const int nt64 = ((Mq + 63) / 64) * (Nqkv / d) + (int)((Mc + 63) / 64) * (Nkv / d);
@@ -481,6 +527,37 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   const bool fused = L->mx || L->append_mode != DFLASH_APPEND_SEPARATE;
   const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, nt128 >= target ? nt128 : nt64, 1}
                               : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
+  const int G = (int)attn_groups(L, n_tiles, (int64_t)B * nkv);
+  // o_proj: too few rows for the CUs (a small batch) and a weight large enough
+  // that streaming it dominates (>= 4 MB; below that the extra launch costs
+  // more): k split over fp32 slices in the q|k|v region of the scratch (its
+  // contents are consumed by then), summed into out with one rounding.
+  const bool o_big = (int64_t)H * nq * d * elem_size(c) >= (4 << 20);
+  const TileChoice to = choose_tiles(L, Mq, H, 0, 0, !L->mx && o_big);
+  const bool o_split = to.kslices > 1 && (int64_t)to.kslices * H <= (int64_t)kMaxKSlices * Nqkv;
+
+  Carve wc;
+  if (noalloc) {
+    const StepPlan plan{fused, tq.kslices, G, o_split ? to.kslices : 1};
+    wc = carve(L, B, Mc, &plan);
+    if (wc.total > kNoAllocScratchBytes) return DFLASH_ERR_WORKSPACE;
+    workspace = noalloc_scratch(L->device);
+    if (!workspace) return DFLASH_ERR_HIP;
+  } else {
+    if (!workspace) return DFLASH_ERR_WORKSPACE;
+    wc = carve(L, B, Mc);
+    if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return DFLASH_ERR_WORKSPACE;
+  }
+  if (validate_only) return DFLASH_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qkv = reinterpret_cast<float*>(ws + wc.qkv);
+  float* ctxkv = reinterpret_cast<float*>(ws + wc.ctxkv);
+  void* qpack = ws + wc.qpack;
+  void* obuf = ws + wc.obuf;
+
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.nprob = 1;
@@ -568,7 +645,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   // A window at least the capacity keeps every key (|query - key| < T_b <= capacity).
   aa.window = c.sliding_window >= cache->capacity ? 0 : c.sliding_window;
   aa.total_tiles = n_tiles;
-  aa.G = (int32_t)attn_groups(L, n_tiles, (int64_t)B * nkv);
+  aa.G = G;
   // an MXFP8 layer's attention writes o_proj's MXFP8 input directly
   aa.mxo = L->mx ? MxOut{reinterpret_cast<uint8_t*>(ws + wc.oq), reinterpret_cast<uint8_t*>(ws + wc.os), nq * d, Mq}
                  : MxOut{nullptr, nullptr, 0, 0};
@@ -620,15 +697,8 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     record_end(L, DFLASH_K_MERGE, ev, s);
   }
 
-  // HK1: o_proj. Too few rows for the CUs (a small batch) and a weight large
-  // enough that streaming it dominates (>= 4 MB; below that the extra launch
-  // costs more): k split over fp32 slices in the q|k|v region of the workspace
-  // (its contents are consumed by now), summed into out with one rounding.
-  const bool o_big = (int64_t)H * nq * d * elem_size(c) >= (4 << 20);
-  const TileChoice to = choose_tiles(L, Mq, H, 0, 0, !L->mx && o_big);
+  // HK1: o_proj (k split as decided above)
   const int64_t o_slice = (int64_t)Mq * H;
-  const bool o_split = to.kslices > 1 && (size_t)to.kslices * o_slice * 4 <=
-                                             (size_t)kMaxKSlices * Mq * (nq + 2 * nkv) * d * 4;
   GemmArgs go;
   std::memset(&go, 0, sizeof(go));
   go.nprob = 1;
@@ -661,6 +731,13 @@ int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* tar
                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, workspace,
                         workspace_bytes, stream, false);
+}
+
+int dflash_attn_step_noalloc(dflash_layer* L, const void* hidden_states, const void* target_hidden,
+                             const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
+                             void* out, void* stream) {
+  return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, nullptr, 0, stream,
+                        false, true);
 }
 
 int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len) {

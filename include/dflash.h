@@ -29,7 +29,8 @@
  *     passed in and keeps weights alive for the layer's lifetime. The library
  *     allocates only each handle's own cos/sin table and error flag (at
  *     create), and an MXFP8 layer or precompute handle its repacked weight
- *     scales.
+ *     scales; it also holds one static scratch array per device for
+ *     dflash_attn_step_noalloc.
  *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream) and the calls return without synchronising,
  *     except dflash_layer_poll_error, dflash_layer_kernel_times and
@@ -221,6 +222,33 @@ int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
                      const void* target_hidden, const int32_t* ctx_offsets,
                      const int32_t* positions, dflash_kv_cache* cache, void* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * step of dflash_attn_step without a workspace argument. Its scratch (packed
+ * queries, the attention output, the split-KV partials and, where the step
+ * uses them, fp32 projection slices) is a buffer the library keeps on every
+ * device it runs on: a device array of DFLASH_NOALLOC_SCRATCH_BYTES, whose
+ * address is resolved when a layer is created on that device and which lives
+ * until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine) and needs no zeroed memory: each step writes
+ * every scratch byte it reads. All calls on one device share that buffer, and
+ * it keeps the last call's contents, so calls that overlap on one GPU (other
+ * streams, other threads, other layers) race: the caller must order them.
+ * The step carves exactly what it needs: for batch B and head_dim d about
+ * 2 * B * block_size * n_q_heads * d elements of the dtype (queries and
+ * attention output) plus at most 2 * 256 * 64 * (d + 2) * 4 bytes of partials
+ * (16.8 MB at d = 128), and fp32 slices when o_proj splits k for few rows or
+ * the append mode is DFLASH_APPEND_SEPARATE.
+ * Arguments, effects and errors are those of dflash_attn_step, plus:
+ * DFLASH_ERR_WORKSPACE (nothing launched, nothing changed) when the step needs
+ * more than DFLASH_NOALLOC_SCRATCH_BYTES; DFLASH_ERR_HIP when the buffer's
+ * address could not be resolved on the layer's device. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dflash_attn_step_noalloc(dflash_layer* layer, const void* hidden_states,
+                             const void* target_hidden, const int32_t* ctx_offsets,
+                             const int32_t* positions, dflash_kv_cache* cache, void* out,
+                             void* stream);
 
 /* Rewind sequence `seq` to its first `new_len` rows (the accepted prefix after
  * verification; "DFlash源码导读（二）" section 4, crop(start)). Only the host
