@@ -288,6 +288,23 @@ class DFlashLayer:
         check(st, "dflash_attn_step_noalloc")
         return out
 
+    def workspace_region(self, workspace: torch.Tensor, batch: int, total_ctx: int, region: str) -> torch.Tensor:
+        """A view into ``workspace`` (as passed to ``step``) of an intermediate
+        the step left there: ``"attn_out"`` ``[B*bs, nq*d]`` in the dtype,
+        ``"attn_out_mx"`` (E4M3 codes, uint8, same shape) or
+        ``"attn_out_mx_scales"`` (``[nq*d/128, B*bs, 4]`` E8M0 bytes)."""
+        off = C.c_size_t()
+        check(_lib.lib().dflash_workspace_offset(self._h, int(batch), int(total_ctx), _lib.WS_REGIONS[region],
+                                                 C.byref(off)), "dflash_workspace_offset")
+        s = self.shape
+        rows, od = batch * s.block_size, s.n_q_heads * s.head_dim
+        if region == "attn_out":
+            es = 2 if s.dtype == torch.bfloat16 else 4
+            return workspace[off.value:off.value + rows * od * es].view(s.dtype).view(rows, od)
+        if region == "attn_out_mx":
+            return workspace[off.value:off.value + rows * od].view(rows, od)
+        return workspace[off.value:off.value + rows * od // 32].view(od // 128, rows, 4)
+
     def poll_error(self, stream=None) -> int:
         return int(_lib.lib().dflash_layer_poll_error(self._h, _stream_handle(stream)))
 
@@ -401,6 +418,22 @@ class ContextKV:
         st = _lib.lib().dflash_ctxkv_append(self._h, _ptr(context_states), offs, _ptr(positions), descs,
                                             _ptr(workspace), workspace.numel(), _stream_handle(stream))
         check(st, "dflash_ctxkv_append")
+
+    def workspace_region(self, workspace: torch.Tensor, total_ctx: int, region: str) -> torch.Tensor:
+        """A view into ``workspace`` (as passed to ``append``) of the
+        hidden_norm-ed rows the append left there: ``"normed"`` ``[rows, H]``
+        (the dtype, or uint8 E4M3 codes with MXFP8 weights) or
+        ``"normed_mx_scales"`` (``[H/128, rows, 4]`` E8M0 bytes)."""
+        off = C.c_size_t()
+        check(_lib.lib().dflash_ctxkv_workspace_offset(self._h, int(total_ctx), _lib.CTX_WS_REGIONS[region],
+                                                       C.byref(off)), "dflash_ctxkv_workspace_offset")
+        s, rows = self.shape, int(total_ctx)
+        if region == "normed_mx_scales":
+            return workspace[off.value:off.value + rows * s.hidden // 32].view(s.hidden // 128, rows, 4)
+        if self.mxfp8:
+            return workspace[off.value:off.value + rows * s.hidden].view(rows, s.hidden)
+        es = 2 if s.dtype == torch.bfloat16 else 4
+        return workspace[off.value:off.value + rows * s.hidden * es].view(s.dtype).view(rows, s.hidden)
 
     def set_fc(self, w_fc: Optional[torch.Tensor]) -> None:
         """Register the fc weight ``[H, fc_in]`` (the dtype, device) used by
@@ -535,6 +568,20 @@ class DFlashDecoder:
                                             _stream_handle(stream))
         check(st, "dflash_decoder_step")
         return out
+
+    def workspace_region(self, workspace: torch.Tensor, batch: int, total_ctx: int, region: str) -> torch.Tensor:
+        """A view into ``workspace`` (as passed to ``step``) of an intermediate
+        the step left there, in the dtype: ``"a"``, ``"att"``, ``"h"``, ``"m"``
+        (``[B*bs, H]``) or ``"act"`` (``[B*bs, I]``)."""
+        off = C.c_size_t()
+        check(_lib.lib().dflash_decoder_workspace_offset(self._h, int(batch), int(total_ctx),
+                                                         _lib.DEC_WS_REGIONS[region], C.byref(off)),
+              "dflash_decoder_workspace_offset")
+        s = self.shape
+        rows = batch * s.block_size
+        cols = self.intermediate if region == "act" else s.hidden
+        es = 2 if s.dtype == torch.bfloat16 else 4
+        return workspace[off.value:off.value + rows * cols * es].view(s.dtype).view(rows, cols)
 
     def poll_error(self, stream=None) -> int:
         return self.attention.poll_error(stream)

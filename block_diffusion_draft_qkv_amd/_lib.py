@@ -39,7 +39,11 @@ EXPORTS = (
     "dflash_ctxkv_combine_workspace_bytes",
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
+    "dflash_workspace_offset", "dflash_decoder_workspace_offset", "dflash_ctxkv_workspace_offset",
 )
+CTX_WS_REGIONS = {"normed": 0, "normed_mx_scales": 1}
+WS_REGIONS = {"attn_out": 0, "attn_out_mx": 1, "attn_out_mx_scales": 2}
+DEC_WS_REGIONS = {"a": 0, "att": 1, "h": 2, "m": 3, "act": 4}
 
 
 class Config(C.Structure):
@@ -176,6 +180,13 @@ def lib() -> C.CDLL:
         h.dflash_rms_norm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_double,
                                       C.c_int32, C.c_void_p]
         h.dflash_rms_norm.restype = C.c_int
+        h.dflash_workspace_offset.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.POINTER(C.c_size_t)]
+        h.dflash_workspace_offset.restype = C.c_int
+        h.dflash_decoder_workspace_offset.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32,
+                                                      C.POINTER(C.c_size_t)]
+        h.dflash_decoder_workspace_offset.restype = C.c_int
+        h.dflash_ctxkv_workspace_offset.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_size_t)]
+        h.dflash_ctxkv_workspace_offset.restype = C.c_int
         h.dflash_status_string.argtypes = [C.c_int]
         h.dflash_status_string.restype = C.c_char_p
         _lib = h

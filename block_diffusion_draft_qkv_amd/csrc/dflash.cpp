@@ -459,6 +459,24 @@ size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t tota
   return carve(L, batch, total_ctx).total;
 }
 
+int dflash_workspace_offset(const dflash_layer* L, int32_t batch, int64_t total_ctx, int32_t region,
+                            size_t* offset) {
+  if (!L || !offset || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0) return DFLASH_ERR_ARG;
+  const Carve wc = carve(L, batch, total_ctx);
+  switch (region) {
+    case DFLASH_WS_ATTN_OUT: *offset = wc.obuf; return DFLASH_OK;
+    case DFLASH_WS_ATTN_OUT_MX:
+      if (!L->mx) return DFLASH_ERR_ARG;
+      *offset = wc.oq;
+      return DFLASH_OK;
+    case DFLASH_WS_ATTN_OUT_MX_SCALES:
+      if (!L->mx) return DFLASH_ERR_ARG;
+      *offset = wc.os;
+      return DFLASH_OK;
+    default: return DFLASH_ERR_ARG;
+  }
+}
+
 // The layer step; with validate_only it returns after the host-side checks,
 // having enqueued nothing (the decoder layer checks before its first launch).
 // With noalloc the scratch is the library's per-device buffer (exactly what
@@ -948,6 +966,19 @@ size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx) {
   return ctx_carve(h->cfg, total_ctx, h->mx).total;
 }
 
+int dflash_ctxkv_workspace_offset(const dflash_ctxkv* h, int64_t total_ctx, int32_t region, size_t* offset) {
+  if (!h || !offset || total_ctx < 0) return DFLASH_ERR_ARG;
+  const CtxCarve wc = ctx_carve(h->cfg, total_ctx, h->mx);
+  switch (region) {
+    case DFLASH_CTX_WS_NORMED: *offset = wc.normed; return DFLASH_OK;
+    case DFLASH_CTX_WS_NORMED_MX_SCALES:
+      if (!h->mx) return DFLASH_ERR_ARG;
+      *offset = wc.scales;
+      return DFLASH_OK;
+    default: return DFLASH_ERR_ARG;
+  }
+}
+
 int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
                         const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
                         size_t workspace_bytes, void* stream) {
@@ -1156,6 +1187,20 @@ void dflash_decoder_destroy(dflash_decoder* D) {
 size_t dflash_decoder_workspace_bytes(const dflash_decoder* D, int32_t batch, int64_t total_ctx) {
   if (!D || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0) return 0;
   return dec_carve(D, batch, total_ctx).total;
+}
+
+int dflash_decoder_workspace_offset(const dflash_decoder* D, int32_t batch, int64_t total_ctx, int32_t region,
+                                    size_t* offset) {
+  if (!D || !offset || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0) return DFLASH_ERR_ARG;
+  const DecCarve wc = dec_carve(D, batch, total_ctx);
+  switch (region) {
+    case DFLASH_DEC_WS_A: *offset = wc.a; return DFLASH_OK;
+    case DFLASH_DEC_WS_ATT: *offset = wc.att; return DFLASH_OK;
+    case DFLASH_DEC_WS_H: *offset = wc.h; return DFLASH_OK;
+    case DFLASH_DEC_WS_M: *offset = wc.m; return DFLASH_OK;
+    case DFLASH_DEC_WS_ACT: *offset = wc.act; return DFLASH_OK;
+    default: return DFLASH_ERR_ARG;
+  }
 }
 
 int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hidden, const int32_t* ctx_offsets,

@@ -192,6 +192,27 @@ void dflash_layer_destroy(dflash_layer* layer);
 size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
                               int64_t total_ctx, int64_t total_keys);
 
+/* Where a step leaves its intermediate results in the workspace (for tests
+ * and inspection): the byte offset of `region` in the workspace of a step of
+ * `batch` sequences and `total_ctx` new context rows (the layout that
+ * dflash_workspace_bytes sizes). Once a dflash_attn_step with that workspace
+ * has run, the region holds that step's values:
+ *   DFLASH_WS_ATTN_OUT           [B * bs][nq * d] the attention output, o_proj's
+ *                                input, in the dtype (not written by an MXFP8
+ *                                layer)
+ *   DFLASH_WS_ATTN_OUT_MX        [B * bs][nq * d] an MXFP8 layer's attention
+ *                                output as E4M3 codes (o_proj's input)
+ *   DFLASH_WS_ATTN_OUT_MX_SCALES its E8M0 scale bytes, step-major:
+ *                                [nq * d / 128][B * bs][4], byte (c, m, j) scaling
+ *                                columns 128 c + 32 j .. + 31 of row m
+ * The scratch of dflash_attn_step_noalloc has another layout.
+ * Errors: DFLASH_ERR_ARG (null layer or offset, batch outside [1,
+ * DFLASH_MAX_BATCH], total_ctx < 0, unknown region, an MXFP8 region of a
+ * bf16 or fp32 layer). */
+enum { DFLASH_WS_ATTN_OUT = 0, DFLASH_WS_ATTN_OUT_MX = 1, DFLASH_WS_ATTN_OUT_MX_SCALES = 2 };
+int dflash_workspace_offset(const dflash_layer* layer, int32_t batch, int64_t total_ctx, int32_t region,
+                            size_t* offset);
+
 /* One layer step for every sequence of `cache` (B = cache->batch).
  *   hidden_states  device [B * bs, H]: the draft block of sequence b is rows
  *                  b*bs .. b*bs+bs-1 (one anchor plus bs-1 mask embeddings).
@@ -416,6 +437,18 @@ int dflash_ctxkv_combine(dflash_ctxkv* h, const void* aux_states, int64_t rows, 
 /* Device workspace bytes for up to `total_ctx` context rows; 0 on bad input. */
 size_t dflash_ctxkv_workspace_bytes(const dflash_ctxkv* h, int64_t total_ctx);
 
+/* Where an append leaves the hidden_norm-ed context rows in its workspace (for
+ * tests and inspection): the byte offset of `region` in the workspace of an
+ * append of `total_ctx` rows. After the append they hold:
+ *   DFLASH_CTX_WS_NORMED            [total_ctx][H]: the rows in the dtype, or as
+ *                                   E4M3 codes with MXFP8 weights
+ *   DFLASH_CTX_WS_NORMED_MX_SCALES  their E8M0 scale bytes (MXFP8 weights only),
+ *                                   step-major [H / 128][total_ctx][4]
+ * Errors: DFLASH_ERR_ARG (null handle or offset, total_ctx < 0, unknown
+ * region, the scales of a handle without MXFP8 weights). */
+enum { DFLASH_CTX_WS_NORMED = 0, DFLASH_CTX_WS_NORMED_MX_SCALES = 1 };
+int dflash_ctxkv_workspace_offset(const dflash_ctxkv* h, int64_t total_ctx, int32_t region, size_t* offset);
+
 /* Append the new context rows of `caches[0 .. L-1]->batch` sequences to every
  * layer's cache.
  *   context_states  device [sum n_b, H] raw context rows (before hidden_norm),
@@ -515,6 +548,21 @@ dflash_layer* dflash_decoder_attention(dflash_decoder* decoder);
 /* Device workspace bytes of a decoder step for `batch` sequences with
  * `total_ctx` new context rows in all; 0 on bad input. */
 size_t dflash_decoder_workspace_bytes(const dflash_decoder* decoder, int32_t batch, int64_t total_ctx);
+
+/* The decoder step's intermediates in its workspace (for tests and
+ * inspection), as for dflash_workspace_offset: the byte offset of `region` in
+ * the workspace of a step of `batch` sequences and `total_ctx` context rows.
+ * After the step they hold, in the dtype:
+ *   DFLASH_DEC_WS_A    [B * bs][H] input_layernorm output a
+ *   DFLASH_DEC_WS_ATT  [B * bs][H] the attention layer step's output (o_proj)
+ *   DFLASH_DEC_WS_H    [B * bs][H] the residual h = x + att (rounded once)
+ *   DFLASH_DEC_WS_M    [B * bs][H] post_attention_layernorm output m
+ *   DFLASH_DEC_WS_ACT  [B * bs][I] the MLP activation silu(m Wg^T) * (m Wu^T)
+ * Errors: DFLASH_ERR_ARG (null decoder or offset, bad batch, total_ctx < 0,
+ * unknown region). */
+enum { DFLASH_DEC_WS_A = 0, DFLASH_DEC_WS_ATT = 1, DFLASH_DEC_WS_H = 2, DFLASH_DEC_WS_M = 3, DFLASH_DEC_WS_ACT = 4 };
+int dflash_decoder_workspace_offset(const dflash_decoder* decoder, int32_t batch, int64_t total_ctx,
+                                    int32_t region, size_t* offset);
 
 /* One decoder layer step. x and out: device [B * bs, H] (16-byte aligned; out
  * must not overlap x); the other arguments, the cache effects and the errors

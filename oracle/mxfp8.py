@@ -169,13 +169,14 @@ def _mx_rows(x):
 
 
 def layer_step_mxfp8(cfg, weights, cache: OracleCache, hidden_states, target_hidden, ctx_offsets, positions,
-                     quantise_o: bool = True):
+                     quantise_o: bool = True, o_rows_out: list = None):
     """``layer_step`` with MXFP8 projections. ``weights`` has ``w_qkv_codes
     [(nq+2nkv)*d, H]`` and ``w_qkv_scales [.., H/32]`` (rows q | k | v),
     ``w_o_codes [H, nq*d]`` and ``w_o_scales [H, nq*d/32]`` (uint8), and
     ``q_norm, k_norm [d]``. ``quantise_o=False`` feeds o_proj the bf16
     attention output unquantised (a reference point for tests, not the
-    method)."""
+    method). ``o_rows_out``, if given, receives each sequence's attention
+    output rows ``[bs, nq*d]`` (float64, before any rounding), in order."""
     H, nq, nkv, d = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     wqkv = mx_dequantize(weights.w_qkv_codes, weights.w_qkv_scales)
     plain = SimpleNamespace(w_q=wqkv[:nq * d], w_k=wqkv[nq * d:(nq + nkv) * d], w_v=wqkv[(nq + nkv) * d:],
@@ -183,5 +184,9 @@ def layer_step_mxfp8(cfg, weights, cache: OracleCache, hidden_states, target_hid
                             q_norm=weights.q_norm, k_norm=weights.k_norm)
     X = _mx_rows(_f64(hidden_states).reshape(-1, H))
     C = _mx_rows(_f64(target_hidden).reshape(-1, H)) if target_hidden is not None else None
-    return layer_step(cfg, plain, cache, X, C, ctx_offsets, positions,
-                      o_input=(lambda o: _mx_rows(round_bf16(o))) if quantise_o else round_bf16)
+    def o_input(o):
+        if o_rows_out is not None:
+            o_rows_out.append(o)
+        return _mx_rows(round_bf16(o)) if quantise_o else round_bf16(o)
+
+    return layer_step(cfg, plain, cache, X, C, ctx_offsets, positions, o_input=o_input)

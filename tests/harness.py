@@ -168,3 +168,15 @@ def check_cache_after_step(case: Case, cache, before_k, before_v, new_cache: ora
         v_new = to64(vt_rows[b, :, :, lb:tb].transpose(1, 2))
         assert_close(k_new, new_cache.k[b][:, lb:tb], case.cfg.dtype, f"cache K seq {b}")
         assert_close(v_new, new_cache.v[b][:, lb:tb], case.cfg.dtype, f"cache V seq {b}")
+
+
+def sampled_rows(n_rows: int, seed: int, n_random: int = 48, edge: int = 64, tile: int = 128) -> np.ndarray:
+    """Rows to check of a large row-parallel result: the first and last `edge`
+    rows, both rows on either side of every `tile`-row boundary (where the
+    projection's row tiles meet), and `n_random` more drawn from the seed."""
+    rows = [np.arange(min(edge, n_rows)), np.arange(max(0, n_rows - edge), n_rows)]
+    b = np.arange(tile, n_rows, tile)
+    rows += [b - 1, b]
+    rows.append(np.random.default_rng(seed).choice(n_rows, min(n_random, n_rows), replace=False))
+    return np.unique(np.concatenate(rows)).astype(np.int64)
+

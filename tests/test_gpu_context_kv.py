@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from harness import sampled_rows  # noqa: E402
 from harness import (assert_close, assert_close_stored, cache_bits, dev, fill_canary, poison_workspaces, raw_bits,
                      to64)
 from workload import CTXKV_CONFIGS, make_ctxkv_case
@@ -117,19 +118,22 @@ def test_context_kv_prefill_rows_sampled():
     pre.append(dev(case.context_states, dt), case.ctx_offsets, torch.from_numpy(case.positions).cuda(), caches)
     torch.cuda.synchronize()
     assert pre.poll_error() == 0
-    rows = np.random.default_rng(0).choice(int(case.ctx_offsets[-1]), 48, replace=False)
+    rows = sampled_rows(int(case.ctx_offsets[-1]), seed=0)
     sub = case.context_states[rows]
     offs = np.arange(len(rows) + 1, dtype=np.int32)
     empty = [oracle.OracleCache.from_arrays([np.zeros((case.cfg.n_kv_heads, 0, case.cfg.head_dim))] * len(rows),
                                             [np.zeros((case.cfg.n_kv_heads, 0, case.cfg.head_dim))] * len(rows))
              for _ in range(case.cfg.n_layers)]
     ref = oracle.context_kv_precompute(case.cfg, case.weights, empty, sub, offs, case.positions[rows])
+    print(f"[P4] {len(rows)} rows checked: the first and last 64, both sides of every 128-row tile "
+          f"boundary, 48 random", flush=True)
     for layer, kv in enumerate(caches):
         assert kv.lengths.tolist() == [4096]
+        k_all = to64(kv.k_rows()[0])                  # [nkv, cap, d]
+        v_all = to64(kv.vt_rows()[0]).transpose(0, 2, 1)
         for i, r in enumerate(rows):
-            assert_close_stored(to64(kv.k_rows()[0, :, r:r + 1]), ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
-            assert_close_stored(to64(kv.vt_rows()[0, :, :, r:r + 1].transpose(1, 2)), ref[layer].v[i], "bf16",
-                                f"layer {layer} V row {r}")
+            assert_close_stored(k_all[:, r:r + 1], ref[layer].k[i], "bf16", f"layer {layer} K row {r}")
+            assert_close_stored(v_all[:, r:r + 1], ref[layer].v[i], "bf16", f"layer {layer} V row {r}")
 
 
 def test_layer_step_after_precompute_matches_oracle():
