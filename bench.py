@@ -79,6 +79,28 @@ def parse():
     return ap.parse_args()
 
 
+SETTLE_S = 1.0  # set from --settle in main()
+
+
+def settle(step, seconds: float = None) -> int:
+    """Run `step(i)` for a fixed wall time, untimed, so that the GPU clocks
+    reach the level they hold under sustained load (they drop during the host
+    set-up of each workload); returns the number of calls."""
+    import torch
+    seconds = SETTLE_S if seconds is None else seconds
+    n = 0
+    if seconds <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def source_hash(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -196,6 +218,7 @@ def bench_context_kv(steps: int, warmup: int, names=("P3", "P4"), formats=("bf16
             for kv in caches:
                 kv.set_lengths(L0)
 
+        settle(lambda i: run())
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
@@ -306,6 +329,7 @@ def bench_decoder(steps: int, warmup: int, seed: int = 0, copies: int = 3):
         dec.step(x, th, offs, pos, cache, out=out, workspace=ws)
         cache.set_lengths(L0)
 
+    settle(one)
     for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
@@ -386,6 +410,7 @@ def bench_other_configs(names, steps: int, warmup: int, seed: int = 0, copies: i
             c.crop_all(accepted)
             c.set_lengths(L0)
 
+        settle(one)
         for i in range(warmup):
             one(i)
         torch.cuda.synchronize()
@@ -472,6 +497,7 @@ def bench_mxfp8_layer(steps: int, warmup: int, seed: int = 0, copies: int = 3):
         c.crop_all(accepted)
         c.set_lengths(L0)
 
+    settle(one)
     for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
@@ -542,6 +568,7 @@ def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
         layer.step(hs, th, offs, pos, c, out=out, workspace=ws)
         c.set_lengths(L0)
 
+    settle(one)
     for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
@@ -591,7 +618,9 @@ def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
 
 
 def main():
+    global SETTLE_S
     a = parse()
+    SETTLE_S = a.settle
     if a.gpus != 1:
         print("bench.py measures one GPU only: the multi-GPU path of this layer is a design "
               "(sequence/head sharding) that is not built; run with --gpus 1.", file=sys.stderr)
@@ -663,15 +692,7 @@ def main():
     # sustained load, and the first tens of steps of a cold run (a few ms) run
     # the projections ~20 % slower. Untimed steps for a fixed wall time first,
     # then the W warm-up steps, then the K timed ones.
-    settle_steps = 0
-    if a.settle > 0:
-        torch.cuda.synchronize()
-        t_end = time.perf_counter() + a.settle
-        while time.perf_counter() < t_end:
-            for _ in range(50):
-                one_step(settle_steps)
-                settle_steps += 1
-            torch.cuda.synchronize()
+    settle_steps = settle(one_step, a.settle)
     for i in range(a.warmup):
         one_step(i)
     torch.cuda.synchronize()

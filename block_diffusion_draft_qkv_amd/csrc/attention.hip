@@ -117,13 +117,32 @@ template <> __device__ inline int key_of<__bf16>(int kb, int m) {
 template <> __device__ inline int key_of<float>(int kb, int m) { return 16 * kb + m; }
 
 // LDS chunk swizzles. A ds_read_b128 of an MFMA operand reads 16 rows (lane %
-// 16) at one logical chunk; the chunk is stored at logical ^ swz(row), chosen
-// so those 16 reads hit distinct 16-byte bank groups whether the hardware
-// serves 8 or 16 lanes per pass. For K the 16 rows are key_of(kb, 0..15) and
-// the swizzle depends only on the lane; V^T and Q reads take 16 consecutive
-// rows and use rswz (lds_dma.h).
+// 16) at logical chunks 4 c + lane / 16; the chunk is stored at logical ^
+// swz(row). gfx950's LDS has 128 banks of 4 bytes and serves a ds_read_b128 as
+// two 8-byte halves, 32 lanes a pass (fitted to SQ_LDS_BANK_CONFLICT: a
+// contiguous 1 KB read stalls 0 cycles, 16 rows of 128 bytes at one chunk 12,
+// a swizzle built for 8- or 16-lane passes 4). A pass is conflict-free when
+// its 32 lanes' 8-byte pieces fall on distinct bank pairs, (address / 8) % 64:
+//   * 128-byte rows (CPR 8: V^T tiles, and K and Q at head_dim 64 in bf16):
+//     the bank pair is (r % 4) * 16 + 2 c + h, so the rows r, r + 4, r + 8,
+//     r + 12 of one residue class, read at the chunk pair {x, x ^ 1} of a
+//     pass, need distinct bits 1-2 of the chunk: ((r >> 2) & 3) << 1;
+//   * 256-byte rows (CPR 16): the pair is (r % 2) * 32 + 2 c + h: r % 16;
+//   * 512-byte rows (CPR 32, fp32 at head_dim 128): the pair is 2 c + h, so
+//     the 16 rows need 16 distinct chunk pairs: (r % 16) << 1.
+// V^T and Q reads take 16 consecutive rows and use aswz; for K the 16 rows are
+// key_of(kb, 0..15) and kswz depends only on bits kb does not change. (Moving
+// V^T off the 8/16-lane swizzle, which stalled 4 cycles a read, measured 0.1
+// to 0.7 us faster at C3 in same-box comparisons: the kernel is bound by its
+// stream, not by these reads.)
+template <int CPR> __device__ inline int aswz(int row) {
+  if constexpr (CPR >= 32) return (row & 15) << 1;
+  else if constexpr (CPR == 16) return row & 15;
+  else if constexpr (CPR == 8) return ((row >> 2) & 3) << 1;
+  else return ((row >> 1) ^ (row >> 2)) & 3;
+}
 template <typename T, int CPR> __device__ inline int kswz(int row) {
-  if constexpr (sizeof(T) == 4) return row & 15;
+  if constexpr (sizeof(T) == 4) return CPR >= 32 ? (row & 15) << 1 : row & 15;
   else if constexpr (CPR == 16) return (row & 3) | ((row >> 1) & 12);
   else return (((row >> 1) & 1) | ((row >> 2) & 6)) ^ ((row & 1) << 2);
 }
@@ -292,13 +311,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
 #pragma unroll
     for (int i = 0; i < KPP; ++i) {
       const int blk = i * kProducerWaves + pw, row = blk * (64 / VCPR) + lane / VCPR;
-      const int c = (lane % VCPR) ^ rswz<VCPR>(row);
+      const int c = (lane % VCPR) ^ aswz<VCPR>(row);
       vdma[i] = (uint32_t)(row * vstride + c * E) * (uint32_t)sizeof(T);
     }
 #pragma unroll
     for (int i = 0; i < QPP; ++i) {
       const int blk = i * kProducerWaves + pw, row = blk * (64 / CPR) + lane / CPR;
-      const int c = (lane % CPR) ^ rswz<CPR>(row);
+      const int c = (lane % CPR) ^ aswz<CPR>(row);
       qdma[i] = (uint32_t)(row * D + c * E) * (uint32_t)sizeof(T);
     }
     // A paged cache's physical block of the cursor's tile is loaded one step
@@ -379,10 +398,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
     const int krow = key_of<T>(0, r16), ksw = kswz<T, CPR>(krow);
 #pragma unroll
     for (int c = 0; c < NC; ++c) koff[c] = (uint32_t)(krow * CPR + ((4 * c + q) ^ ksw)) * 16u;
-    const int vsw = rswz<VCPR>(r16);
+    const int vsw = aswz<VCPR>(r16);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) voff[ks] = (uint32_t)(r16 * VCPR + ((4 * ks + q) ^ vsw)) * 16u + K_BYTES;
-    const int qsw = rswz<CPR>(qrow);
+    const int qsw = aswz<CPR>(qrow);
 #pragma unroll
     for (int c = 0; c < NC; ++c) qoff[c] = (uint32_t)(qrow * CPR + ((4 * c + q) ^ qsw)) * 16u;
   }

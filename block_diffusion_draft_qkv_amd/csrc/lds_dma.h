@@ -78,8 +78,13 @@ __device__ inline uint32_t lds_read_u8(uint32_t byte_addr) {
 
 // Chunk swizzle for rows of CPR 16-byte chunks read 16 consecutive rows at a
 // time (one MFMA operand): logical chunk c of row r is stored at c ^ rswz(r),
-// which puts the 16 reads on distinct 16-byte bank groups whether the hardware
+// which puts the 16 reads on distinct 16-byte bank groups when the hardware
 // serves 8 or 16 lanes per ds_read_b128 pass. Depends on the row's low 4 bits.
+// The projection GEMM uses it. gfx950 serves a ds_read_b128 in 32-lane passes
+// of 8-byte halves over 128 banks (see the attention kernel's swizzles), and
+// in that model these reads stall 4 cycles each; the GEMM with a swizzle that
+// stalls none measured no faster (C3 q|k|v 41.7 against 41.1 us, 4096-row
+// precompute 236 against 231 us on the same box), so it keeps this one.
 template <int CPR> __device__ inline int rswz(int row) {
   if constexpr (CPR >= 16) return row & 15;
   else if constexpr (CPR == 8) return (row & 7) ^ ((row >> 3) & 1);
