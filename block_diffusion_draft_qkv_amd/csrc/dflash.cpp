@@ -365,7 +365,7 @@ const char* dflash_status_string(int status) {
     case DFLASH_ERR_ARG: return "invalid argument";
     case DFLASH_ERR_SHAPE: return "inconsistent or non-divisible shape";
     case DFLASH_ERR_CAPACITY: return "step would exceed the cache capacity";
-    case DFLASH_ERR_RANGE: return "value out of range (crop length or position)";
+    case DFLASH_ERR_RANGE: return "value out of range (crop length, position or block-table entry)";
     case DFLASH_ERR_UNSUPPORTED: return "configuration not supported by the kernels";
     case DFLASH_ERR_HIP: return "HIP runtime error";
     case DFLASH_ERR_WORKSPACE: return "workspace missing or too small";
@@ -993,10 +993,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   if (c0->capacity <= 0 || c0->capacity % kKeyTile || c0->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
   for (int l = 1; l < nl; ++l) {
     if (caches[l]->batch != B || caches[l]->capacity != c0->capacity) return DFLASH_ERR_SHAPE;
-    // one layout for every layer (a paged stack shares its block table)
-    if (caches[l]->block_table != c0->block_table || caches[l]->num_blocks != c0->num_blocks ||
-        caches[l]->max_blocks != c0->max_blocks)
-      return DFLASH_ERR_SHAPE;
+    // every layer paged or none; a paged layer may have its own table and pools
+    if ((caches[l]->block_table == nullptr) != (c0->block_table == nullptr)) return DFLASH_ERR_SHAPE;
     for (int b = 0; b < B; ++b)
       if (caches[l]->len[b] != c0->len[b]) return DFLASH_ERR_SHAPE;
   }
@@ -1018,8 +1016,10 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   {
     int64_t rows[kMaxBatch];
     for (int b = 0; b < B; ++b) rows[b] = (int64_t)c0->len[b] + (ctx_offsets[b + 1] - ctx_offsets[b]);
-    const int lst = check_layout(c0, rows);
-    if (lst != DFLASH_OK) return lst;
+    for (int l = 0; l < nl; ++l) {
+      const int lst = check_layout(caches[l], rows);
+      if (lst != DFLASH_OK) return lst;
+    }
   }
   if (Mc == 0) return DFLASH_OK;
   if (!context_states || !positions || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
@@ -1063,6 +1063,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   for (int l = 0; l < nl; ++l) {
     na.layer_kc[l] = caches[l]->k;
     na.layer_vc[l] = caches[l]->v;
+    na.layer_bt[l] = caches[l]->block_table;
+    na.layer_nb[l] = caches[l]->block_table ? caches[l]->num_blocks : 0;
   }
   na.err = h->err;
   na.nq = nkv; na.nkv = nkv; na.bs = 0; na.cap = c0->capacity; na.max_pos = c.max_position;

@@ -563,6 +563,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
   }
   T* const kc = static_cast<T*>(layer == 0 ? a.kc : a.layer_kc[layer]);
   T* const vc = static_cast<T*>(layer == 0 ? a.vc : a.layer_vc[layer]);
+  const CacheMap map = a.map_of(layer);
 
   // Consumers: this lane's rows (sequence, window row: context rows first,
   // then block rows). After the swap below, wave (wm, wn) finishes whole rows
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
     }
     // The cache block of each row (a paged cache's from its table, loaded with the positions).
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) blk[mi] = ok[mi] ? (int)a.map.block_of(sb[mi], crow[mi]) : 0;
+    for (int mi = 0; mi < MI; ++mi) blk[mi] = ok[mi] ? (int)map.block_of(sb[mi], crow[mi]) : 0;
   }
 
   f32x4 acc[NI][MI];
@@ -645,7 +646,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
     // Values: raw, transposed into cache V (key index contiguous); each wave
     // writes its own half of the columns for all its rows.
     T* vbase = vc;
-    const size_t vs = (size_t)a.map.vstride();
+    const size_t vs = (size_t)CacheMap::vstride();
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!ok[mi]) continue;

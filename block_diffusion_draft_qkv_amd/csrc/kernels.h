@@ -113,11 +113,24 @@ struct NormRopeArgs {
   // The multi-layer context precompute (bs = 0, no queries) runs grid.z =
   // layers: layer z > 0 reads the columns ctxkv + z * ctx_layer_off, its gain
   // k_norm + z * d and writes the cache layer_kc[z] / layer_vc[z].
+  // Layer z > 0 of a paged stack may have its own block table and pool size
+  // (layer_bt[z], layer_nb[z]); the table stride, capacity and lengths are
+  // every layer's.
   int64_t ctx_layer_off;
   void* layer_kc[kMaxLayers];
   void* layer_vc[kMaxLayers];
-  CacheMap map;            // cache layout (the same for every layer)
+  const int32_t* layer_bt[kMaxLayers];
+  int32_t layer_nb[kMaxLayers];
+  CacheMap map;            // cache layout of layer 0 (and of a layer step)
   SeqTable seq;
+  __device__ inline CacheMap map_of(int z) const {
+    CacheMap m = map;
+    if (z > 0 && m.bt) {
+      m.bt = layer_bt[z];
+      m.num_blocks = layer_nb[z];
+    }
+    return m;
+  }
 };
 // grid: B * n_kv (one column of work-groups per sequence and KV head) times
 // `layers` (1 for a layer step); max_new_rows: the largest n_b + bs.

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   // Layer z of a multi-layer context precompute (z = 0 for a layer step).
   const int z = blockIdx.z;
   const float* ctxkv = a.ctxkv + (size_t)z * a.ctx_layer_off;
+  const CacheMap map = a.map_of(z);
   const size_t pair = (size_t)b * nkv + j;
 
   if ((int)blockIdx.y >= yv) {
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       const float o1 = y1 * cs[s] - y2 * sn[s];
       const float o2 = y2 * cs[s] + y1 * sn[s];
       const int r = base + s * RPW;
-      T* dst = key ? kbase + a.map.k_row(b, j, L + r, D) : qdst + (size_t)(r - nnew) * D;
+      T* dst = key ? kbase + map.k_row(b, j, L + r, D) : qdst + (size_t)(r - nnew) * D;
       if (kind[s] != 0) {
         dst[t] = Elem<T>::from_f32(o1);
         dst[t + HALF] = Elem<T>::from_f32(o2);
@@ -204,10 +205,10 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   }
   // Where each row's column starts (a paged cache maps rows to blocks).
   __shared__ size_t vcol[VT];
-  if (tid < nr) vcol[tid] = a.map.v_col(b, j, L + r0 + tid, D);
+  if (tid < nr) vcol[tid] = map.v_col(b, j, L + r0 + tid, D);
   __syncthreads();
   T* vbase = static_cast<T*>(z == 0 ? a.vc : a.layer_vc[z]);
-  const size_t vs = (size_t)a.map.vstride();
+  const size_t vs = (size_t)CacheMap::vstride();
   for (int idx = tid; idx < D * nr; idx += 256) {
     const int dd = idx / nr, rr = idx % nr;
     vbase[vcol[rr] + (size_t)dd * vs] = vt[dd][rr];

@@ -460,13 +460,20 @@ int dflash_ctxkv_workspace_offset(const dflash_ctxkv* h, int64_t total_ctx, int3
  *                   [0, max_position): a violation is clamped and latched as
  *                   for a layer step (dflash_ctxkv_poll_error).
  *   caches          HOST array of L cache descriptors, one per layer, with the
- *                   same batch, capacity and lengths.
+ *                   same batch, capacity and lengths; all contiguous or all
+ *                   paged. Paged layers may share one block table or each
+ *                   have their own table and pools (the vLLM page
+ *                   "qwen3_dflash", precompute_and_store_context_kv, takes
+ *                   one slot mapping for all layers or one per layer).
  * Effects: rows [len_b, len_b + n_b) of every layer's K and V for every b,
  * nothing else in the caches; then every layer's len[b] += n_b. Validation
- * (shapes, equal lengths across layers, capacity, workspace) happens before
- * anything is enqueued; on an error nothing runs and no length changes.
- * Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE, DFLASH_ERR_CAPACITY,
- * DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP. */
+ * (shapes, equal lengths across layers, capacity, every layer's table entries
+ * for the rows written, workspace) happens before anything is enqueued; on an
+ * error nothing runs and no length changes.
+ * Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE (also a mix of paged and
+ * contiguous layers), DFLASH_ERR_CAPACITY, DFLASH_ERR_RANGE (a needed table
+ * entry of some layer outside its pools), DFLASH_ERR_WORKSPACE,
+ * DFLASH_ERR_HIP. */
 int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
                         const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
                         size_t workspace_bytes, void* stream);

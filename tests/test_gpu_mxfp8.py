@@ -234,12 +234,12 @@ def test_mxfp8_rejections_leave_the_caches_alone():
         mxfp8_quantize(torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda"))
 
 
-def test_mxfp8_precompute_into_paged_stack():
-    """The MXFP8 precompute writing three layers' paged caches that share one
-    shuffled block table, against the oracle, dead slots untouched."""
-    from block_diffusion_draft_qkv_amd import PagedKVCache
-    from harness import fill_canary
-    from test_gpu_paged import check_paged_after
+@pytest.mark.parametrize("tables", ["shared", "per_layer"])
+def test_mxfp8_precompute_into_paged_stack(tables):
+    """The MXFP8 precompute writing three layers' paged caches with one shared
+    shuffled block table or a table per layer, against the oracle, dead slots
+    untouched."""
+    from test_gpu_paged import check_paged_after, paged_stack
     from workload import CTXKV_CONFIGS
     pc = CTXKV_CONFIGS["M2"].replace(batch=4, cached_len=(0, 300), new_ctx=(1, 40), config_id=78)
     case = make_ctxkv_case(pc, seed=7)
@@ -247,23 +247,7 @@ def test_mxfp8_precompute_into_paged_stack():
     mx = make_mxfp8_kv_weights(c, 2)
     pre = make_mx_precompute(case, mx)
     tot = case.cached_len + case.new_ctx
-    need = [-(-int(t) // 64) for t in tot]
-    caches = [PagedKVCache(case.batch, c.n_kv_heads, c.head_dim, sum(need) + 4, max(need) + 1, dt)
-              for _ in range(c.n_layers)]
-    order = list(caches[0].free)
-    np.random.default_rng(5).shuffle(order)
-    for layer, kv in enumerate(caches):
-        fill_canary(kv.k)
-        fill_canary(kv.v)
-        kv.free = list(order)
-        for b in range(case.batch):
-            kv.write_prefix(b, dev(case.cache_k[layer][b], dt), dev(case.cache_v[layer][b], dt))
-            kv.reserve(b, int(tot[b]))
-        kv.sync()
-    for kv in caches[1:]:
-        assert np.array_equal(kv.table_host, caches[0].table_host)
-        kv.table = caches[0].table
-        kv.desc.block_table = caches[0].table.data_ptr()
+    caches = paged_stack(case, dt, 5, tables)
     befores = [(raw_bits(kv.k), raw_bits(kv.v)) for kv in caches]
     pre.append(dev(case.context_states, dt), case.ctx_offsets, torch.from_numpy(case.positions).cuda(), caches)
     torch.cuda.synchronize()

@@ -152,10 +152,52 @@ def test_multi_round_decode_driver_matches_oracle():
     assert layer.poll_error() == 0
 
 
-def test_context_precompute_into_paged_stack():
-    """The multi-layer precompute writing three layers' paged caches that share
-    one block table."""
-    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape, PagedKVCache
+def paged_stack(case, dt, seed, tables):
+    """One paged cache per layer holding the case's prefixes, blocks for every
+    sequence's new rows reserved. ``tables="shared"``: every layer takes the
+    same shuffled blocks and the caches share layer 0's device table;
+    ``"per_layer"``: each layer has its own pool size and its own shuffle, so
+    no two layers' tables agree."""
+    from block_diffusion_draft_qkv_amd import PagedKVCache
+    c = case.cfg
+    tot = case.cached_len + case.new_ctx
+    need = [-(-int(t) // 64) for t in tot]
+    rng = np.random.default_rng(seed)
+    caches = []
+    for layer in range(c.n_layers):
+        spare = 4 if tables == "shared" else 4 + 3 * layer
+        kv = PagedKVCache(case.batch, c.n_kv_heads, c.head_dim, sum(need) + spare, max(need) + 1, dt)
+        fill_canary(kv.k)
+        fill_canary(kv.v)
+        if tables == "shared" and caches:
+            kv.free = list(caches[0].free_at_start)
+        else:
+            rng.shuffle(kv.free)
+        kv.free_at_start = list(kv.free)
+        for b in range(case.batch):
+            kv.write_prefix(b, dev(case.cache_k[layer][b], dt), dev(case.cache_v[layer][b], dt))
+            kv.reserve(b, int(tot[b]))
+        kv.sync()
+        caches.append(kv)
+    if tables == "shared":
+        for kv in caches[1:]:
+            assert np.array_equal(kv.table_host, caches[0].table_host)
+            kv.table = caches[0].table
+            kv.desc.block_table = caches[0].table.data_ptr()
+    else:
+        for a in range(c.n_layers):
+            for b in range(a + 1, c.n_layers):
+                assert not np.array_equal(caches[a].table_host, caches[b].table_host)
+    return caches
+
+
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+@pytest.mark.parametrize("tables", ["shared", "per_layer"])
+def test_context_precompute_into_paged_stack(tables, mode):
+    """The multi-layer precompute writing three layers' paged caches, which
+    share one block table or each have their own (a slot mapping for all
+    layers or one per layer), in both append modes."""
+    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape
     pc = CTXKV_CONFIGS["P3"].replace(batch=4, hidden=512, n_kv_heads=2, cached_len=(0, 300), new_ctx=(1, 40),
                                      config_id=77)
     case = make_ctxkv_case(pc, seed=6)
@@ -164,25 +206,9 @@ def test_context_precompute_into_paged_stack():
                                                      c.rope_theta, c.rms_eps, c.max_position),
                                       dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt),
                                       dev(w.k_norm, dt)))
+    pre.set_append_mode(mode)
     tot = case.cached_len + case.new_ctx
-    need = [-(-int(t) // 64) for t in tot]
-    caches = [PagedKVCache(case.batch, c.n_kv_heads, c.head_dim, sum(need) + 4, max(need) + 1, dt)
-              for _ in range(c.n_layers)]
-    order = list(caches[0].free)
-    np.random.default_rng(4).shuffle(order)
-    for layer, kv in enumerate(caches):
-        fill_canary(kv.k)
-        fill_canary(kv.v)
-        kv.free = list(order)
-        for b in range(case.batch):
-            kv.write_prefix(b, dev(case.cache_k[layer][b], dt), dev(case.cache_v[layer][b], dt))
-            kv.reserve(b, int(tot[b]))
-        kv.sync()
-    # one shared table: every layer allocated the same blocks in the same order
-    for kv in caches[1:]:
-        assert np.array_equal(kv.table_host, caches[0].table_host)
-        kv.table = caches[0].table
-        kv.desc.block_table = caches[0].table.data_ptr()
+    caches = paged_stack(case, dt, 4, tables)
     befores = [(raw_bits(kv.k), raw_bits(kv.v)) for kv in caches]
     pre.append(dev(case.context_states, dt), case.ctx_offsets, torch.from_numpy(case.positions).cuda(), caches)
     torch.cuda.synchronize()
@@ -191,7 +217,51 @@ def test_context_precompute_into_paged_stack():
                                               for l in range(c.n_layers)],
                                        case.context_states, case.ctx_offsets, case.positions)
     for layer, kv in enumerate(caches):
+        assert kv.lengths.tolist() == tot.tolist()
         check_paged_after(kv, *befores[layer], case.cached_len, tot, ref[layer], "bf16", f"layer {layer}")
+
+
+def test_paged_stack_rejections_leave_every_layer_alone():
+    """A bad entry in one layer's own table (past its pools, or a block the
+    append needs left out) and a mix of paged and contiguous layers are
+    refused before anything runs: no layer's pools or lengths change."""
+    from block_diffusion_draft_qkv_amd import ContextKV, ContextKVShape, DFlashError, KVCache, _lib
+    pc = CTXKV_CONFIGS["P3"].replace(batch=3, hidden=512, n_kv_heads=2, cached_len=(0, 200), new_ctx=(1, 30),
+                                     config_id=79)
+    case = make_ctxkv_case(pc, seed=8)
+    c, w, dt = case.cfg, case.weights, torch.bfloat16
+    pre = poison_workspaces(ContextKV(ContextKVShape(c.hidden, c.n_layers, c.n_kv_heads, c.head_dim, dt,
+                                                     c.rope_theta, c.rms_eps, c.max_position),
+                                      dev(w.hidden_norm, dt), dev(w.w_kv.reshape(-1, c.hidden), dt),
+                                      dev(w.k_norm, dt)))
+    caches = paged_stack(case, dt, 9, "per_layer")
+    befores = [(raw_bits(kv.k), raw_bits(kv.v), kv.lengths.copy()) for kv in caches]
+    args = (dev(case.context_states, dt), case.ctx_offsets, torch.from_numpy(case.positions).cuda())
+    last = caches[-1]
+    good = int(last.table_host[1, 0])
+    last.table_host[1, 0] = last.num_blocks              # past the last layer's pools
+    with pytest.raises(DFlashError) as e:
+        pre.append(*args, caches)
+    assert e.value.status == _lib.DFLASH_ERR_RANGE
+    last.table_host[1, 0] = good
+    b = int(np.argmax(case.new_ctx > 0))
+    tail = last.blocks_of(b) - 1
+    blk = int(last.table_host[b, tail])
+    last.table_host[b, tail] = -1                        # a block the append writes is missing
+    with pytest.raises(DFlashError) as e:
+        pre.append(*args, caches)
+    assert e.value.status == _lib.DFLASH_ERR_RANGE
+    last.table_host[b, tail] = blk
+    flat = KVCache(case.batch, c.n_kv_heads, c.head_dim, last.capacity, dt)
+    flat.lengths[:] = last.lengths
+    with pytest.raises(DFlashError) as e:
+        pre.append(*args, caches[:-1] + [flat])
+    assert e.value.status == _lib.DFLASH_ERR_SHAPE
+    torch.cuda.synchronize()
+    for kv, (bk, bv, lens) in zip(caches, befores):
+        np.testing.assert_array_equal(raw_bits(kv.k), bk)
+        np.testing.assert_array_equal(raw_bits(kv.v), bv)
+        assert kv.lengths.tolist() == lens.tolist()
 
 
 def test_bad_block_tables_are_rejected_before_enqueueing():
