@@ -7,7 +7,13 @@ warns that it does not know that feature, which is harmless. MFMA results are
 kept in ordinary VGPRs (``-amdgpu-mfma-vgpr-form``) so that the online-softmax
 rescale of the accumulators needs no AGPR moves.
 
-Usage: ``python -m block_diffusion_draft_qkv_amd.build [--debug]``.
+``build(sanitize=True)`` instead compiles the same sources with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+(``-Xarch_host`` before each ``-fsanitize=``; the device code is unchanged) into
+the static archive ``_build/sanitize/libdflash_san.a``, for a host-only check
+program that links it with a host stand-in of the HIP runtime.
+
+Usage: ``python -m block_diffusion_draft_qkv_amd.build [--debug] [--sanitize]``.
 """
 from __future__ import annotations
 
@@ -43,14 +49,20 @@ def flags(debug: bool = False):
     return f
 
 
-def build(debug: bool = False, verbose: bool = False) -> str:
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(PKG, "_build", "sanitize", "libdflash_san.a")
+
+
+def build(debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
     cc = hipcc()
-    out_dir = os.path.join(PKG, "_build")
+    out_dir = os.path.join(PKG, "_build", "sanitize") if sanitize else os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
+    extra = [*SANITIZE_FLAGS, "-O1", "-g"] if sanitize else []
 
     def compile_one(src: str) -> str:
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *flags(debug), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(debug), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-xhip")
         if verbose:
@@ -62,6 +74,15 @@ def build(debug: bool = False, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
+    if sanitize:
+        tmp = SAN_LIB + ".tmp"
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        r = subprocess.run(["ar", "rcs", tmp, *objs], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"ar failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, SAN_LIB)
+        return SAN_LIB
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -75,6 +96,7 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true")
     a = ap.parse_args()
-    print(build(debug=a.debug, verbose=a.verbose))
+    print(build(debug=a.debug, verbose=a.verbose, sanitize=a.sanitize))
     sys.exit(0)

@@ -1,0 +1,24 @@
+// Queries of the host-memory HIP stand-in (hip_stub.cpp) for the host check.
+#pragma once
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  char name[160];
+  unsigned grid[3], block[3];
+  size_t shmem;
+} StubLaunch;
+
+size_t stub_live_allocations(void);             /* hipMalloc blocks not yet freed      */
+size_t stub_allocation_size(const void* p);     /* bytes of a live block, else 0       */
+size_t stub_launch_count(void);
+StubLaunch stub_launch(size_t i);
+void stub_clear_launches(void);
+void stub_fail_malloc_after(int n);             /* the n-th next hipMalloc fails (0: the next) */
+
+#ifdef __cplusplus
+}
+#endif
