@@ -37,10 +37,14 @@ METRIC = "draft-block tokens/s + attention HBM GB/s (% of peak), B=32 ctx 512–
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_splitkv_c3_traffic.json")
-# every source the attention kernel is compiled from
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_merge_c3_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "projection_gemms_c3_mfma_counters.json")
+# every source the attention and merge kernels are compiled and planned from
 ATTN_SOURCES = [os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", f)
-                for f in ("attention.hip", "kernels.h", "common.h", "lds_dma.h")]
+                for f in ("attention.hip", "kernels.h", "common.h", "lds_dma.h", "dflash.cpp")]
+# every source the projection GEMMs are compiled and planned from
+GEMM_SOURCES = [os.path.join(ROOT, "block_diffusion_draft_qkv_amd", "csrc", f)
+                for f in ("gemm.hip", "kernels.h", "common.h", "lds_dma.h", "dflash.cpp")]
 
 
 def parse():
@@ -109,9 +113,9 @@ def source_hash(paths) -> str:
 
 
 def traffic_per_launch(workload: str):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when there is none, it covers another workload, or the kernel's
-    sources changed since it was taken."""
+    """HBM bytes of one attention launch and its merge from the committed
+    counter summary, or None when there is none, it covers another workload,
+    or the kernels' sources changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -121,6 +125,20 @@ def traffic_per_launch(workload: str):
     if rec.get("attention_source_sha256_16") != source_hash(ATTN_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def mfma_counters(workload: str):
+    """The projection GEMMs' MFMA counters (utilisation, counted flops per
+    dispatch duration) from the committed counter summary, or None when there
+    is none, it covers another workload, or the GEMM sources changed since."""
+    try:
+        rec = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    if not rec.get("workload", "").startswith(workload) or rec.get("gemm_source_sha256_16") != source_hash(GEMM_SOURCES):
+        return None
+    return {k: {"mfma_util": v["mfma_util"], "counted_tflops": v["tflops"], "dispatch_us": v["dispatch_us"]}
+            for k, v in rec["kernels"].items()}
 
 
 def copy_calibration():
@@ -779,6 +797,7 @@ def main():
             "bound": "mfma", "flops_per_step": proj_flops,
             "achieved_tflops": round(proj_flops / (t_proj * 1e-6) / 1e12, 1) if t_proj else None,
             "peak_tflops": BF16_PEAK_TFLOPS,
+            "counters": mfma_counters(f"{cfg.name}: ") if a.seed == 0 else None,
         },
         "kernel_mean_us": {k: round(mean_us(k), 2) for k in kt},
         "kernel_sum_us_per_step": round(sum(v[0] for v in kt.values()) * 1e3 / a.steps, 2),
