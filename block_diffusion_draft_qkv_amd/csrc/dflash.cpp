@@ -246,6 +246,36 @@ TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, b
   return choose_tiles(L->num_cus, m0, n0, m1, n1, allow_split);
 }
 
+// Tile shape and k split of a plain projection with a deep k (m x n outputs,
+// k deep, es-byte elements). Its work-groups are bound by the bytes each
+// streams into LDS, so a launch is modelled as rounds x (a ~15 us ramp and
+// epilogue + (BM + BN) (k / ks) es bytes at ~100 GB/s per CU), plus, with a k
+// split, ~3 us for the summing launch and the fp32 partials' round trip at
+// ~8 TB/s. Fitted to measured launches on gfx950 (decoder down_proj 512 x 4096
+// x 12288: 128 x 64 unsplit 397 us per decoder step, 128 x 128 in two slices
+// 386 us; fc projection 281 x 4096 x 12288: 128 x 64 62.7 us, 128 x 128 in
+// two slices 53.0 us, 128 x 128 unsplit 80.3 us). Ties keep the larger tiles
+// and the fewer slices.
+TileChoice choose_tiles_fill(int num_cus, int m, int n, int k, int es, int max_ks) {
+  static const int cand[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
+  const int steps = k * es / 128;  // 128-byte k steps
+  TileChoice best{64, 64, ((m + 63) / 64) * ((n + 63) / 64), 1};
+  double best_t = -1.0;
+  for (int i = 0; i < 4; ++i)
+    for (int ks = 1; ks <= std::max(1, std::min(max_ks, steps)); ++ks) {
+      const int bm = cand[i][0], bn = cand[i][1];
+      const int64_t tiles = (int64_t)((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+      const int64_t rounds = (tiles * ks + num_cus - 1) / num_cus;
+      double t = (double)rounds * (15.0 + (double)(bm + bn) * ((double)k / ks) * es / 1e5);
+      if (ks > 1) t += 3.0 + 2.0 * ks * (double)m * n * 4 / 8e6;
+      if (best_t < 0 || t < best_t - 1e-9) {
+        best_t = t;
+        best = TileChoice{bm, bn, (int)tiles, ks};
+      }
+    }
+  return best;
+}
+
 // Workspace of a context precompute of mc rows: hidden_norm-ed rows in the
 // element type, then the fp32 projection [k slices][mc][L * 2 * nkv * d]. With
 // MXFP8 weights: the hidden_norm-ed rows as E4M3 codes [mc][H] and their E8M0
@@ -918,7 +948,7 @@ int dflash_ctxkv_combine(dflash_ctxkv* h, const void* aux_states, int64_t rows, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Few rows and a long k: split k over fp32 slices in the workspace and sum
   // them (one rounding to the dtype); otherwise the GEMM rounds directly.
-  const TileChoice t = choose_tiles(h->num_cus, (int)rows, H, 0, 0, true);
+  const TileChoice t = choose_tiles_fill(h->num_cus, (int)rows, H, K, c.dtype == DFLASH_BF16 ? 2 : 4, kMaxKSlices);
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.nprob = 1;
@@ -1141,6 +1171,13 @@ namespace {
 struct DecCarve {
   size_t attn, a, att, h, m, act, total;
 };
+// down_proj's tiles; k slices only where their fp32 partials fit the attention
+// step's scratch region.
+TileChoice down_tiles(const dflash_decoder* D, int m, int n, int k, size_t scratch_bytes) {
+  const int es = D->cfg.attn.dtype == DFLASH_BF16 ? 2 : 4;
+  const int fit = (int)std::min<size_t>(kMaxKSlices, scratch_bytes / ((size_t)m * n * 4));
+  return choose_tiles_fill(D->num_cus, m, n, k, es, fit);
+}
 DecCarve dec_carve(const dflash_decoder* D, int64_t batch, int64_t total_ctx) {
   const dflash_config& c = D->cfg.attn;
   const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, mq = batch * c.block_size;
@@ -1257,13 +1294,25 @@ int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hid
   }
   // out = h + act Wd^T
   {
-    const TileChoice t = choose_tiles(D->num_cus, Mq, H, 0, 0, false);
+    const TileChoice t = down_tiles(D, Mq, H, I, attn_bytes);
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.nprob = 1;
     ga.p[0] = {act, D->w.w_down, out, Mq, H, I, I, I, H, (H + t.bn - 1) / t.bn, 0, 0};
-    ga.p[0].r = h;
-    if (launch_gemm(c.dtype, false, ga, t.tiles, t.bm, t.bn, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (t.kslices > 1) {
+      // fp32 k slices in the attention step's scratch (consumed by now), summed
+      // with the residual into out (one rounding)
+      const int64_t slice = (int64_t)Mq * H;
+      float* part = reinterpret_cast<float*>(ws + wc.attn);
+      ga.p[0].c = part;
+      ga.p[0].slice_stride = slice;
+      if (launch_gemm(c.dtype, true, ga, t.tiles, t.bm, t.bn, t.kslices, s) != hipSuccess) return DFLASH_ERR_HIP;
+      if (launch_sum_slices(c.dtype == DFLASH_BF16 ? 1 : 0, part, t.kslices, slice, out, slice, s, h) != hipSuccess)
+        return DFLASH_ERR_HIP;
+    } else {
+      ga.p[0].r = h;
+      if (launch_gemm(c.dtype, false, ga, t.tiles, t.bm, t.bn, 1, s) != hipSuccess) return DFLASH_ERR_HIP;
+    }
   }
   return DFLASH_OK;
 }

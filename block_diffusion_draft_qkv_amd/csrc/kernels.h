@@ -166,10 +166,11 @@ hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormR
 // [h / 128][step_rows][4] when step_rows > 0 (step_rows >= rows).
 hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
                               float eps, int step_rows, hipStream_t stream);
-// out[i] = sum_s in[s * slice_stride + i] rounded to the dtype (0 fp32, 1
-// bf16) for i < n (n % 4 == 0, 16-byte aligned buffers).
+// out[i] = sum_s in[s * slice_stride + i] (+ residual[i] when given, in the
+// dtype) rounded to the dtype (0 fp32, 1 bf16) for i < n (n % 4 == 0, 16-byte
+// aligned buffers).
 hipError_t launch_sum_slices(int dtype, const float* in, int slices, int64_t slice_stride, void* out, int64_t n,
-                             hipStream_t stream);
+                             hipStream_t stream, const void* residual = nullptr);
 // Two bf16 row sets [rows1][h], [rows2][h] quantised (no norm) in one launch,
 // each with step-major scales [h / 128][rows_i][4].
 hipError_t launch_rows_mx2(const void* x1, uint8_t* c1, uint8_t* s1, int rows1, const void* x2, uint8_t* c2,

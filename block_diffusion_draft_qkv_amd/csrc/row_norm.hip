@@ -209,16 +209,22 @@ __global__ __launch_bounds__(256) void rms_rows_mx_kernel(const __bf16* __restri
   mx_row(x, g, codes, scales, blockIdx.x, h, eps, step_rows);
 }
 
-// out[i] = sum over s of in[s * slice_stride + i], rounded once to T: the
-// k-sliced fp32 partial sums of a projection folded into its output. Four
-// elements per thread (n % 4 == 0, 16-byte aligned rows).
+// out[i] = sum over s of in[s * slice_stride + i] (+ res[i]), rounded once to
+// T: the k-sliced fp32 partial sums of a projection folded into its output,
+// with the residual of a projection that adds one. Four elements per thread
+// (n % 4 == 0, 16-byte aligned rows).
 template <typename T>
 __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ in, int slices,
-                                                         int64_t slice_stride, T* __restrict__ out, int64_t n4) {
+                                                         int64_t slice_stride, const T* __restrict__ res,
+                                                         T* __restrict__ out, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   f32x4 acc = reinterpret_cast<const f32x4*>(in)[i];
   for (int s = 1; s < slices; ++s) acc += reinterpret_cast<const f32x4*>(in + (size_t)s * slice_stride)[i];
+  if (res != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += Elem<T>::to_f32(res[4 * i + r]);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) out[4 * i + r] = Elem<T>::from_f32(acc[r]);
 }
@@ -255,16 +261,16 @@ hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint
 }
 
 hipError_t launch_sum_slices(int dtype, const float* in, int slices, int64_t slice_stride, void* out, int64_t n,
-                             hipStream_t stream) {
+                             hipStream_t stream, const void* residual) {
   if (n <= 0) return hipSuccess;
   const int64_t n4 = n / 4;
   const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
   if (dtype == 1)
     hipLaunchKernelGGL(sum_slices_kernel<__bf16>, grid, block, 0, stream, in, slices, slice_stride,
-                       static_cast<__bf16*>(out), n4);
+                       static_cast<const __bf16*>(residual), static_cast<__bf16*>(out), n4);
   else
     hipLaunchKernelGGL(sum_slices_kernel<float>, grid, block, 0, stream, in, slices, slice_stride,
-                       static_cast<float*>(out), n4);
+                       static_cast<const float*>(residual), static_cast<float*>(out), n4);
   return hipGetLastError();
 }
 
