@@ -313,8 +313,13 @@ class DFlashLayer:
         ``"auto"`` (default), ``"fused"`` (projection epilogue) or ``"separate"``."""
         check(_lib.lib().dflash_layer_set_append_mode(self._h, _lib.APPEND_MODES[mode]), "set_append_mode")
 
-    def set_profiling(self, enable: bool) -> None:
-        check(_lib.lib().dflash_layer_set_profiling(self._h, int(bool(enable))), "set_profiling")
+    def set_profiling(self, enable) -> None:
+        """``True`` / ``"kernels"``: HIP events around each kernel of a step;
+        ``"attn_span"``: one pair around the attention and its merge
+        (``"attn_merge"`` in ``kernel_times``); ``False`` / ``"off"``."""
+        if enable not in _lib.PROFILE_MODES:
+            raise ValueError(f"unknown profiling mode {enable!r}")
+        check(_lib.lib().dflash_layer_set_profiling(self._h, _lib.PROFILE_MODES[enable]), "set_profiling")
 
     def kernel_times(self):
         """``{kernel name: (total ms, launches)}`` since profiling was enabled."""

@@ -24,7 +24,8 @@ DFLASH_BF16 = 1
 DFLASH_MAX_BATCH = 256
 DFLASH_NOALLOC_SCRATCH_BYTES = 64 << 20
 APPEND_MODES = {"auto": 0, "fused": 1, "separate": 2}
-KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o")
+KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o", "attn_merge")
+PROFILE_MODES = {False: 0, True: 1, "off": 0, "kernels": 1, "attn_span": 2}
 
 # Every symbol include/dflash.h declares.
 EXPORTS = (

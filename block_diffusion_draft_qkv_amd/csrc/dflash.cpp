@@ -87,7 +87,7 @@ struct dflash_layer {
   int num_cus = 256;
   float* cos_sin = nullptr;  // [max_pos][d/2] cos, then [max_pos][d/2] sin
   int32_t* err = nullptr;
-  bool profiling = false;
+  int profiling = 0;  // DFLASH_PROFILE_*
   int append_mode = DFLASH_APPEND_AUTO;
   bool mx = false;                 // MXFP8 projections (dflash_layer_create_mxfp8): w holds E4M3 codes
   uint8_t* wqkv_scale = nullptr;   // their scales, repacked step-major (owned)
@@ -373,13 +373,15 @@ hipEvent_t pooled_event(dflash_layer* L) {
   hipEventCreate(&e);
   return e;
 }
-void record(dflash_layer* L, hipEvent_t* start, hipStream_t s) {
-  if (!L->profiling) return;
+// Events of the profiling mode `mode` (per-kernel pairs, or the one pair
+// around the attention and its merge); nothing in the other modes.
+void record(dflash_layer* L, hipEvent_t* start, hipStream_t s, int mode = DFLASH_PROFILE_KERNELS) {
+  if (L->profiling != mode) return;
   *start = pooled_event(L);
   hipEventRecord(*start, s);
 }
-void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s) {
-  if (!L->profiling) return;
+void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s, int mode = DFLASH_PROFILE_KERNELS) {
+  if (L->profiling != mode) return;
   hipEvent_t stop = pooled_event(L);
   hipEventRecord(stop, s);
   L->pending.push_back({kernel, start, stop});
@@ -712,6 +714,8 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
         f = end;
       }
   }
+  hipEvent_t span = nullptr;
+  record(L, &span, s, DFLASH_PROFILE_ATTN_SPAN);
   record(L, &ev, s);
   if (launch_attn(c.dtype, d, aa, s) != hipSuccess) return DFLASH_ERR_HIP;
   record_end(L, DFLASH_K_ATTN, ev, s);
@@ -744,6 +748,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     if (launch_merge(c.dtype, d, ma, s) != hipSuccess) return DFLASH_ERR_HIP;
     record_end(L, DFLASH_K_MERGE, ev, s);
   }
+  record_end(L, DFLASH_K_ATTN_MERGE, span, s, DFLASH_PROFILE_ATTN_SPAN);
 
   // HK1: o_proj (k split as decided above)
   const int64_t o_slice = (int64_t)Mq * H;
@@ -823,7 +828,7 @@ int dflash_layer_set_append_mode(dflash_layer* L, int32_t mode) {
 }
 
 int dflash_layer_set_profiling(dflash_layer* L, int32_t enable) {
-  if (!L) return DFLASH_ERR_ARG;
+  if (!L || enable < DFLASH_PROFILE_OFF || enable > DFLASH_PROFILE_ATTN_SPAN) return DFLASH_ERR_ARG;
   if (hipDeviceSynchronize() != hipSuccess) return DFLASH_ERR_HIP;
   for (auto& p : L->pending) {
     L->event_pool.push_back(p.start);
@@ -832,7 +837,7 @@ int dflash_layer_set_profiling(dflash_layer* L, int32_t enable) {
   L->pending.clear();
   std::fill(L->ms, L->ms + DFLASH_K_COUNT, 0.0);
   std::fill(L->count, L->count + DFLASH_K_COUNT, 0);
-  L->profiling = enable != 0;
+  L->profiling = enable;
   return DFLASH_OK;
 }
 

@@ -305,20 +305,30 @@ int dflash_layer_poll_error(dflash_layer* layer, void* stream);
 enum { DFLASH_APPEND_AUTO = 0, DFLASH_APPEND_FUSED = 1, DFLASH_APPEND_SEPARATE = 2 };
 int dflash_layer_set_append_mode(dflash_layer* layer, int32_t mode);
 
-/* Per-kernel timing with HIP events recorded on the launch stream around each
- * kernel of a step. enable != 0 turns it on (and clears the totals). */
+/* Timing with HIP events recorded on the launch stream. enable:
+ *   DFLASH_PROFILE_OFF        no events (the default)
+ *   DFLASH_PROFILE_KERNELS    an event pair around each kernel of a step
+ *   DFLASH_PROFILE_ATTN_SPAN  one pair around the attention and its merge
+ *                             together (DFLASH_K_ATTN_MERGE), nothing between
+ *                             them: every event packet on the stream adds its
+ *                             own time, so per-kernel pairs overstate a span
+ *                             of consecutive kernels.
+ * Setting a mode synchronises the device and clears the totals.
+ * Errors: DFLASH_ERR_ARG (null layer, unknown mode), DFLASH_ERR_HIP. */
+enum { DFLASH_PROFILE_OFF = 0, DFLASH_PROFILE_KERNELS = 1, DFLASH_PROFILE_ATTN_SPAN = 2 };
 int dflash_layer_set_profiling(dflash_layer* layer, int32_t enable);
 
 /* Synchronise on the recorded events and return, for each kernel of the step
  * (indices DFLASH_K_*), the summed milliseconds and the number of launches
- * since profiling was enabled. `ms` and `count` hold DFLASH_K_COUNT entries. */
+ * (spans) since the profiling mode was set. `ms` and `count` hold DFLASH_K_COUNT entries. */
 enum {
     DFLASH_K_GEMM_QKV = 0,   /* grouped projection: block QKV and context KV     */
     DFLASH_K_NORM_ROPE = 1,  /* per-head RMSNorm + RoPE + Q pack + cache append   */
     DFLASH_K_ATTN = 2,       /* split-KV non-causal GQA attention                 */
     DFLASH_K_MERGE = 3,      /* log-sum-exp merge of split partials               */
     DFLASH_K_GEMM_O = 4,     /* o_proj                                            */
-    DFLASH_K_COUNT = 5
+    DFLASH_K_ATTN_MERGE = 5, /* attention + merge as one span (ATTN_SPAN mode)   */
+    DFLASH_K_COUNT = 6
 };
 int dflash_layer_kernel_times(dflash_layer* layer, double* ms, int64_t* count);
 

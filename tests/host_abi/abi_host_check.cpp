@@ -408,6 +408,18 @@ void test_layer_steps_fixed() {
         CHECK(cnt[DFLASH_K_GEMM_QKV] == 1 && cnt[DFLASH_K_ATTN] == 1 && cnt[DFLASH_K_GEMM_O] == 1,
               "kernel counts %lld %lld %lld", (long long)cnt[0], (long long)cnt[2], (long long)cnt[4]);
       }
+      // one span around the attention and its merge, nothing per kernel
+      CHECK(dflash_layer_set_profiling(L, DFLASH_PROFILE_ATTN_SPAN) == DFLASH_OK, "span profiling");
+      {
+        Cache cache(2, 2, d, es, 128, false, 0, &rng);
+        run_step(L, c, cache, offsets({4, 4}), false, DFLASH_OK, "span-profiled step");
+        double ms[DFLASH_K_COUNT];
+        int64_t cnt[DFLASH_K_COUNT];
+        CHECK(dflash_layer_kernel_times(L, ms, cnt) == DFLASH_OK, "span times");
+        CHECK(cnt[DFLASH_K_ATTN_MERGE] == 1 && cnt[DFLASH_K_ATTN] == 0 && cnt[DFLASH_K_GEMM_QKV] == 0,
+              "span counts %lld %lld", (long long)cnt[DFLASH_K_ATTN_MERGE], (long long)cnt[DFLASH_K_ATTN]);
+      }
+      CHECK(dflash_layer_set_profiling(L, 3) == DFLASH_ERR_ARG, "unknown profiling mode");
       CHECK(dflash_layer_set_profiling(L, 0) == DFLASH_OK, "profiling off");
       CHECK(dflash_layer_poll_error(L, nullptr) == DFLASH_OK, "poll");
       dflash_layer_destroy(L);
