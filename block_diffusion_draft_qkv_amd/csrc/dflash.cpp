@@ -253,17 +253,22 @@ TileChoice choose_tiles(const dflash_layer* L, int m0, int n0, int m1, int n1, b
 // split, ~3 us for the summing launch and the fp32 partials' round trip at
 // ~8 TB/s. Fitted to measured launches on gfx950 (decoder down_proj 512 x 4096
 // x 12288: 128 x 64 unsplit 397 us per decoder step, 128 x 128 in two slices
-// 386 us; fc projection 281 x 4096 x 12288: 128 x 64 62.7 us, 128 x 128 in
-// two slices 53.0 us, 128 x 128 unsplit 80.3 us). Ties keep the larger tiles
-// and the fewer slices.
-TileChoice choose_tiles_fill(int num_cus, int m, int n, int k, int es, int max_ks) {
-  static const int cand[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
+// 386 us, 256 x 128 in four slices 8 us less again; fc projection 281 x 4096
+// x 12288: 128 x 64 62.7 us, 128 x 128 in two slices 53.0 us, 128 x 128
+// unsplit 80.3 us, 256 x 128 in four slices 62.5 us; 4096 x 4096 x 12288:
+// 128 x 128 440 us, 256 x 128 431 us). 256-row tiles (bf16 only) are offered
+// only when they cover m exactly: the half-empty second row tile of m = 281
+// measured slower than the model says. Ties keep the larger tiles and the
+// fewer slices. only_bn != 0 restricts the tiles to that width.
+TileChoice choose_tiles_fill(int num_cus, int m, int n, int k, int es, int max_ks, int only_bn = 0) {
+  static const int cand[5][2] = {{256, 128}, {128, 128}, {128, 64}, {64, 128}, {64, 64}};
   const int steps = k * es / 128;  // 128-byte k steps
   TileChoice best{64, 64, ((m + 63) / 64) * ((n + 63) / 64), 1};
   double best_t = -1.0;
-  for (int i = 0; i < 4; ++i)
+  for (int i = (es == 2 && m % 256 == 0) ? 0 : 1; i < 5; ++i)
     for (int ks = 1; ks <= std::max(1, std::min(max_ks, steps)); ++ks) {
       const int bm = cand[i][0], bn = cand[i][1];
+      if (only_bn && bn != only_bn) continue;
       const int64_t tiles = (int64_t)((m + bm - 1) / bm) * ((n + bn - 1) / bn);
       const int64_t rounds = (tiles * ks + num_cus - 1) / num_cus;
       double t = (double)rounds * (15.0 + (double)(bm + bn) * ((double)k / ks) * es / 1e5);
@@ -1283,19 +1288,17 @@ int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hid
   if (st != DFLASH_OK) return st;
   // h = x + att (the residual stream), m = post_attention_layernorm(h)
   if (launch_rms_rows(c.dtype, x, att, D->w.post_norm, h, m, Mq, H, eps, s) != hipSuccess) return DFLASH_ERR_HIP;
-  // act = silu(m Wg^T) * (m Wu^T)
+  // act = silu(m Wg^T) * (m Wu^T): 128-column tiles (64 gate + 64 up) of the
+  // rows the fill model picks, no k split (the activation needs whole sums)
   {
     const int tn = (2 * I + 127) / 128;
-    const int t64 = ((Mq + 63) / 64) * tn, t128 = ((Mq + 127) / 128) * tn;
-    const long r64 = (long)((t64 + D->num_cus - 1) / D->num_cus) * (64 + 128);
-    const long r128 = (long)((t128 + D->num_cus - 1) / D->num_cus) * (128 + 128);
-    const int bm = r128 <= r64 ? 128 : 64;
+    const int bm = choose_tiles_fill(D->num_cus, Mq, 2 * I, H, elem_size(c), 1, 128).bm;
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.nprob = 1;
     ga.p[0] = {m, D->w.w_gate_up, act, Mq, 2 * I, H, H, H, I, tn, 0, 0};
     ga.p[0].b_pair = I;
-    if (launch_gemm_swiglu(c.dtype, ga, bm == 128 ? t128 : t64, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
+    if (launch_gemm_swiglu(c.dtype, ga, ((Mq + bm - 1) / bm) * tn, bm, s) != hipSuccess) return DFLASH_ERR_HIP;
   }
   // out = h + act Wd^T
   {

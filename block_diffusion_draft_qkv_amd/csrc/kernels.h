@@ -44,7 +44,7 @@ struct GemmArgs {
 };
 // dtype: 0 fp32, 1 bf16 (A, B element type). out_f32: C is fp32, else C has
 // the element type of A and B (then kslices must be 1). (bm, bn) in
-// {64, 128}^2.
+// {64, 128}^2, or 256 x 128 for bf16.
 hipError_t launch_gemm(int dtype, bool out_f32, const GemmArgs& args, int total_tiles, int bm, int bn,
                        int kslices, hipStream_t stream);
 
