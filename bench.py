@@ -575,7 +575,9 @@ def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     caches = []
     for i in range(copies):
         c = PagedKVCache(B, cfg.n_kv_heads, cfg.head_dim, sum(need) + 4 * B, max(need) + 4, dt)
-        np.random.default_rng(seed + i).shuffle(c.free)
+        order = c.free
+        np.random.default_rng(seed + i).shuffle(order)
+        c.free = order
         for b in range(B):
             c.write_prefix(b, dev(case.cache_k[b]), dev(case.cache_v[b]))
             c.reserve(b, int(case.total_len[b]))
@@ -619,6 +621,9 @@ def bench_paged(steps: int, warmup: int, seed: int = 0, copies: int = 3):
     c.crop_all(L0)
     rng = np.random.default_rng(seed + 7)
     accepts = rng.integers(0, bs + 1, size=(steps, B))
+    for r in range(min(warmup, steps)):
+        run_round(layer, c, hs, th, offs, accepts[r], out=out)
+        c.crop_all(L0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(steps):

@@ -98,7 +98,8 @@ def _check_step_args(shape: "LayerShape", device: torch.device, act_dtype: torch
         if target_hidden is None:
             raise ValueError(f"target_hidden is required for {mc} new context rows")
         _check_tensor(target_hidden, "target_hidden", act_dtype, (mc, H), device)
-    _check_tensor(positions, "positions", torch.int32, (mc + B * bs,), device)
+    if positions is not None:  # None: contiguous positions len_b, len_b + 1, ... (the library's)
+        _check_tensor(positions, "positions", torch.int32, (mc + B * bs,), device)
     if out is not None:
         _check_tensor(out, "out", act_dtype, (B * bs, H), device)
         if out.data_ptr() == x.data_ptr():
@@ -413,7 +414,8 @@ class ContextKV:
         offs = _ctx_offsets(ctx_offsets, B)
         mc = int(offs[-1])
         _check_tensor(context_states, "context_states", s.dtype, (mc, s.hidden), self.device)
-        _check_tensor(positions, "positions", torch.int32, (mc,), self.device)
+        if positions is not None:  # None: contiguous positions len_b, len_b + 1, ...
+            _check_tensor(positions, "positions", torch.int32, (mc,), self.device)
         if workspace is not None:
             _check_workspace(workspace, self.device)
         offs = (C.c_int32 * (B + 1))(*offs.tolist())
@@ -620,44 +622,15 @@ def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float, out: Optional[torc
     return out
 
 
-class _PinnedUploads:
-    """Stream-ordered host-to-device copies of small int32 arrays through a
-    ring of pinned staging buffers. A copy from pageable memory would block the
-    host until the device caught up; here a buffer is only refilled once the
-    copy that last read it has completed (its event), so the host can enqueue
-    ahead of the device."""
-
-    def __init__(self, capacity: int, depth: int = 4):
-        self.capacity = int(capacity)
-        self._bufs = [torch.empty(self.capacity, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
-        self._events = [None] * depth
-        self._i = 0
-
-    def upload(self, src: np.ndarray, dst: torch.Tensor, stream=None) -> None:
-        src = np.ascontiguousarray(src, dtype=np.int32).reshape(-1)
-        if src.size > self.capacity or dst.numel() < src.size or dst.dtype != torch.int32:
-            raise ValueError("upload does not fit its staging buffer or destination")
-        i = self._i
-        self._i = (i + 1) % len(self._bufs)
-        if self._events[i] is not None:
-            self._events[i].synchronize()
-        buf = self._bufs[i][: src.size]
-        buf.numpy()[:] = src
-        s = torch.cuda.current_stream(dst.device) if stream is None else stream
-        with torch.cuda.stream(s):
-            dst.view(-1)[: src.size].copy_(buf, non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(s)
-        self._events[i] = ev
-
-
 class PagedKVCache:
     """Draft KV cache of ``batch`` sequences in 64-row blocks (the paged layout
     of include/dflash.h): pools ``k [num_blocks, n_kv, 64, d]`` and ``v
     [num_blocks, n_kv, d, 64]``, a block table per sequence (``max_blocks``
     entries; a device copy for the kernels and the host copy the library
-    checks) and a free list. Blocks are reserved before a step writes rows
-    and released when a crop drops them."""
+    checks) and the library's block pool (``dflash_block_pool``), which hands
+    out and takes back physical blocks and records the table entries it
+    changes until ``sync`` writes them to the device table. Blocks are
+    reserved before a step writes rows and released when a crop drops them."""
 
     BLOCK = 64
 
@@ -674,70 +647,67 @@ class PagedKVCache:
         self.table = torch.full((batch, max_blocks), -1, dtype=torch.int32, device=device)
         self._len = (C.c_int32 * max(batch, 1))()
         self.lengths = np.ctypeslib.as_array(self._len)[:batch]
-        self.free = list(range(num_blocks - 1, -1, -1))
         self.desc = _lib.KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(), C.cast(self._len, C.POINTER(C.c_int32)),
                                      batch, self.capacity, self.table.data_ptr(),
                                      C.cast(self._tab, C.POINTER(C.c_int32)), max_blocks, num_blocks)
-        self._dirty = False
-        self._uploads: Optional[_PinnedUploads] = None
+        self._pool = C.c_void_p()
+        check(_lib.lib().dflash_block_pool_create(int(num_blocks), C.byref(self._pool)), "dflash_block_pool_create")
+
+    def __del__(self):
+        pool = getattr(self, "_pool", None)
+        if pool and _lib._lib is not None:
+            _lib._lib.dflash_block_pool_destroy(pool)
+            self._pool = None
 
     # ------------------------------------------------------------ blocks
+    @property
+    def free(self) -> list:
+        """The free blocks, bottom of the stack first (the last is taken next);
+        assigning a list (e.g. a shuffled order) replaces them."""
+        n = int(_lib.lib().dflash_block_pool_free_count(self._pool))
+        buf = (C.c_int32 * max(n, 1))()
+        check(_lib.lib().dflash_block_pool_get_free(self._pool, buf, n), "dflash_block_pool_get_free")
+        return list(buf[:n])
+
+    @free.setter
+    def free(self, blocks) -> None:
+        arr = np.ascontiguousarray(blocks, dtype=np.int32)
+        check(_lib.lib().dflash_block_pool_set_free(self._pool, arr.ctypes.data_as(C.POINTER(C.c_int32)),
+                                                    int(arr.size)), "dflash_block_pool_set_free")
+
+    def _pool_call(self, fn, *args) -> None:
+        st = fn(C.byref(self.desc), self._pool, *args)
+        if st == _lib.DFLASH_ERR_SHAPE:
+            raise ValueError(f"a sequence would need more than max_blocks {self.max_blocks} blocks")
+        if st == _lib.DFLASH_ERR_CAPACITY:
+            raise MemoryError("no free cache block")
+        check(st, fn.__name__)
+
     def blocks_of(self, seq: int) -> int:
         return int(np.count_nonzero(self.table_host[seq] >= 0))
 
     def reserve(self, seq: int, rows: int) -> None:
-        """Back logical rows [0, rows) of ``seq`` with blocks."""
-        need = -(-int(rows) // self.BLOCK)
-        if need > self.max_blocks:
-            raise ValueError(f"sequence {seq} needs {need} blocks > max_blocks {self.max_blocks}")
-        for i in range(self.blocks_of(seq), need):
-            if not self.free:
-                raise MemoryError("no free cache block")
-            self.table_host[seq, i] = self.free.pop()
-            self._dirty = True
+        """Back logical rows [0, rows) of ``seq`` with blocks (all or nothing)."""
+        self._pool_call(_lib.lib().dflash_cache_reserve, int(seq), int(rows))
 
     def release(self, seq: int, rows: int) -> None:
-        """Return the blocks of ``seq`` past logical row ``rows`` to the free list."""
-        keep = -(-int(rows) // self.BLOCK)
-        for i in range(self.blocks_of(seq) - 1, keep - 1, -1):
-            self.free.append(int(self.table_host[seq, i]))
-            self.table_host[seq, i] = -1
-            self._dirty = True
+        """Return the blocks of ``seq`` past logical row ``rows`` to the pool."""
+        self._pool_call(_lib.lib().dflash_cache_release, int(seq), int(rows))
 
     def reserve_all(self, rows) -> None:
-        """``reserve`` for every sequence at once: back logical rows
-        [0, rows[b]) of each sequence b, taking blocks off the free list in the
-        order the per-sequence calls would (sequence 0 first)."""
-        rows = np.asarray(rows, dtype=np.int64)
-        need = -(-rows // self.BLOCK)
-        if (need > self.max_blocks).any():
-            raise ValueError(f"a sequence needs more than max_blocks {self.max_blocks} blocks")
-        have = np.count_nonzero(self.table_host >= 0, axis=1)
-        new = np.maximum(need - have, 0)
-        total = int(new.sum())
-        if total == 0:
-            return
-        if total > len(self.free):
-            raise MemoryError("no free cache block")
-        taken = np.asarray(self.free[-total:][::-1], dtype=np.int32)
-        del self.free[-total:]
-        seq = np.repeat(np.arange(self.batch), new)
-        first = np.repeat(np.cumsum(new) - new, new)
-        self.table_host[seq, have[seq] + np.arange(total) - first] = taken
-        self._dirty = True
+        """``reserve`` for every sequence at once (sequence 0 first)."""
+        arr = np.ascontiguousarray(rows, dtype=np.int64)
+        if arr.shape != (self.batch,):
+            raise ValueError("one row count per sequence")
+        self._pool_call(_lib.lib().dflash_cache_reserve_all, arr.ctypes.data_as(C.POINTER(C.c_int64)))
 
     def release_all(self, rows) -> None:
         """``release`` for every sequence at once (blocks past logical row
-        rows[b] go back to the free list in the per-sequence calls' order)."""
-        keep = -(-np.asarray(rows, dtype=np.int64) // self.BLOCK)
-        cols = np.arange(self.max_blocks)
-        drop = (cols[None, :] >= keep[:, None]) & (self.table_host >= 0)
-        if not drop.any():
-            return
-        # sequence by sequence, last block first
-        self.free.extend(self.table_host[:, ::-1][drop[:, ::-1]].tolist())
-        self.table_host[drop] = -1
-        self._dirty = True
+        rows[b] go back sequence by sequence, last block first)."""
+        arr = np.ascontiguousarray(rows, dtype=np.int64)
+        if arr.shape != (self.batch,):
+            raise ValueError("one row count per sequence")
+        self._pool_call(_lib.lib().dflash_cache_release_all, arr.ctypes.data_as(C.POINTER(C.c_int64)))
 
     def crop_all(self, new_lengths) -> None:
         """Crop every sequence at once (all checked before any changes) and
@@ -750,17 +720,18 @@ class PagedKVCache:
         self.release_all(arr)
 
     def sync(self, stream=None) -> None:
-        """Copy the host table to the device table, asynchronously and
-        stream-ordered before the steps enqueued after it (a pinned staging
-        copy of the table is taken now, so the host table may change at once)."""
-        if self._dirty:
-            if self.table.device.type != "cuda":  # a host-resident cache (block accounting only)
-                self.table.copy_(torch.from_numpy(self.table_host))
-            else:
-                if self._uploads is None:
-                    self._uploads = _PinnedUploads(self.table_host.size)
-                self._uploads.upload(self.table_host, self.table, stream)
-            self._dirty = False
+        """Write the table entries the pool changed to the device table, ordered
+        on the stream before the steps enqueued after it (small patch kernels;
+        the host table may change again at once)."""
+        if int(_lib.lib().dflash_block_pool_pending(self._pool)) == 0:
+            return
+        if self.table.device.type != "cuda":  # a host-resident cache (block accounting only)
+            self.table.copy_(torch.from_numpy(self.table_host))
+            check(_lib.lib().dflash_block_pool_drop_pending(self._pool), "dflash_block_pool_drop_pending")
+            return
+        with torch.cuda.device(self.table.device):
+            check(_lib.lib().dflash_cache_push_table(C.byref(self.desc), self._pool, _stream_handle(stream)),
+                  "dflash_cache_push_table")
 
     # ------------------------------------------------------------ rows
     def _slots(self, seq: int, r0: int, r1: int):
@@ -801,30 +772,20 @@ class PagedKVCache:
 def run_round(model, cache, hidden_states: torch.Tensor, target_hidden: Optional[torch.Tensor], ctx_offsets,
               accept: Sequence[int], out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """One draft round on a paged (or contiguous) cache: reserve the blocks the
-    step appends to, run the layer (or decoder) step with positions len_b ..
-    len_b + n_b + bs - 1, then crop each sequence to its accepted prefix
-    len_b + n_b + accept[b] (releasing the blocks a crop drops)."""
+    step appends to and push the table entries that changed, run the layer (or
+    decoder) step at the contiguous positions len_b .. len_b + n_b + bs - 1
+    (computed by the kernels), then crop each sequence to its accepted prefix
+    len_b + n_b + accept[b], releasing the blocks a crop drops."""
     B, bs = cache.batch, model.shape.block_size
-    L = cache.lengths.astype(np.int64).copy()
+    L = cache.lengths.astype(np.int64)
     n = np.diff(np.asarray(ctx_offsets, dtype=np.int64))
     acc = np.asarray(accept, dtype=np.int64)
     if acc.shape != (B,) or (acc < 0).any() or (acc > bs).any():
         raise ValueError("accepted counts: one per sequence, each in [0, block_size]")
+    keep = L + n + acc
     if isinstance(cache, PagedKVCache):
         cache.reserve_all(L + n + bs)
         cache.sync(stream)
-    cnt = n + bs  # positions L_b .. L_b + n_b + bs - 1 of every sequence
-    pos = (np.repeat(L, cnt) + np.arange(int(cnt.sum())) - np.repeat(np.cumsum(cnt) - cnt, cnt)).astype(np.int32)
-    # positions go up through a pinned ring kept on the cache, so the round
-    # never waits for the device
-    ring = getattr(cache, "_pos_uploads", None)
-    if ring is None or ring.capacity < pos.size:
-        ring = _PinnedUploads(max(pos.size, 4096))
-        cache._pos_uploads = ring
-    pos_d = torch.empty(pos.size, dtype=torch.int32, device=hidden_states.device)
-    if stream is not None:
-        pos_d.record_stream(stream)
-    ring.upload(pos, pos_d, stream)
-    out = model.step(hidden_states, target_hidden, ctx_offsets, pos_d, cache, out=out, stream=stream)
-    cache.crop_all(L + n + acc)
+    out = model.step(hidden_states, target_hidden, ctx_offsets, None, cache, out=out, stream=stream)
+    cache.crop_all(keep)
     return out

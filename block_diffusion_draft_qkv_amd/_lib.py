@@ -41,6 +41,10 @@ EXPORTS = (
     "dflash_decoder_create", "dflash_decoder_destroy", "dflash_decoder_attention",
     "dflash_decoder_workspace_bytes", "dflash_decoder_step", "dflash_rms_norm",
     "dflash_workspace_offset", "dflash_decoder_workspace_offset", "dflash_ctxkv_workspace_offset",
+    "dflash_block_pool_create", "dflash_block_pool_destroy", "dflash_block_pool_free_count",
+    "dflash_block_pool_get_free", "dflash_block_pool_set_free", "dflash_cache_reserve", "dflash_cache_reserve_all",
+    "dflash_cache_release", "dflash_cache_release_all", "dflash_cache_push_table", "dflash_block_pool_pending",
+    "dflash_block_pool_drop_pending",
 )
 CTX_WS_REGIONS = {"normed": 0, "normed_mx_scales": 1}
 WS_REGIONS = {"attn_out": 0, "attn_out_mx": 1, "attn_out_mx_scales": 2}
@@ -153,6 +157,28 @@ def lib() -> C.CDLL:
         h.dflash_ctxkv_combine_workspace_bytes.restype = C.c_size_t
         h.dflash_cache_crop_all.argtypes = [C.POINTER(KVCacheDesc), C.POINTER(C.c_int32)]
         h.dflash_cache_crop_all.restype = C.c_int
+        h.dflash_block_pool_create.argtypes = [C.c_int32, C.POINTER(C.c_void_p)]
+        h.dflash_block_pool_create.restype = C.c_int
+        h.dflash_block_pool_destroy.argtypes = [C.c_void_p]
+        h.dflash_block_pool_destroy.restype = None
+        h.dflash_block_pool_free_count.argtypes = [C.c_void_p]
+        h.dflash_block_pool_free_count.restype = C.c_int32
+        h.dflash_block_pool_get_free.argtypes = [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]
+        h.dflash_block_pool_get_free.restype = C.c_int
+        h.dflash_block_pool_set_free.argtypes = [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]
+        h.dflash_block_pool_set_free.restype = C.c_int
+        for name in ("dflash_cache_reserve", "dflash_cache_release"):
+            getattr(h, name).argtypes = [C.POINTER(KVCacheDesc), C.c_void_p, C.c_int32, C.c_int64]
+            getattr(h, name).restype = C.c_int
+        for name in ("dflash_cache_reserve_all", "dflash_cache_release_all"):
+            getattr(h, name).argtypes = [C.POINTER(KVCacheDesc), C.c_void_p, C.POINTER(C.c_int64)]
+            getattr(h, name).restype = C.c_int
+        h.dflash_cache_push_table.argtypes = [C.POINTER(KVCacheDesc), C.c_void_p, C.c_void_p]
+        h.dflash_cache_push_table.restype = C.c_int
+        h.dflash_block_pool_pending.argtypes = [C.c_void_p]
+        h.dflash_block_pool_pending.restype = C.c_int32
+        h.dflash_block_pool_drop_pending.argtypes = [C.c_void_p]
+        h.dflash_block_pool_drop_pending.restype = C.c_int
         h.dflash_ctxkv_destroy.argtypes = [C.c_void_p]
         h.dflash_ctxkv_destroy.restype = None
         h.dflash_ctxkv_workspace_bytes.argtypes = [C.c_void_p, C.c_int64]

@@ -394,6 +394,77 @@ void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s, in
 
 }  // namespace
 
+// A paged cache's free physical blocks (a stack: the last entry is taken
+// next) and the table entries changed since the last upload.
+struct dflash_block_pool {
+  int32_t num_blocks = 0;
+  std::vector<int32_t> free;
+  std::vector<std::pair<int32_t, int32_t>> pending;  // (flat index, value)
+};
+
+namespace {
+
+bool pool_cache_ok(const dflash_kv_cache* c, const dflash_block_pool* p) {
+  return c && p && c->block_table && c->block_table_host && c->batch >= 1 && c->max_blocks > 0 &&
+         c->num_blocks == p->num_blocks;
+}
+
+// Table entries in use by sequence b (the non-negative ones).
+int32_t blocks_in_use(const dflash_kv_cache* c, int b) {
+  const int32_t* row = c->block_table_host + (int64_t)b * c->max_blocks;
+  int32_t n = 0;
+  for (int32_t i = 0; i < c->max_blocks; ++i) n += row[i] >= 0;
+  return n;
+}
+
+void set_entry(dflash_kv_cache* c, dflash_block_pool* p, int64_t idx, int32_t v) {
+  const_cast<int32_t*>(c->block_table_host)[idx] = v;
+  p->pending.push_back({(int32_t)idx, v});
+}
+
+// Back rows [0, rows[b]) of every sequence b with rows[b] >= 0 by blocks:
+// sequence by sequence (0 first), each new logical block taking the pool's
+// next block. All or nothing: DFLASH_ERR_SHAPE past max_blocks,
+// DFLASH_ERR_CAPACITY when the pool holds too few.
+int reserve_rows(dflash_kv_cache* c, dflash_block_pool* p, const int64_t* rows) {
+  int64_t total = 0;
+  for (int b = 0; b < c->batch; ++b) {
+    if (rows[b] < 0) continue;
+    const int64_t need = (rows[b] + kKeyTile - 1) / kKeyTile;
+    if (need > c->max_blocks) return DFLASH_ERR_SHAPE;
+    total += std::max<int64_t>(0, need - blocks_in_use(c, b));
+  }
+  if (total > (int64_t)p->free.size()) return DFLASH_ERR_CAPACITY;
+  for (int b = 0; b < c->batch; ++b) {
+    if (rows[b] < 0) continue;
+    const int64_t need = (rows[b] + kKeyTile - 1) / kKeyTile;
+    for (int64_t i = blocks_in_use(c, b); i < need; ++i) {
+      set_entry(c, p, (int64_t)b * c->max_blocks + i, p->free.back());
+      p->free.pop_back();
+    }
+  }
+  return DFLASH_OK;
+}
+
+// Return the blocks of every sequence b with rows[b] >= 0 past its first
+// ceil(rows[b] / 64) to the pool: sequence by sequence, last block first.
+int release_rows(dflash_kv_cache* c, dflash_block_pool* p, const int64_t* rows) {
+  for (int b = 0; b < c->batch; ++b) {
+    if (rows[b] < 0) continue;
+    const int64_t keep = (rows[b] + kKeyTile - 1) / kKeyTile;
+    for (int64_t i = c->max_blocks - 1; i >= keep; --i) {
+      const int64_t idx = (int64_t)b * c->max_blocks + i;
+      const int32_t blk = c->block_table_host[idx];
+      if (blk < 0) continue;
+      p->free.push_back(blk);
+      set_entry(c, p, idx, -1);
+    }
+  }
+  return DFLASH_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* dflash_status_string(int status) {
@@ -522,7 +593,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
                           const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
                           void* out, void* workspace, size_t workspace_bytes, void* stream,
                           bool validate_only, bool noalloc = false) {
-  if (!L || !hidden_states || !ctx_offsets || !positions || !cache || !out) return DFLASH_ERR_ARG;
+  if (!L || !hidden_states || !ctx_offsets || !cache || !out) return DFLASH_ERR_ARG;
   if (!cache->k || !cache->v || !cache->len) return DFLASH_ERR_ARG;
   const dflash_config& c = L->cfg;
   const int B = cache->batch;
@@ -554,6 +625,12 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     n_tiles += (int64_t)nkv * tile_cnt[b];
   }
   seq.ctx_off[B] = ctx_offsets[B];
+  // Without a position array every window takes len_b, len_b + 1, ...: all
+  // of them must lie inside the RoPE table.
+  if (!positions)
+    for (int b = 0; b < B; ++b)
+      if ((int64_t)cache->len[b] + (ctx_offsets[b + 1] - ctx_offsets[b]) + bs > c.max_position)
+        return DFLASH_ERR_RANGE;
   const int64_t Mc = ctx_offsets[B];
   if (Mc > 0 && !target_hidden) return DFLASH_ERR_ARG;
   {
@@ -813,6 +890,108 @@ int dflash_cache_crop_all(dflash_kv_cache* cache, const int32_t* new_len) {
   return DFLASH_OK;
 }
 
+// ------------------------------------------------------------ block pool
+
+int dflash_block_pool_create(int32_t num_blocks, dflash_block_pool** out) {
+  if (!out) return DFLASH_ERR_ARG;
+  *out = nullptr;
+  if (num_blocks <= 0) return DFLASH_ERR_SHAPE;
+  dflash_block_pool* p = new (std::nothrow) dflash_block_pool();
+  if (!p) return DFLASH_ERR_HIP;
+  p->num_blocks = num_blocks;
+  p->free.resize(num_blocks);
+  for (int32_t i = 0; i < num_blocks; ++i) p->free[i] = num_blocks - 1 - i;  // block 0 is taken first
+  *out = p;
+  return DFLASH_OK;
+}
+
+void dflash_block_pool_destroy(dflash_block_pool* p) { delete p; }
+
+int32_t dflash_block_pool_free_count(const dflash_block_pool* p) { return p ? (int32_t)p->free.size() : -1; }
+
+int dflash_block_pool_get_free(const dflash_block_pool* p, int32_t* blocks, int32_t capacity) {
+  if (!p || (!blocks && !p->free.empty())) return DFLASH_ERR_ARG;
+  if (capacity < (int32_t)p->free.size()) return DFLASH_ERR_SHAPE;
+  std::copy(p->free.begin(), p->free.end(), blocks);
+  return DFLASH_OK;
+}
+
+int dflash_block_pool_set_free(dflash_block_pool* p, const int32_t* blocks, int32_t n) {
+  if (!p || n < 0 || (n > 0 && !blocks)) return DFLASH_ERR_ARG;
+  if (n > p->num_blocks) return DFLASH_ERR_SHAPE;
+  std::vector<char> seen(p->num_blocks, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (blocks[i] < 0 || blocks[i] >= p->num_blocks || seen[blocks[i]]) return DFLASH_ERR_RANGE;
+    seen[blocks[i]] = 1;
+  }
+  p->free.assign(blocks, blocks + n);
+  return DFLASH_OK;
+}
+
+int dflash_cache_reserve(dflash_kv_cache* c, dflash_block_pool* p, int32_t seq, int64_t rows) {
+  if (!pool_cache_ok(c, p) || seq < 0 || seq >= c->batch) return DFLASH_ERR_ARG;
+  std::vector<int64_t> all(c->batch, -1);
+  all[seq] = rows;
+  return reserve_rows(c, p, all.data());
+}
+
+int dflash_cache_reserve_all(dflash_kv_cache* c, dflash_block_pool* p, const int64_t* rows) {
+  if (!pool_cache_ok(c, p) || !rows) return DFLASH_ERR_ARG;
+  return reserve_rows(c, p, rows);
+}
+
+int dflash_cache_release(dflash_kv_cache* c, dflash_block_pool* p, int32_t seq, int64_t rows) {
+  if (!pool_cache_ok(c, p) || seq < 0 || seq >= c->batch) return DFLASH_ERR_ARG;
+  std::vector<int64_t> all(c->batch, -1);
+  all[seq] = rows;
+  return release_rows(c, p, all.data());
+}
+
+int dflash_cache_release_all(dflash_kv_cache* c, dflash_block_pool* p, const int64_t* rows) {
+  if (!pool_cache_ok(c, p) || !rows) return DFLASH_ERR_ARG;
+  return release_rows(c, p, rows);
+}
+
+int dflash_cache_push_table(dflash_kv_cache* c, dflash_block_pool* p, void* stream) {
+  if (!pool_cache_ok(c, p)) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* table = const_cast<int32_t*>(c->block_table);
+  // One entry per index, its latest value: a patch kernel writes its entries
+  // concurrently, so an index released and taken again since the last push
+  // (two pending values) must go up once.
+  const size_t n_entries = (size_t)c->batch * c->max_blocks;
+  std::vector<char> seen(n_entries, 0);
+  std::vector<std::pair<int32_t, int32_t>> latest;
+  latest.reserve(p->pending.size());
+  for (size_t k = p->pending.size(); k-- > 0;) {
+    const auto& e = p->pending[k];
+    if (e.first < 0 || (size_t)e.first >= n_entries) return DFLASH_ERR_ARG;
+    if (seen[e.first]) continue;
+    seen[e.first] = 1;
+    latest.push_back(e);
+  }
+  size_t i = 0;
+  while (i < latest.size()) {
+    TablePatch patch;
+    int n = 0;
+    for (; n < kTablePatch && i < latest.size(); ++n, ++i) {
+      patch.idx[n] = latest[i].first;
+      patch.val[n] = latest[i].second;
+    }
+    if (launch_table_patch(table, patch, n, s) != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  p->pending.clear();
+  return DFLASH_OK;
+}
+
+int32_t dflash_block_pool_pending(const dflash_block_pool* p) { return p ? (int32_t)p->pending.size() : -1; }
+
+int dflash_block_pool_drop_pending(dflash_block_pool* p) {
+  if (!p) return DFLASH_ERR_ARG;
+  p->pending.clear();
+  return DFLASH_OK;
+}
+
 int dflash_layer_poll_error(dflash_layer* L, void* stream) {
   if (!L) return DFLASH_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1061,8 +1240,11 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
       if (lst != DFLASH_OK) return lst;
     }
   }
+  if (!positions)
+    for (int b = 0; b < B; ++b)
+      if ((int64_t)c0->len[b] + (ctx_offsets[b + 1] - ctx_offsets[b]) > c.max_position) return DFLASH_ERR_RANGE;
   if (Mc == 0) return DFLASH_OK;
-  if (!context_states || !positions || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
+  if (!context_states || reinterpret_cast<uintptr_t>(context_states) % 16) return DFLASH_ERR_ARG;
   if (!workspace) return DFLASH_ERR_WORKSPACE;
   if (h->mx && h->append_mode == DFLASH_APPEND_SEPARATE) return DFLASH_ERR_UNSUPPORTED;
   const CtxCarve wc = ctx_carve(c, Mc, h->mx);

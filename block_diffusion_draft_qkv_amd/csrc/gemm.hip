@@ -623,7 +623,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_append_kernel(GemmArgs a
       for (int u = 0; u < MH; ++u) {
         // row block wn * MH + u, selected without indexing by a runtime value
         const int pi = wn == 0 ? pb[u] + win[u] : pb[MH + u] + win[MH + u];
-        pos[u] = a.positions[pi];
+        // no position array: contiguous positions, the row's cache row
+        pos[u] = a.positions ? a.positions[pi] : (wn == 0 ? crow[u] : crow[MH + u]);
       }
     }
     // The cache block of each row (a paged cache's from its table, loaded with the positions).

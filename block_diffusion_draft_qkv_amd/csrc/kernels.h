@@ -99,7 +99,7 @@ struct NormRopeArgs {
   const float* ctxkv;      // [kslices][sum n_b][2 nkv d] context projections (fp32)
   int64_t qkv_slice, ctx_slice;  // elements between k slices (summed on read)
   int32_t kslices;
-  const int32_t* positions;
+  const int32_t* positions;  // NULL: contiguous, len_b + (row in the window)
   const float* cos_sin;    // cos [max_pos][d/2] then sin [max_pos][d/2]
   const void* q_norm;
   const void* k_norm;
@@ -166,6 +166,15 @@ hipError_t launch_gemm_append_mx(int head_dim, const GemmArgs& args, const NormR
 // [h / 128][step_rows][4] when step_rows > 0 (step_rows >= rows).
 hipError_t launch_rms_rows_mx(const void* x, const void* g, uint8_t* codes, uint8_t* scales, int rows, int h,
                               float eps, int step_rows, hipStream_t stream);
+// table[idx[i]] = val[i] for i < count (count <= kTablePatch): the entries of a
+// paged cache's block table that its block pool changed since the last upload.
+constexpr int kTablePatch = 448;
+struct TablePatch {
+  int32_t idx[kTablePatch];
+  int32_t val[kTablePatch];
+};
+hipError_t launch_table_patch(int32_t* table, const TablePatch& patch, int count, hipStream_t stream);
+
 // out[i] = sum_s in[s * slice_stride + i] (+ residual[i] when given, in the
 // dtype) rounded to the dtype (0 fp32, 1 bf16) for i < n (n % 4 == 0, 16-byte
 // aligned buffers).

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
     int p[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-      p[s] = a.positions[pidx[s]];
+      // no position array: contiguous positions from the cached length
+      p[s] = a.positions ? a.positions[pidx[s]] : L + (pidx[s] - pos_off);
       if (p[s] < 0 || p[s] >= a.max_pos) {
         if (kind[s] != 0 && t == 0) atomicOr(a.err, 1);
         p[s] = p[s] < 0 ? 0 : a.max_pos - 1;

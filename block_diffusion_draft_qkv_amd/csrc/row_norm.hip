@@ -229,6 +229,11 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
   for (int r = 0; r < 4; ++r) out[4 * i + r] = Elem<T>::from_f32(acc[r]);
 }
 
+__global__ __launch_bounds__(512) void table_patch_kernel(int32_t* __restrict__ table, TablePatch p, int count) {
+  const int i = threadIdx.x;
+  if (i < count) table[p.idx[i]] = p.val[i];
+}
+
 // Two row sets quantised (no norm) in one launch, each with step-major scale
 // planes of its own rows: a layer step's draft block and new context rows.
 __global__ __launch_bounds__(256) void rows_mx2_kernel(const __bf16* __restrict__ x1, uint8_t* __restrict__ c1,
@@ -271,6 +276,12 @@ hipError_t launch_sum_slices(int dtype, const float* in, int slices, int64_t sli
   else
     hipLaunchKernelGGL(sum_slices_kernel<float>, grid, block, 0, stream, in, slices, slice_stride,
                        static_cast<const float*>(residual), static_cast<float*>(out), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_patch(int32_t* table, const TablePatch& patch, int count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_patch_kernel, dim3(1), dim3(512), 0, stream, table, patch, count);
   return hipGetLastError();
 }
 

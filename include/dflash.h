@@ -226,6 +226,11 @@ int dflash_workspace_offset(const dflash_layer* layer, int32_t batch, int64_t to
  *                  position, queries at the block's positions (the window's
  *                  suffix). Values outside [0, max_position) are clamped and
  *                  latch DFLASH_ERR_RANGE for dflash_layer_poll_error.
+ *                  NULL: the contiguous positions len_b, len_b + 1, ...,
+ *                  len_b + n_b + bs - 1 of every window (a draft that
+ *                  continues its sequence), computed by the kernels; a window
+ *                  reaching past max_position is then refused with
+ *                  DFLASH_ERR_RANGE before anything is enqueued.
  *   cache          rows [len_b, len_b + n_b + bs) of each sequence receive the
  *                  new context rows then the block rows; len_b then becomes
  *                  T_b = len_b + n_b + bs. Nothing else in the cache is
@@ -286,6 +291,63 @@ int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len);
  * Errors: DFLASH_ERR_ARG (null pointer), DFLASH_ERR_RANGE (an entry outside
  * [0, len[b]]). */
 int dflash_cache_crop_all(dflash_kv_cache* cache, const int32_t* new_len);
+
+/* ------------------------------------------------------------------------
+ * Block pool of a paged cache: the host-side allocator behind the block table
+ * (the vLLM page "qwen3_dflash" leaves block management to vLLM's cache
+ * manager; this is the draft's own, so that a draft round needs no host work
+ * outside the library). A pool owns the free physical blocks of one cache's
+ * pools (or of a stack of caches that share one table) as a stack whose last
+ * entry is taken next, and records every table entry it changes until they
+ * are pushed to the device table. The table entries themselves live in the
+ * cache descriptor's host mirror (block_table_host), which the calls below
+ * write; they require a paged cache whose num_blocks equals the pool's.
+ * ------------------------------------------------------------------------ */
+typedef struct dflash_block_pool dflash_block_pool; /* opaque */
+
+/* A pool of blocks 0 .. num_blocks - 1, all free, block 0 taken first.
+ * Errors: DFLASH_ERR_ARG (null out), DFLASH_ERR_SHAPE (num_blocks <= 0). */
+int dflash_block_pool_create(int32_t num_blocks, dflash_block_pool** out);
+void dflash_block_pool_destroy(dflash_block_pool* pool);  /* NULL is a no-op */
+/* Free blocks (-1 for a NULL pool). */
+int32_t dflash_block_pool_free_count(const dflash_block_pool* pool);
+/* Copy the free stack (bottom first; the last entry is taken next) into
+ * blocks[capacity]. Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE (too small). */
+int dflash_block_pool_get_free(const dflash_block_pool* pool, int32_t* blocks, int32_t capacity);
+/* Replace the free stack by blocks[0 .. n-1] (distinct, in [0, num_blocks)),
+ * e.g. a shuffled order. Errors: DFLASH_ERR_ARG, DFLASH_ERR_SHAPE (n too
+ * large), DFLASH_ERR_RANGE (an entry out of range or repeated; nothing
+ * changed). */
+int dflash_block_pool_set_free(dflash_block_pool* pool, const int32_t* blocks, int32_t n);
+
+/* Back rows [0, rows) of sequence `seq` (reserve) or of every sequence b with
+ * rows[b] >= 0 (reserve_all; b ascending) with blocks: each logical block
+ * past the sequence's blocks in use (its non-negative table entries) takes
+ * the pool's next block. All or nothing: DFLASH_ERR_SHAPE when a sequence
+ * would need more than max_blocks, DFLASH_ERR_CAPACITY when the pool holds too
+ * few free blocks; DFLASH_ERR_ARG for a null or unpaged cache, a pool of
+ * another size or a bad seq. Host-only. */
+int dflash_cache_reserve(dflash_kv_cache* cache, dflash_block_pool* pool, int32_t seq, int64_t rows);
+int dflash_cache_reserve_all(dflash_kv_cache* cache, dflash_block_pool* pool, const int64_t* rows);
+
+/* Return to the pool every block of sequence `seq` (release) or of every
+ * sequence b with rows[b] >= 0 (release_all) past the first ceil(rows / 64)
+ * logical blocks (a crop's dropped blocks): sequence by sequence, last block
+ * first; their entries become -1. The lengths are not changed (see
+ * dflash_cache_crop / _crop_all). Errors: as for reserve. Host-only. */
+int dflash_cache_release(dflash_kv_cache* cache, dflash_block_pool* pool, int32_t seq, int64_t rows);
+int dflash_cache_release_all(dflash_kv_cache* cache, dflash_block_pool* pool, const int64_t* rows);
+
+/* Write the table entries the pool changed since the last push into the
+ * cache's device table (each index once, with its latest value): small patch
+ * kernels on `stream` (448 entries each), so that steps enqueued after it see
+ * them; then forget them. The device
+ * table must be device memory. Errors: DFLASH_ERR_ARG, DFLASH_ERR_HIP. */
+int dflash_cache_push_table(dflash_kv_cache* cache, dflash_block_pool* pool, void* stream);
+/* Table entries changed since the last push (-1 for a NULL pool), and a way
+ * to forget them (after the caller copied the whole table itself). */
+int32_t dflash_block_pool_pending(const dflash_block_pool* pool);
+int dflash_block_pool_drop_pending(dflash_block_pool* pool);
 
 /* Synchronise `stream`, then return and clear the layer's sticky device-side
  * error (DFLASH_ERR_RANGE if a position fell outside the table since the last
@@ -468,7 +530,9 @@ int dflash_ctxkv_workspace_offset(const dflash_ctxkv* h, int64_t total_ctx, int3
  *   positions       device int32 [sum n_b]: the position of every context row
  *                   (normally len_b, len_b + 1, ...); each must lie in
  *                   [0, max_position): a violation is clamped and latched as
- *                   for a layer step (dflash_ctxkv_poll_error).
+ *                   for a layer step (dflash_ctxkv_poll_error). NULL: those
+ *                   contiguous positions, computed by the kernels (rows past
+ *                   max_position refused with DFLASH_ERR_RANGE up front).
  *   caches          HOST array of L cache descriptors, one per layer, with the
  *                   same batch, capacity and lengths; all contiguous or all
  *                   paged. Paged layers may share one block table or each

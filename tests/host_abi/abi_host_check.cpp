@@ -705,6 +705,138 @@ void test_decoder() {
   CHECK(stub_live_allocations() == live + 4, "decoder left allocations");
 }
 
+// The block pool against a plain model of the same rules (a free stack,
+// sequence-major reserve, last-block-first release), over random operations.
+void test_block_pool() {
+  const size_t live = stub_live_allocations();
+  Rng rng(99);
+  const int B = 7, per = 9, nb = 40;
+  Cache cache(B, 1, 64, 2, per * 64, true, 0, &rng);  // pools of B * per blocks; the pool hands out nb < that
+  cache.c.num_blocks = nb;
+  std::fill(cache.table.begin(), cache.table.end(), -1);
+  dflash_block_pool* pool = nullptr;
+  CHECK(dflash_block_pool_create(0, &pool) == DFLASH_ERR_SHAPE && !pool, "pool of 0 blocks");
+  CHECK(dflash_block_pool_create(nb, &pool) == DFLASH_OK && pool, "pool create");
+  CHECK(dflash_block_pool_free_count(pool) == nb, "all free");
+  std::vector<int32_t> order(nb);
+  for (int i = 0; i < nb; ++i) order[i] = i;
+  for (int i = nb - 1; i > 0; --i) std::swap(order[i], order[rng.range(0, i)]);
+  std::vector<int32_t> bad = order;
+  bad[3] = bad[4];
+  CHECK(dflash_block_pool_set_free(pool, bad.data(), nb) == DFLASH_ERR_RANGE, "repeated block");
+  CHECK(dflash_block_pool_set_free(pool, order.data(), nb) == DFLASH_OK, "set free");
+  std::vector<int32_t> model_free = order, model_table(B * per, -1);
+  auto in_use = [&](int b) {
+    int n = 0;
+    for (int i = 0; i < per; ++i) n += model_table[b * per + i] >= 0;
+    return n;
+  };
+  for (int op = 0; op < 3000; ++op) {
+    const int kind = rng.range(0, 3);
+    std::vector<int64_t> rows(B, -1);
+    if (kind == 0 || kind == 2) {
+      const int b = rng.range(0, B - 1);
+      rows[b] = rng.range(0, per * 64 + 70);
+    } else {
+      for (int b = 0; b < B; ++b) rows[b] = rng.range(0, 2) ? rng.range(0, per * 64 + 10) : -1;
+    }
+    const bool reserve = kind < 2;
+    // the model
+    int expect = DFLASH_OK;
+    if (reserve) {
+      int64_t total = 0;
+      for (int b = 0; b < B; ++b)
+        if (rows[b] >= 0) {
+          const int64_t need = (rows[b] + 63) / 64;
+          if (need > per) expect = DFLASH_ERR_SHAPE;
+          total += std::max<int64_t>(0, need - in_use(b));
+        }
+      if (expect == DFLASH_OK && total > (int64_t)model_free.size()) expect = DFLASH_ERR_CAPACITY;
+      if (expect == DFLASH_OK)
+        for (int b = 0; b < B; ++b)
+          if (rows[b] >= 0)
+            for (int64_t i = in_use(b); i < (rows[b] + 63) / 64; ++i) {
+              model_table[b * per + i] = model_free.back();
+              model_free.pop_back();
+            }
+    } else {
+      for (int b = 0; b < B; ++b)
+        if (rows[b] >= 0)
+          for (int64_t i = per - 1; i >= (rows[b] + 63) / 64; --i)
+            if (model_table[b * per + i] >= 0) {
+              model_free.push_back(model_table[b * per + i]);
+              model_table[b * per + i] = -1;
+            }
+    }
+    int st;
+    int seq = 0;
+    for (int b = 0; b < B; ++b)
+      if (rows[b] >= 0) seq = b;
+    if (kind == 0) st = dflash_cache_reserve(&cache.c, pool, seq, rows[seq]);
+    else if (kind == 1) st = dflash_cache_reserve_all(&cache.c, pool, rows.data());
+    else if (kind == 2) st = dflash_cache_release(&cache.c, pool, seq, rows[seq]);
+    else st = dflash_cache_release_all(&cache.c, pool, rows.data());
+    CHECK(st == expect, "pool op %d kind %d: status %d, expected %d", op, kind, st, expect);
+    CHECK(cache.table == model_table, "pool op %d: table differs from the model", op);
+    std::vector<int32_t> got(nb);
+    const int32_t nfree = dflash_block_pool_free_count(pool);
+    CHECK(nfree == (int32_t)model_free.size() &&
+              dflash_block_pool_get_free(pool, got.data(), nb) == DFLASH_OK &&
+              std::equal(model_free.begin(), model_free.end(), got.begin()),
+          "pool op %d: free stack differs from the model", op);
+    if (rng.range(0, 9) == 0) {
+      stub_clear_launches();
+      const int32_t pending = dflash_block_pool_pending(pool);
+      CHECK(dflash_cache_push_table(&cache.c, pool, nullptr) == DFLASH_OK, "push table");
+      CHECK((int)stub_launch_count() <= (pending + 447) / 448, "push launches %zu for %d entries",
+            stub_launch_count(), pending);
+      CHECK(dflash_block_pool_pending(pool) == 0, "push clears pending");
+      check_launches("push table");
+    }
+  }
+  std::vector<int32_t> small(3);
+  CHECK(dflash_block_pool_get_free(pool, small.data(), 3) == DFLASH_ERR_SHAPE || dflash_block_pool_free_count(pool) <= 3,
+        "get_free into a short buffer");
+  dflash_kv_cache flat = cache.c;
+  flat.block_table = nullptr;
+  CHECK(dflash_cache_reserve(&flat, pool, 0, 64) == DFLASH_ERR_ARG, "reserve on a contiguous cache");
+  CHECK(dflash_cache_reserve(&cache.c, pool, B, 64) == DFLASH_ERR_ARG, "reserve past the batch");
+  dflash_block_pool_destroy(pool);
+  dflash_block_pool_destroy(nullptr);
+  CHECK(stub_live_allocations() == live + 3, "pool test allocations");
+}
+
+// Steps without a position array: contiguous positions, refused up front when
+// a window would pass max_position.
+void test_contiguous_positions() {
+  Rng rng(17);
+  LayerBufs b;
+  dflash_config c = config(512, 8, 2, 128, 16, DFLASH_BF16);
+  c.max_position = 300;
+  dflash_layer* L = make_layer(c, b, false);
+  Cache cache(3, 2, 128, 2, 512, false, 0, &rng);
+  cache.len = {10, 200, 260};
+  cache.c.len = cache.len.data();
+  const std::vector<int32_t> offs = offsets({3, 5, 24});  // 260 + 24 + 16 = 300: the last position 299
+  StepIO io;
+  io.hs = dev(3 * 16 * 512 * 2);
+  io.th = dev(32 * 512 * 2);
+  io.out = dev(3 * 16 * 512 * 2);
+  io.ws_bytes = dflash_workspace_bytes(L, 3, 32, 600);
+  io.ws = dev(io.ws_bytes);
+  stub_clear_launches();
+  CHECK(dflash_attn_step(L, io.hs, io.th, offs.data(), nullptr, &cache.c, io.out, io.ws, io.ws_bytes, nullptr) ==
+            DFLASH_OK,
+        "step without positions");
+  check_launches("contiguous positions");
+  cache.len = {10, 200, 261};
+  CHECK(dflash_attn_step(L, io.hs, io.th, offs.data(), nullptr, &cache.c, io.out, io.ws, io.ws_bytes, nullptr) ==
+                DFLASH_ERR_RANGE &&
+            stub_launch_count() == 0 && cache.len[2] == 261,
+        "window past max_position refused");
+  dflash_layer_destroy(L);
+}
+
 void test_free_functions() {
   void* x = dev_zero(300 * 512 * 2);
   void* g = dev_zero(512 * 2);
@@ -740,6 +872,8 @@ int main(int argc, char** argv) {
   test_layer_steps_random(random_cases);
   test_ctxkv();
   test_decoder();
+  test_block_pool();
+  test_contiguous_positions();
   test_free_functions();
   CHECK(stub_live_allocations() == live0, "%zu device allocations left at exit", stub_live_allocations() - live0);
   std::printf("host ABI check: %d checks, %zu launches checked, %d failures\n", g_checks, g_launches_checked,

@@ -33,7 +33,9 @@ def make_paged(case, spare_blocks=8, seed=0, prefix=True, extra_blocks=2):
     cache = PagedKVCache(case.batch, cfg.n_kv_heads, cfg.head_dim, sum(need) + spare_blocks, max_blocks, dt)
     fill_canary(cache.k)
     fill_canary(cache.v)
-    np.random.default_rng(seed).shuffle(cache.free)
+    order = cache.free
+    np.random.default_rng(seed).shuffle(order)
+    cache.free = order
     if prefix:
         for b in range(case.batch):
             cache.write_prefix(b, dev(case.cache_k[b], dt), dev(case.cache_v[b], dt))
@@ -172,7 +174,9 @@ def paged_stack(case, dt, seed, tables):
         if tables == "shared" and caches:
             kv.free = list(caches[0].free_at_start)
         else:
-            rng.shuffle(kv.free)
+            order = kv.free
+            rng.shuffle(order)
+            kv.free = order
         kv.free_at_start = list(kv.free)
         for b in range(case.batch):
             kv.write_prefix(b, dev(case.cache_k[layer][b], dt), dev(case.cache_v[layer][b], dt))
