@@ -21,7 +21,8 @@ DFLASH_ERR_HIP = 6
 DFLASH_ERR_WORKSPACE = 7
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
-DFLASH_MAX_BATCH = 256
+DFLASH_MAX_BATCH = 65536
+DFLASH_LAUNCH_BATCH = 256
 DFLASH_NOALLOC_SCRATCH_BYTES = 64 << 20
 APPEND_MODES = {"auto": 0, "fused": 1, "separate": 2}
 KERNEL_NAMES = ("gemm_qkv", "norm_rope", "attn", "merge", "gemm_o", "attn_merge")

@@ -392,6 +392,24 @@ void record_end(dflash_layer* L, int kernel, hipEvent_t start, hipStream_t s, in
   L->pending.push_back({kernel, start, stop});
 }
 
+// Sequences b0 .. b0 + nb - 1 of a cache as a cache of their own: the same
+// pools (paged: the table rows of those sequences) or the contiguous layout's
+// slabs of those sequences, and their lengths.
+dflash_kv_cache cache_view(const dflash_kv_cache* c, int b0, int nb, int nkv, int d, int es) {
+  dflash_kv_cache v = *c;
+  v.batch = nb;
+  v.len = c->len + b0;
+  if (c->block_table) {
+    v.block_table = c->block_table + (size_t)b0 * c->max_blocks;
+    v.block_table_host = c->block_table_host ? c->block_table_host + (size_t)b0 * c->max_blocks : nullptr;
+  } else {
+    const size_t seq_bytes = (size_t)c->capacity * nkv * d * es;
+    v.k = static_cast<char*>(c->k) + (size_t)b0 * seq_bytes;
+    v.v = static_cast<char*>(c->v) + (size_t)b0 * seq_bytes;
+  }
+  return v;
+}
+
 }  // namespace
 
 // A paged cache's free physical blocks (a stack: the last entry is taken
@@ -564,12 +582,13 @@ int dflash_layer_create_mxfp8(const dflash_config* cfg, const dflash_mxfp8_weigh
 size_t dflash_workspace_bytes(const dflash_layer* L, int32_t batch, int64_t total_ctx,
                               int64_t total_keys) {
   if (!L || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0 || total_keys < 0) return 0;
-  return carve(L, batch, total_ctx).total;
+  // a larger batch runs in runs of at most kMaxBatch sequences sharing it
+  return carve(L, std::min<int32_t>(batch, kMaxBatch), total_ctx).total;
 }
 
 int dflash_workspace_offset(const dflash_layer* L, int32_t batch, int64_t total_ctx, int32_t region,
                             size_t* offset) {
-  if (!L || !offset || batch < 1 || batch > DFLASH_MAX_BATCH || total_ctx < 0) return DFLASH_ERR_ARG;
+  if (!L || !offset || batch < 1 || batch > kMaxBatch || total_ctx < 0) return DFLASH_ERR_ARG;
   const Carve wc = carve(L, batch, total_ctx);
   switch (region) {
     case DFLASH_WS_ATTN_OUT: *offset = wc.obuf; return DFLASH_OK;
@@ -597,7 +616,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   if (!cache->k || !cache->v || !cache->len) return DFLASH_ERR_ARG;
   const dflash_config& c = L->cfg;
   const int B = cache->batch;
-  if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
+  if (B < 1 || B > kMaxBatch) return DFLASH_ERR_ARG;
   if (cache->capacity <= 0 || cache->capacity % kKeyTile) return DFLASH_ERR_SHAPE;
   if (cache->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
   if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
@@ -861,18 +880,54 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   return DFLASH_OK;
 }
 
+static_assert(kMaxBatch == DFLASH_LAUNCH_BATCH, "one launch plans for DFLASH_LAUNCH_BATCH sequences");
+
+// A step of more sequences than one launch plans for (kMaxBatch): the
+// sequences are independent, so it runs as consecutive steps over runs of at
+// most kMaxBatch of them, each on a view of the cache and of the step's rows
+// sharing the workspace, after every run has passed the host-side checks.
+static int attn_step_any(dflash_layer* L, const void* hidden_states, const void* target_hidden,
+                         const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream, bool validate_only,
+                         bool noalloc = false) {
+  if (!L || !cache || !ctx_offsets) return DFLASH_ERR_ARG;
+  const int B = cache->batch;
+  if (B <= kMaxBatch)
+    return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, workspace,
+                          workspace_bytes, stream, validate_only, noalloc);
+  if (B > DFLASH_MAX_BATCH || !hidden_states || !out || !cache->len) return DFLASH_ERR_ARG;
+  if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
+  const dflash_config& c = L->cfg;
+  const size_t row_bytes = (size_t)c.hidden * elem_size(c);
+  for (int pass = 0; pass < (validate_only ? 1 : 2); ++pass)
+    for (int b0 = 0; b0 < B; b0 += kMaxBatch) {
+      const int nb = std::min(kMaxBatch, B - b0);
+      int32_t offs[kMaxBatch + 1];
+      for (int i = 0; i <= nb; ++i) offs[i] = ctx_offsets[b0 + i] - ctx_offsets[b0];
+      dflash_kv_cache view = cache_view(cache, b0, nb, c.n_kv_heads, c.head_dim, elem_size(c));
+      const size_t row0 = (size_t)b0 * c.block_size;
+      const int st = attn_step_impl(
+          L, static_cast<const char*>(hidden_states) + row0 * row_bytes,
+          target_hidden ? static_cast<const char*>(target_hidden) + (size_t)ctx_offsets[b0] * row_bytes : nullptr,
+          offs, positions ? positions + ctx_offsets[b0] + row0 : nullptr, &view,
+          static_cast<char*>(out) + row0 * row_bytes, workspace, workspace_bytes, stream, pass == 0, noalloc);
+      if (st != DFLASH_OK) return st;
+    }
+  return DFLASH_OK;
+}
+
 int dflash_attn_step(dflash_layer* L, const void* hidden_states, const void* target_hidden,
                      const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, workspace,
-                        workspace_bytes, stream, false);
+  return attn_step_any(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, workspace,
+                       workspace_bytes, stream, false);
 }
 
 int dflash_attn_step_noalloc(dflash_layer* L, const void* hidden_states, const void* target_hidden,
                              const int32_t* ctx_offsets, const int32_t* positions, dflash_kv_cache* cache,
                              void* out, void* stream) {
-  return attn_step_impl(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, nullptr, 0, stream,
-                        false, true);
+  return attn_step_any(L, hidden_states, target_hidden, ctx_offsets, positions, cache, out, nullptr, 0, stream,
+                       false, true);
 }
 
 int dflash_cache_crop(dflash_kv_cache* cache, int32_t seq, int32_t new_len) {
@@ -1198,9 +1253,13 @@ int dflash_ctxkv_workspace_offset(const dflash_ctxkv* h, int64_t total_ctx, int3
   }
 }
 
-int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
-                        const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// The precompute for at most kMaxBatch sequences; with validate_only it
+// returns after the host-side checks, having enqueued nothing.
+static int ctxkv_append_impl(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
+                             const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
+                             size_t workspace_bytes, void* stream, bool validate_only) {
   if (!h || !ctx_offsets || !caches) return DFLASH_ERR_ARG;
   const dflash_ctxkv_config& c = h->cfg;
   const int nl = c.n_layers, nkv = c.n_kv_heads, d = c.head_dim, H = c.hidden;
@@ -1208,7 +1267,7 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
     if (!caches[l] || !caches[l]->k || !caches[l]->v || !caches[l]->len) return DFLASH_ERR_ARG;
   const dflash_kv_cache* c0 = caches[0];
   const int B = c0->batch;
-  if (B < 1 || B > DFLASH_MAX_BATCH) return DFLASH_ERR_ARG;
+  if (B < 1 || B > kMaxBatch) return DFLASH_ERR_ARG;
   if (c0->capacity <= 0 || c0->capacity % kKeyTile || c0->capacity > kMaxCapacity) return DFLASH_ERR_SHAPE;
   for (int l = 1; l < nl; ++l) {
     if (caches[l]->batch != B || caches[l]->capacity != c0->capacity) return DFLASH_ERR_SHAPE;
@@ -1250,6 +1309,8 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   const CtxCarve wc = ctx_carve(c, Mc, h->mx);
   if (workspace_bytes < wc.total || reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return DFLASH_ERR_WORKSPACE;
+
+  if (validate_only) return DFLASH_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -1336,6 +1397,44 @@ int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32
   return DFLASH_OK;
 }
 
+extern "C" {
+
+int dflash_ctxkv_append(dflash_ctxkv* h, const void* context_states, const int32_t* ctx_offsets,
+                        const int32_t* positions, dflash_kv_cache* const* caches, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!h || !ctx_offsets || !caches || !caches[0]) return DFLASH_ERR_ARG;
+  const int B = caches[0]->batch;
+  if (B <= kMaxBatch)
+    return ctxkv_append_impl(h, context_states, ctx_offsets, positions, caches, workspace, workspace_bytes, stream,
+                             false);
+  // more sequences than one launch plans for: runs of at most kMaxBatch on
+  // views of every layer's cache, all checked before the first runs
+  const dflash_ctxkv_config& c = h->cfg;
+  if (B > DFLASH_MAX_BATCH || c.n_layers > kMaxLayers) return DFLASH_ERR_ARG;
+  if (ctx_offsets[0] != 0) return DFLASH_ERR_SHAPE;
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!caches[l] || !caches[l]->len || caches[l]->batch != B) return caches[l] ? DFLASH_ERR_SHAPE : DFLASH_ERR_ARG;
+  const int es = c.dtype == DFLASH_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)c.hidden * es;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int b0 = 0; b0 < B; b0 += kMaxBatch) {
+      const int nb = std::min(kMaxBatch, B - b0);
+      int32_t offs[kMaxBatch + 1];
+      for (int i = 0; i <= nb; ++i) offs[i] = ctx_offsets[b0 + i] - ctx_offsets[b0];
+      dflash_kv_cache views[kMaxLayers];
+      dflash_kv_cache* vp[kMaxLayers];
+      for (int l = 0; l < c.n_layers; ++l) {
+        views[l] = cache_view(caches[l], b0, nb, c.n_kv_heads, c.head_dim, es);
+        vp[l] = &views[l];
+      }
+      const int st = ctxkv_append_impl(
+          h, context_states ? static_cast<const char*>(context_states) + (size_t)ctx_offsets[b0] * row_bytes : nullptr,
+          offs, positions ? positions + ctx_offsets[b0] : nullptr, vp, workspace, workspace_bytes, stream, pass == 0);
+      if (st != DFLASH_OK) return st;
+    }
+  return DFLASH_OK;
+}
+
 int dflash_ctxkv_set_append_mode(dflash_ctxkv* h, int32_t mode) {
   if (!h || mode < DFLASH_APPEND_AUTO || mode > DFLASH_APPEND_SEPARATE) return DFLASH_ERR_ARG;
   h->append_mode = mode;
@@ -1375,7 +1474,7 @@ DecCarve dec_carve(const dflash_decoder* D, int64_t batch, int64_t total_ctx) {
   const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, mq = batch * c.block_size;
   DecCarve w{};
   size_t off = 0;
-  w.attn = off; off += align_up(carve(D->attn, batch, total_ctx).total);
+  w.attn = off; off += align_up(carve(D->attn, std::min<int64_t>(batch, kMaxBatch), total_ctx).total);
   w.a = off;    off += align_up(mq * c.hidden * es);
   w.att = off;  off += align_up(mq * c.hidden * es);
   w.h = off;    off += align_up(mq * c.hidden * es);
@@ -1455,8 +1554,8 @@ int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hid
   void* act = ws + wc.act;
   const size_t attn_bytes = wc.a - wc.attn;
   // every check of the attention step before anything is enqueued
-  int st = attn_step_impl(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
-                          stream, true);
+  int st = attn_step_any(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
+                         stream, true);
   if (st != DFLASH_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1465,8 +1564,8 @@ int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hid
   // input_layernorm, then the attention layer step (its o_proj output in att)
   if (launch_rms_rows(c.dtype, x, nullptr, D->w.input_norm, nullptr, a, Mq, H, eps, s) != hipSuccess)
     return DFLASH_ERR_HIP;
-  st = attn_step_impl(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
-                      stream, false);
+  st = attn_step_any(D->attn, a, target_hidden, ctx_offsets, positions, cache, att, ws + wc.attn, attn_bytes,
+                     stream, false);
   if (st != DFLASH_OK) return st;
   // h = x + att (the residual stream), m = post_attention_layernorm(h)
   if (launch_rms_rows(c.dtype, x, att, D->w.post_norm, h, m, Mq, H, eps, s) != hipSuccess) return DFLASH_ERR_HIP;

@@ -63,9 +63,13 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
-/* Largest batch one step accepts (per-sequence lengths ride in the kernel
- * arguments). */
-#define DFLASH_MAX_BATCH 256
+/* Largest batch one step (or precompute append) accepts. Per-sequence lengths
+ * ride in the kernel arguments of one launch for at most DFLASH_LAUNCH_BATCH
+ * sequences; a larger batch runs as consecutive launches over runs of at most
+ * DFLASH_LAUNCH_BATCH sequences (they are independent), each run checked
+ * before the first is enqueued, sharing one workspace sized for one run. */
+#define DFLASH_MAX_BATCH 65536
+#define DFLASH_LAUNCH_BATCH 256
 
 /* Layer shape and numerics. Limits checked by dflash_layer_create:
  *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0; n_kv_heads <= 256;
@@ -207,8 +211,8 @@ size_t dflash_workspace_bytes(const dflash_layer* layer, int32_t batch,
  *                                columns 128 c + 32 j .. + 31 of row m
  * The scratch of dflash_attn_step_noalloc has another layout.
  * Errors: DFLASH_ERR_ARG (null layer or offset, batch outside [1,
- * DFLASH_MAX_BATCH], total_ctx < 0, unknown region, an MXFP8 region of a
- * bf16 or fp32 layer). */
+ * DFLASH_LAUNCH_BATCH] (a larger step reuses the workspace run by run),
+ * total_ctx < 0, unknown region, an MXFP8 region of a bf16 or fp32 layer). */
 enum { DFLASH_WS_ATTN_OUT = 0, DFLASH_WS_ATTN_OUT_MX = 1, DFLASH_WS_ATTN_OUT_MX_SCALES = 2 };
 int dflash_workspace_offset(const dflash_layer* layer, int32_t batch, int64_t total_ctx, int32_t region,
                             size_t* offset);

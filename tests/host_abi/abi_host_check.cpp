@@ -463,8 +463,9 @@ void test_layer_steps_random(int cases) {
     LayerBufs b;
     dflash_layer* L = make_layer(c, b, mx);
     if (!L) continue;
-    const int B = rng.range(0, 4) == 0 ? rng.range(200, DFLASH_MAX_BATCH) : rng.range(1, 24);
-    const int capacity = 64 * rng.range(1, B > 64 ? 8 : 24);
+    const int pick = rng.range(0, 9);
+    const int B = pick < 2 ? rng.range(200, DFLASH_LAUNCH_BATCH) : (pick == 2 ? rng.range(257, 700) : rng.range(1, 24));
+    const int capacity = 64 * rng.range(1, B > 256 ? 4 : (B > 64 ? 8 : 24));
     const bool paged = rng.range(0, 1);
     const int es = dtype == DFLASH_BF16 ? 2 : 4;
     Cache cache(B, nkv, d, es, capacity, paged, rng.range(0, 3), &rng);
