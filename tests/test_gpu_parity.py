@@ -246,3 +246,16 @@ def test_invalid_steps_change_nothing():
     assert cache.lengths[0] == cache.capacity - 16 and cache.lengths[1] == lens[1]
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+def test_maximum_capacity_single_sequence():
+    """One sequence filling the largest capacity (2^21 rows, the 16-bit key-tile
+    index at its top: 32768 tiles) at the largest positions, split over every
+    work-group, so the merge folds 256 parts of one pair."""
+    cap = 1 << 21
+    cfg = small(batch=1, hidden=64, n_q_heads=1, n_kv_heads=1, head_dim=64, block_size=16,
+                cached_len=cap - 16 - 3, new_ctx=3, max_position=cap, config_id=23)
+    case = make_case(cfg, seed=0)
+    assert int(case.total_len[0]) == cap and case.capacity() == cap
+    print(f"[max capacity] T = {cap} keys", flush=True)
+    run_and_check(case)
