@@ -1,0 +1,72 @@
+"""A seeded sweep of small random layer shapes against the float64 oracle:
+dtype, head_dim, KV heads, group size, block size, window, batch, ragged
+lengths (empty caches and context-free sequences included), contiguous or
+paged cache, append path, and with or without a position array. Each case is
+small enough for the oracle to finish in well under a second, and spans
+several key tiles, so the sweep reaches shape combinations the hand-picked
+cases do not."""
+import numpy as np
+import pytest
+import torch
+
+from harness import (assert_close, cache_bits, check_cache_after_step, make_cache, make_layer, run_oracle,
+                     step_inputs, to64)
+from workload import LayerConfig, make_case
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+
+
+def draw(i):
+    rng = np.random.default_rng(1000 + i)
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    d = int(rng.choice([64, 128]))
+    nkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    bs = int(rng.choice([b for b in (1, 2, 4, 8, 16) if b * g <= 64]))
+    hidden = 64 * int(rng.integers(1, 9))
+    window = int(rng.choice([0, 0, 0, int(rng.integers(1, 400))]))
+    B = int(rng.integers(1, 9))
+    lo = int(rng.choice([0, 0, 50, 300]))
+    cached = (lo, lo + int(rng.integers(0, 500)))
+    new_ctx = (0, int(rng.choice([0, 5, 40])))
+    cfg = LayerConfig(f"R{i}", B, hidden, nkv * g, nkv, d, bs, dtype, cached, new_ctx, config_id=200 + i,
+                      sliding_window=window)
+    layout = "paged" if rng.random() < 0.4 else "contiguous"
+    mode = str(rng.choice(["auto", "fused", "separate"]))
+    positions = bool(rng.random() < 0.7)
+    return cfg, layout, mode, positions
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape_matches_oracle(i):
+    cfg, layout, mode, use_pos = draw(i)
+    case = make_case(cfg, seed=i)
+    print(f"[sweep {i}] {cfg.dtype} B={cfg.batch} H={cfg.hidden} nq={cfg.n_q_heads} nkv={cfg.n_kv_heads} "
+          f"d={cfg.head_dim} bs={cfg.block_size} W={cfg.sliding_window} lens={case.cached_len.tolist()} "
+          f"ctx={case.new_ctx.tolist()} {layout} {mode} positions={'array' if use_pos else 'none'}", flush=True)
+    layer = make_layer(case)
+    layer.set_append_mode(mode)
+    if layout == "paged":
+        from test_gpu_paged import check_paged_after, make_paged
+        cache = make_paged(case, seed=i)
+        for b in range(case.batch):
+            cache.reserve(b, int(case.total_len[b]))
+        cache.sync()
+    else:
+        cache = make_cache(case)
+    bk, bv = cache_bits(cache) if layout == "contiguous" else (None, None)
+    if layout == "paged":
+        from harness import raw_bits
+        pk, pv = raw_bits(cache.k), raw_bits(cache.v)
+    hs, th, pos = step_inputs(case)
+    out = layer.step(hs, th, case.ctx_offsets, pos if use_pos else None, cache)
+    torch.cuda.synchronize()
+    ref, new = run_oracle(case)
+    assert_close(to64(out), ref, cfg.dtype, f"sweep {i} out")
+    if layout == "paged":
+        check_paged_after(cache, pk, pv, case.cached_len, case.total_len, new, cfg.dtype, f"sweep {i}")
+    else:
+        check_cache_after_step(case, cache, bk, bv, new)
+    assert layer.poll_error() == 0
