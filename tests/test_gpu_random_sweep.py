@@ -70,3 +70,68 @@ def test_random_shape_matches_oracle(i):
     else:
         check_cache_after_step(case, cache, bk, bv, new)
     assert layer.poll_error() == 0
+
+
+def draw_ctxkv(i):
+    from workload import CTXKV_CONFIGS
+    rng = np.random.default_rng(5000 + i)
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    d = int(rng.choice([64, 128]))
+    lo = int(rng.choice([0, 0, 100]))
+    pc = CTXKV_CONFIGS["P1"].replace(name=f"Q{i}", batch=int(rng.integers(1, 7)), hidden=64 * int(rng.integers(1, 9)),
+                                     n_layers=int(rng.integers(1, 5)), n_kv_heads=int(rng.choice([1, 2, 4])),
+                                     head_dim=d, dtype=dtype, cached_len=(lo, lo + int(rng.integers(0, 300))),
+                                     new_ctx=(0, int(rng.choice([1, 20, 90]))), config_id=300 + i)
+    layout = str(rng.choice(["contiguous", "shared", "per_layer"]))
+    mode = str(rng.choice(["auto", "fused", "separate"]))
+    positions = bool(rng.random() < 0.7)
+    return pc, layout, mode, positions
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_precompute_matches_oracle(i):
+    import oracle
+    from harness import dev, raw_bits
+    from test_gpu_context_kv import make_caches, make_precompute, oracle_caches
+    from test_gpu_paged import check_paged_after, paged_stack
+    from workload import make_ctxkv_case
+    pc, layout, mode, use_pos = draw_ctxkv(i)
+    case = make_ctxkv_case(pc, seed=i)
+    print(f"[precompute sweep {i}] {pc.dtype} B={pc.batch} H={pc.hidden} L={pc.n_layers} nkv={pc.n_kv_heads} "
+          f"d={pc.head_dim} lens={case.cached_len.tolist()} ctx={case.new_ctx.tolist()} {layout} {mode} "
+          f"positions={'array' if use_pos else 'none'}", flush=True)
+    dt = torch.bfloat16 if pc.dtype == "bf16" else torch.float32
+    pre = make_precompute(case)
+    pre.set_append_mode(mode)
+    caches = make_caches(case) if layout == "contiguous" else paged_stack(case, dt, i, layout)
+    before = [cache_bits(c) if layout == "contiguous" else (raw_bits(c.k), raw_bits(c.v)) for c in caches]
+    pos = torch.from_numpy(case.positions).cuda() if use_pos else None
+    pre.append(dev(case.context_states, dt), case.ctx_offsets, pos, caches)
+    torch.cuda.synchronize()
+    assert pre.poll_error() == 0
+    ref = oracle.context_kv_precompute(pc, case.weights, oracle_caches(case), case.context_states,
+                                       case.ctx_offsets, case.positions)
+    tot = case.cached_len + case.new_ctx
+    for layer, kv in enumerate(caches):
+        assert kv.lengths.tolist() == tot.tolist()
+        if layout == "contiguous":
+            from harness import assert_close_stored
+            k, v = kv.k_rows(), kv.vt_rows()
+            kb, vb = cache_bits(kv)
+            for b in range(case.batch):
+                lb, tb = int(case.cached_len[b]), int(tot[b])
+                if tb > lb:
+                    assert_close_stored(to64(k[b, :, lb:tb]), ref[layer].k[b][:, lb:tb], pc.dtype, f"{i} K {b}")
+                    assert_close_stored(to64(v[b, :, :, lb:tb].transpose(1, 2)), ref[layer].v[b][:, lb:tb],
+                                        pc.dtype, f"{i} V {b}")
+            # nothing outside the appended rows changed
+            kept = np.ones(kb.shape, bool)
+            keptv = np.ones(vb.shape, bool)
+            for b in range(case.batch):
+                lb, tb = int(case.cached_len[b]), int(tot[b])
+                kept[b, :, lb:tb] = False
+                keptv[b, :, :, lb:tb] = False
+            np.testing.assert_array_equal(kb[kept], before[layer][0][kept])
+            np.testing.assert_array_equal(vb[keptv], before[layer][1][keptv])
+        else:
+            check_paged_after(kv, *before[layer], case.cached_len, tot, ref[layer], pc.dtype, f"sweep {i} layer {layer}")
