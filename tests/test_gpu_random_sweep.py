@@ -135,3 +135,25 @@ def test_random_precompute_matches_oracle(i):
             np.testing.assert_array_equal(vb[keptv], before[layer][1][keptv])
         else:
             check_paged_after(kv, *before[layer], case.cached_len, tot, ref[layer], pc.dtype, f"sweep {i} layer {layer}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_decoder_matches_oracle(i):
+    """The decoder layer on random shapes, every piece against the oracle fed
+    the kernel's own intermediates within its derived bound."""
+    from test_gpu_decoder import check_pieces, make_decoder
+    from workload import make_mlp_weights
+    cfg, layout, mode, use_pos = draw(100 + i)
+    case = make_case(cfg, seed=i)
+    inter = 64 * int(np.random.default_rng(7000 + i).integers(1, 13))
+    print(f"[decoder sweep {i}] {cfg.dtype} B={cfg.batch} H={cfg.hidden} nq={cfg.n_q_heads} nkv={cfg.n_kv_heads} "
+          f"d={cfg.head_dim} bs={cfg.block_size} W={cfg.sliding_window} I={inter}", flush=True)
+    mw = make_mlp_weights(case, inter)
+    dec = make_decoder(case, mw)
+    cache = make_cache(case)
+    x, th, pos = step_inputs(case)
+    ws = dec.workspace(case.batch, int(case.ctx_offsets[-1]))
+    out = dec.step(x, th, case.ctx_offsets, pos if use_pos else None, cache, workspace=ws)
+    torch.cuda.synchronize()
+    assert dec.poll_error() == 0
+    check_pieces(case, mw, dec, ws, x, out)
