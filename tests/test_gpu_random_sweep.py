@@ -157,3 +157,20 @@ def test_random_decoder_matches_oracle(i):
     torch.cuda.synchronize()
     assert dec.poll_error() == 0
     check_pieces(case, mw, dec, ws, x, out)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_mxfp8_layer_matches_oracle(i):
+    """The MXFP8 layer step on random bf16 shapes (hidden and nq * d multiples
+    of 128), through the same derived checks as the hand-picked cases."""
+    from test_gpu_mxfp8_layer import run_mx
+    rng = np.random.default_rng(9000 + i)
+    d = int(rng.choice([64, 128]))
+    nkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([2, 4, 8])) if d == 64 else int(rng.choice([1, 2, 4]))
+    bs = int(rng.choice([b for b in (2, 4, 8, 16) if b * g <= 64]))
+    cfg = LayerConfig(f"X{i}", int(rng.integers(1, 7)), 128 * int(rng.integers(1, 5)), nkv * g, nkv, d, bs, "bf16",
+                      (0, int(rng.integers(1, 600))), (0, int(rng.choice([0, 8, 40]))), config_id=400 + i,
+                      sliding_window=int(rng.choice([0, 0, int(rng.integers(1, 300))])))
+    assert (cfg.n_q_heads * d) % 128 == 0
+    run_mx(make_case(cfg, seed=i), seed=i)
