@@ -22,8 +22,9 @@
 // whose concurrent reads scatter over the cache whenever lengths are ragged).
 // A range crosses pair boundaries; the part of a pair inside a range
 // is a segment. A segment that is a whole pair writes the output directly; a
-// pair cut by a range boundary leaves fp32 partials (un-normalised O, exponent
-// offset, sum) in slot 2w (the range's first segment) or 2w+1 (its last),
+// pair cut by a range boundary leaves partials (un-normalised O in the
+// element type, the exponent offset and the sum in fp32) in slot 2w (the
+// range's first segment) or 2w+1 (its last),
 // which HK4 merges in a launch of its own. Merging inside HK3 (the last
 // part of a pair to finish folds it) needs the partials coherent across
 // XCDs before the part counts itself in. Each XCD has its own L2, so that
@@ -238,6 +239,13 @@ template <> __device__ inline void store4<__bf16>(__bf16* p, const f32x4& v) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) o[r] = (__bf16)v[r];
   *reinterpret_cast<bf16x4*>(p) = o;
+}
+template <typename T> __device__ inline f32x4 load4(const T* p);
+template <> __device__ inline f32x4 load4<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <> __device__ inline f32x4 load4<__bf16>(const __bf16* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);  // element 0 in the low half
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xffff0000u)};
 }
 
 // Position in the flattened work: pair (b, j), key tile, the pair's tiles.
@@ -569,9 +577,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
             }
           } else {
             const int slot = 2 * (int)w + (seg_start_flat == 0 ? 0 : 1);
-            float* po = a.part_o + ((size_t)slot * kMaxQueryRows + qrow) * D;
+            T* po = static_cast<T*>(a.part_o) + ((size_t)slot * kMaxQueryRows + qrow) * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * q) = acc[db];
+            for (int db = 0; db < DB; ++db) store4<T>(po + db * 16 + 4 * q, acc[db]);
             if (q == 0) {
               float* pm = a.part_ml + ((size_t)slot * kMaxQueryRows + qrow) * 2;
               pm[0] = m_run;
@@ -615,7 +623,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
         const size_t sr = (size_t)slot(p0 + k) * kMaxQueryRows + row;
         m[k] = a.part_ml[sr * 2];
         l[k] = a.part_ml[sr * 2 + 1];
-        o[k] = *reinterpret_cast<const f32x4*>(a.part_o + sr * D + d4);
+        o[k] = load4<T>(static_cast<const T*>(a.part_o) + sr * D + d4);
       }
     }
     const float Mn = fmaxf(fmaxf(M, fmaxf(m[0], m[1])), fmaxf(m[2], m[3]));

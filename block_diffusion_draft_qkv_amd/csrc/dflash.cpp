@@ -193,7 +193,7 @@ Carve carve(const dflash_layer* L, int64_t batch, int64_t total_ctx, const StepP
   // The attention kernel fetches whole 64-row query tiles: slack past the end.
   w.qpack = off;   off += align_up(batch * c.n_kv_heads * c.block_size * g * d * es + kMaxQueryRows * d * 4);
   w.obuf = off;    off += align_up(mq * c.n_q_heads * d * es);
-  w.part_o = off;  off += align_up(2 * gmax * kMaxQueryRows * d * 4);
+  w.part_o = off;  off += align_up(2 * gmax * kMaxQueryRows * d * es);
   w.part_ml = off; off += align_up(2 * gmax * kMaxQueryRows * 2 * 4);
   if (L->mx) {
     const int64_t mc = std::max<int64_t>(total_ctx, 1), od = (int64_t)c.n_q_heads * d;
@@ -790,7 +790,7 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   aa.kc = cache->k;
   aa.vc = cache->v;
   aa.o = obuf;
-  aa.part_o = reinterpret_cast<float*>(ws + wc.part_o);
+  aa.part_o = ws + wc.part_o;
   aa.part_ml = reinterpret_cast<float*>(ws + wc.part_ml);
   aa.nq = nq; aa.nkv = nkv; aa.bs = bs; aa.R = R; aa.cap = cache->capacity;
   // A window at least the capacity keeps every key (|query - key| < T_b <= capacity).

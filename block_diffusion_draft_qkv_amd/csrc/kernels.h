@@ -210,7 +210,7 @@ struct AttnArgs {
   const void* kc;
   const void* vc;
   void* o;                 // [B*bs][nq d] attention output (pre o_proj)
-  float* part_o;           // [2G][64][d] un-normalised partial outputs
+  void* part_o;            // [2G][64][d] un-normalised partial outputs, in the element type
   float* part_ml;          // [2G][64][2] running max (log2 domain) and sum
   int32_t nq, nkv, bs, R, cap, window, G;
   MxOut mxo;
@@ -236,7 +236,7 @@ int attn_key_tile(int dtype, int head_dim);
 // Pairs that the attention split over several work-group ranges (at most
 // G - 1: each contains a range boundary), merged by HK4.
 struct MergeArgs {
-  const float* part_o;
+  const void* part_o;
   const float* part_ml;
   void* o;
   MxOut mxo;
