@@ -281,19 +281,21 @@ TileChoice choose_tiles_fill(int num_cus, int m, int n, int k, int es, int max_k
   return best;
 }
 
-// The gate/up SwiGLU projection (m rows, 2 i columns in 128-column tiles of
-// 64 gate + 64 up, k = h, no k split) as one launch of bm-row tiles, or as two
-// launches over disjoint column ranges: the first c1 column tiles in bm-row
-// tiles filling whole rounds of the CUs, the rest in bm2-row tiles. Priced
-// with the fill model of choose_tiles_fill plus ~3 us for the second launch.
-// At m = 512, i = 12288 (C3's decoder) one launch of 256-row tiles takes 384
-// work-groups, a round and a half; 256-row tiles over the first 128 column
-// tiles and 128-row tiles over the other 64 fill two whole rounds (decoder
-// step 359 -> 350 us, bit-identical: a tile's shape does not change the
-// order of any output's sum). The split needs i % 64 == 0 so that both
-// launches cover whole tiles.
+// The gate/up SwiGLU projection (m rows, 2 i columns, k = h, no k split):
+// one launch of bm x 128 tiles (64 gate + 64 up columns), one launch of
+// 256 x 192 tiles (bn = 192: bf16, m % 256 == 0, i % 96 == 0), or two
+// launches of 128-column tiles over disjoint column ranges: the first c1
+// column tiles in bm-row tiles filling whole rounds of the CUs, the rest in
+// bm2-row tiles. Priced with the fill model of choose_tiles_fill plus ~3 us
+// for a second launch. At m = 512, i = 12288 (C3's decoder) 256 x 128 tiles
+// take 384 work-groups, a round and a half (122.6 us by the kernel trace);
+// 256 x 128 tiles over the first 128 column tiles and 128 x 128 over the
+// other 64 fill two whole rounds (63.4 + 41.2 us); 256 x 192 tiles fill one.
+// Every form gives the same bits: no output's sum changes order with the
+// tile's shape. The split needs i % 64 == 0 so that both launches cover whole
+// tiles.
 struct SwigluPlan {
-  int bm, c1, bm2;  // c1 == column tiles: one launch
+  int bm, bn, c1, bm2;  // c1 == the column tiles of width bn: one launch
 };
 SwigluPlan swiglu_plan(int num_cus, int m, int i, int h, int es) {
   const int tn = (2 * i + 127) / 128;
@@ -304,11 +306,17 @@ SwigluPlan swiglu_plan(int num_cus, int m, int i, int h, int es) {
   };
   const int first = es == 2 && m % 256 == 0 ? 0 : 1;
   static const int rows[3] = {256, 128, 64};
-  SwigluPlan best{64, tn, 64};
+  SwigluPlan best{64, 128, tn, 64};
   double best_t = -1.0;
   for (int a = first; a < 3; ++a) {
     const double t = cost(rows[a], tn);
-    if (best_t < 0 || t < best_t - 1e-9) { best_t = t; best = SwigluPlan{rows[a], tn, rows[a]}; }
+    if (best_t < 0 || t < best_t - 1e-9) { best_t = t; best = SwigluPlan{rows[a], 128, tn, rows[a]}; }
+  }
+  if (first == 0 && i % 96 == 0 && h % 32 == 0) {
+    const int tw = 2 * i / 192;
+    const int64_t tiles = (int64_t)(m / 256) * tw;
+    const double t = (double)((tiles + num_cus - 1) / num_cus) * (15.0 + (256 + 192) * fill);
+    if (t < best_t - 1e-9) { best_t = t; best = SwigluPlan{256, 192, tw, 256}; }
   }
   if (i % 64 != 0) return best;
   for (int a = first; a < 3; ++a) {
@@ -317,7 +325,7 @@ SwigluPlan swiglu_plan(int num_cus, int m, int i, int h, int es) {
     if (c1 <= 0 || c1 >= tn || ((int64_t)c1 * mt) % num_cus != 0) continue;
     for (int b = a + 1; b < 3; ++b) {
       const double t = cost(rows[a], c1) + cost(rows[b], tn - c1) + 3.0;
-      if (t < best_t - 1e-9) { best_t = t; best = SwigluPlan{rows[a], c1, rows[b]}; }
+      if (t < best_t - 1e-9) { best_t = t; best = SwigluPlan{rows[a], 128, c1, rows[b]}; }
     }
   }
   return best;
@@ -1611,28 +1619,35 @@ int dflash_decoder_step(dflash_decoder* D, const void* x, const void* target_hid
   if (st != DFLASH_OK) return st;
   // h = x + att (the residual stream), m = post_attention_layernorm(h)
   if (launch_rms_rows(c.dtype, x, att, D->w.post_norm, h, m, Mq, H, eps, s) != hipSuccess) return DFLASH_ERR_HIP;
-  // act = silu(m Wg^T) * (m Wu^T): 128-column tiles (64 gate + 64 up), no k
-  // split (the activation needs whole sums), in one or two launches
+  // act = silu(m Wg^T) * (m Wu^T), no k split (the activation needs whole
+  // sums): 256 x 192 tiles, or 128-column tiles (64 gate + 64 up) in one or two
+  // launches, as swiglu_plan picks
   {
     const int tn = (2 * I + 127) / 128, es = (int)elem_size(c);
     const SwigluPlan sp = swiglu_plan(D->num_cus, Mq, I, H, es);
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.nprob = 1;
-    ga.p[0] = {m, D->w.w_gate_up, act, Mq, sp.c1 < tn ? 2 * sp.c1 * 64 : 2 * I, H, H, H, I, sp.c1, 0, 0};
-    ga.p[0].b_pair = I;
-    if (launch_gemm_swiglu(c.dtype, ga, ((Mq + sp.bm - 1) / sp.bm) * sp.c1, sp.bm, s) != hipSuccess)
-      return DFLASH_ERR_HIP;
-    if (sp.c1 < tn) {
-      // the other column tiles: gate rows and output columns from c1 * 64 on
-      // (the up rows stay b_pair = I past their gate rows)
-      const int c2 = tn - sp.c1;
-      ga.p[0].b = static_cast<const char*>(D->w.w_gate_up) + (size_t)sp.c1 * 64 * H * es;
-      ga.p[0].c = static_cast<char*>(act) + (size_t)sp.c1 * 64 * es;
-      ga.p[0].n = 2 * c2 * 64;
-      ga.p[0].tiles_n = c2;
-      if (launch_gemm_swiglu(c.dtype, ga, ((Mq + sp.bm2 - 1) / sp.bm2) * c2, sp.bm2, s) != hipSuccess)
+    if (sp.bn == 192) {
+      ga.p[0] = {m, D->w.w_gate_up, act, Mq, 2 * I, H, H, H, I, sp.c1, 0, 0};
+      ga.p[0].b_pair = I;
+      if (launch_gemm_swiglu_wide(ga, (Mq / 256) * sp.c1, s) != hipSuccess) return DFLASH_ERR_HIP;
+    } else {
+      ga.p[0] = {m, D->w.w_gate_up, act, Mq, sp.c1 < tn ? 2 * sp.c1 * 64 : 2 * I, H, H, H, I, sp.c1, 0, 0};
+      ga.p[0].b_pair = I;
+      if (launch_gemm_swiglu(c.dtype, ga, ((Mq + sp.bm - 1) / sp.bm) * sp.c1, sp.bm, s) != hipSuccess)
         return DFLASH_ERR_HIP;
+      if (sp.c1 < tn) {
+        // the other column tiles: gate rows and output columns from c1 * 64 on
+        // (the up rows stay b_pair = I past their gate rows)
+        const int c2 = tn - sp.c1;
+        ga.p[0].b = static_cast<const char*>(D->w.w_gate_up) + (size_t)sp.c1 * 64 * H * es;
+        ga.p[0].c = static_cast<char*>(act) + (size_t)sp.c1 * 64 * es;
+        ga.p[0].n = 2 * c2 * 64;
+        ga.p[0].tiles_n = c2;
+        if (launch_gemm_swiglu(c.dtype, ga, ((Mq + sp.bm2 - 1) / sp.bm2) * c2, sp.bm2, s) != hipSuccess)
+          return DFLASH_ERR_HIP;
+      }
     }
   }
   // out = h + act Wd^T

@@ -510,6 +510,161 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_swiglu_kernel(GemmArgs a
   }
 }
 
+// The SwiGLU GEMM in 256 x 192 tiles (96 gate + 96 up columns), bf16 only.
+// At 512 rows and a 12288-wide MLP that is 256 work-groups, one round of 256
+// CUs, where 128-column tiles make 384 (a round and a half) and stream more
+// bytes per output. Roles as in gemm_core (four consumer waves in 2 x 2, two
+// producer waves), but a k step is 32 elements (64-byte rows): a 64-element
+// step of this tile (56 KB) would leave LDS room for two stages only, while
+// 28 KB steps give five, as many bytes in flight as the 128-column tiles
+// keep. A consumer wave holds a 128 x 96 sub-tile (192 accumulator VGPRs), so
+// it reads its A fragments four 16-row blocks at a time. k is summed in the
+// same 32-element MFMA blocks and the same order as gemm_swiglu_kernel, so
+// the outputs are the same bits.
+struct WideShape {
+  static constexpr int BM = 256, BN = 192;
+  static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64, STAGE = A_BYTES + B_BYTES;
+  static constexpr int APP = BM / 16 / kGemmProducers, BPP = BN / 16 / kGemmProducers;  // 1 KB blocks
+  static constexpr int PER = APP + BPP;
+  static constexpr int S = 5;
+  static constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 16, NI = WN / 16, MH = MI / 2;
+  static_assert(S * STAGE <= 160 * 1024, "the ring fits in LDS");
+  static_assert((S - 1) * PER <= 63, "outstanding DMA blocks must fit vmcnt");
+  static_assert(MI % 4 == 0, "A fragments go four blocks at a time");
+};
+
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_swiglu_wide_kernel(GemmArgs args) {
+  using Sh = WideShape;
+  using T = __bf16;
+  constexpr int S = Sh::S, STAGE = Sh::STAGE, A_BYTES = Sh::A_BYTES, APP = Sh::APP, BPP = Sh::BPP;
+  constexpr int PER = Sh::PER, BN = Sh::BN, WM = Sh::WM, WN = Sh::WN, MI = Sh::MI, NI = Sh::NI, MH = Sh::MH;
+  constexpr int XR = MH * NI * 4;
+  static_assert(4 * XR * 64 * 4 <= S * STAGE, "the exchange fits in the ring");
+  __shared__ u32x4 lds[S * STAGE / 16];
+  const TileJob J = tile_job<Sh::BM, Sh::BN>(args);
+  const GemmProblem& P = J.P;
+  const int nk = P.k / 32;  // 64-byte k steps
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = lds_base(lds);
+
+  if (wave >= kGemmConsumers) {
+    // ---------------------------------------------------------- producers
+    // Block i * kGemmProducers + pw of an operand covers 16 rows of 64 bytes;
+    // each lane fetches the chunk that belongs at its swizzled LDS position.
+    const int pw = wave - kGemmConsumers;
+    uint32_t aoff[APP], boff[BPP];
+#pragma unroll
+    for (int i = 0; i < APP; ++i) {
+      const int row = (i * kGemmProducers + pw) * 16 + lane / 4;
+      const int c = (lane % 4) ^ rswz<4>(row);
+      const int gr = J.m0 + row < P.m ? J.m0 + row : P.m - 1;
+      aoff[i] = (uint32_t)((size_t)gr * P.lda * sizeof(T)) + (uint32_t)(c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < BPP; ++i) {
+      const int row = (i * kGemmProducers + pw) * 16 + lane / 4;
+      const int c = (lane % 4) ^ rswz<4>(row);
+      // gate rows for the tile's first half, up rows for its second
+      const int j = J.n0 / 2 + (row < BN / 2 ? row : row - BN / 2);
+      const int gr = (j < P.b_pair ? j : P.b_pair - 1) + (row < BN / 2 ? 0 : P.b_pair);
+      boff[i] = (uint32_t)((size_t)gr * P.ldb * sizeof(T)) + (uint32_t)(c * 16);
+    }
+    const char* Ab = static_cast<const char*>(P.a);
+    const char* Bb = static_cast<const char*>(P.b);
+    auto issue = [&](int step) {
+      const size_t kbyte = (size_t)step * 64;
+      const uint32_t sl = lds0 + (uint32_t)(step % S) * STAGE;
+      const void* ab = uniform_ptr(Ab + kbyte);
+      const void* bb = uniform_ptr(Bb + kbyte);
+#pragma unroll
+      for (int i = 0; i < APP; ++i)
+        lds_dma16(aoff[i], ab, sl + (uint32_t)(i * kGemmProducers + pw) * 1024u);
+#pragma unroll
+      for (int i = 0; i < BPP; ++i)
+        lds_dma16(boff[i], bb, sl + A_BYTES + (uint32_t)(i * kGemmProducers + pw) * 1024u);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s);
+    for (int it = 0; it < nk; ++it) {
+      const int after = nk - 1 - it < S - 2 ? nk - 1 - it : S - 2;
+      stage_wait<PER, S>(after);
+      block_barrier();
+      if (it + S - 1 < nk) issue(it + S - 1);
+    }
+    block_barrier();  // the epilogue's two barriers
+    block_barrier();
+    return;
+  }
+
+  // ------------------------------------------------------------ consumers
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, r16 = lane & 15;
+  // operand rows wm*WM + mi*16 + r16 (A) and wn*WN + ni*16 + r16 (W), logical
+  // chunk q (k 8q .. 8q + 7 of the step); the swizzle depends on r16 only
+  const int sw = rswz<4>(r16);
+  const uint32_t ard = (uint32_t)((wm * WM + r16) * 64 + ((q ^ sw) * 16));
+  const uint32_t brd = (uint32_t)(A_BYTES + (wn * WN + r16) * 64 + ((q ^ sw) * 16));
+  f32x4 acc[NI][MI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < nk; ++it) {
+    block_barrier();
+    const uint32_t sl = lds0 + (uint32_t)(it % S) * STAGE;
+    u32x4 b[NI], a[4];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) b[ni] = lds_read16(sl + brd + (uint32_t)(ni * 1024));
+#pragma unroll
+    for (int g = 0; g < MI / 4; ++g) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = lds_read16(sl + ard + (uint32_t)((4 * g + u) * 1024));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) Mfma<T>::chunk(acc[ni][4 * g + u], b[ni], a[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue as in gemm_swiglu_kernel: wave (wm, 0) holds the gate and wave
+  // (wm, 1) the up half of the same outputs; each hands the partner the row
+  // blocks the partner finishes, then writes silu(g) * u for its own.
+  float* xch = reinterpret_cast<float*>(lds);
+  const int partner = wm * 2 + (1 - wn);
+  block_barrier();  // the last fragment reads of the main loop are done
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int u = 0; u < MH; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xch[(wave * XR + (ni * MH + u) * 4 + r) * 64 + lane] = wn == 0 ? acc[ni][MH + u][r] : acc[ni][u][r];
+  block_barrier();
+  T* C = static_cast<T*>(P.c);
+  const int j0 = J.n0 / 2;
+#pragma unroll
+  for (int u = 0; u < MH; ++u) {
+    const int mi = wn * MH + u;
+    const int m = J.m0 + wm * WM + mi * 16 + r16;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float own = wn == 0 ? acc[ni][u][r] : acc[ni][MH + u][r];
+        const float oth = xch[(partner * XR + (ni * MH + u) * 4 + r) * 64 + lane];
+        const float g = wn == 0 ? own : oth, up = wn == 0 ? oth : own;
+        o[r] = g / (1.0f + __expf(-g)) * up;
+      }
+      const int j = j0 + ni * 16 + 4 * q;
+      if (m < P.m && j < P.b_pair) Store4<T>::put(C + (size_t)m * P.ldc + j, o);
+    }
+  }
+}
+
 // Sum over the four lanes l, l^16, l^32, l^48 that hold one row's columns.
 __device__ inline float quad_sum(float v) {
   v += __shfl_xor(v, 16, 64);
@@ -824,6 +979,12 @@ hipError_t launch_gemm_append(int dtype, int head_dim, const GemmArgs& args, con
   if (total_tiles <= 0) return hipSuccess;
   if (dtype == 1) return launch_append_t<__bf16>(args, nr, total_tiles, bm, head_dim, stream);
   return launch_append_t<float>(args, nr, total_tiles, bm, head_dim, stream);
+}
+
+hipError_t launch_gemm_swiglu_wide(const GemmArgs& args, int total_tiles, hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_swiglu_wide_kernel, dim3(total_tiles), dim3(kGemmThreads), 0, stream, args);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, int bm, hipStream_t stream) {

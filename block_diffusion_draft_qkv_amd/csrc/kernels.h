@@ -149,6 +149,9 @@ hipError_t launch_rms_rows(int dtype, const void* x, const void* y, const void* 
 // W = [W_gate; W_up] stacked ([2 n, k]); one problem, bm x 128 tiles (64 outputs
 // per tile), C in the element type.
 hipError_t launch_gemm_swiglu(int dtype, const GemmArgs& args, int total_tiles, int bm, hipStream_t stream);
+// The same in 256 x 192 tiles (96 gate + 96 up columns; bf16, k % 32 == 0,
+// tiles_n = n / 192 with n = 2 b_pair a multiple of 192).
+hipError_t launch_gemm_swiglu_wide(const GemmArgs& args, int total_tiles, hipStream_t stream);
 
 // The q|k|v + context k|v projection (args as for launch_gemm, tiles bm x
 // head_dim, no k split) doing the work of launch_norm_rope in its epilogue

@@ -136,6 +136,13 @@ CASES = {
     "bf16_window": (lambda: make_case(small(sliding_window=300, cached_len=(200, 900), config_id=63), seed=3),
                     640),
     "C3": (lambda: make_case("C3", seed=0), 12288),
+    # 512 rows: the gate/up projection in 256 x 192 tiles (i % 96 == 0) ...
+    "bf16_wide_tiles": (lambda: make_case(small(batch=32, hidden=1024, cached_len=(0, 300), new_ctx=(0, 8),
+                                                config_id=64), seed=4), 12288),
+    # ... and, with i % 96 != 0 and a deep k, in two launches of 128-column tiles
+    "bf16_two_launches": (lambda: make_case(small(batch=32, hidden=4096, n_q_heads=32, n_kv_heads=8,
+                                                  cached_len=(0, 200), new_ctx=(0, 8), config_id=65), seed=5),
+                          11008),
 }
 
 
