@@ -486,7 +486,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
           }
         }
       }
-      if (t0 + KT > tb || a.window > 0) {
+      // Under a window W the band cuts into a tile only where the tile starts
+      // before T_b - W (the query at T_b - 1 loses its oldest keys there) or
+      // where W < bs (queries lose keys of the block ahead of them): for
+      // t0 >= T_b - W and W >= bs every query q in [T_b - bs, T_b) and key t
+      // in [t0, T_b) have q - t <= W - 1 and t - q <= bs - 1 <= W - 1.
+      const bool band = a.window > 0 && (t0 < tb - a.window || a.window < a.bs);
+      if (t0 + KT > tb || band) {
         // Key t survives if t < T_b and, under a window W, -W < qpos - t < W,
         // i.e. 0 <= qpos - t + W - 1 <= 2W - 2 as one unsigned compare (the
         // host passes W < capacity, so nothing wraps; without a window the
@@ -666,6 +672,14 @@ template <typename T, int D> int wgs_per_cu() { return (160 * 1024) / AttnShape<
 int attn_wgs_per_cu(int dtype, int head_dim) {
   if (dtype == 1) return head_dim == 128 ? wgs_per_cu<__bf16, 128>() : wgs_per_cu<__bf16, 64>();
   return head_dim == 128 ? wgs_per_cu<float, 128>() : wgs_per_cu<float, 64>();
+}
+
+int attn_kv_in_flight(int dtype, int head_dim) {
+  if (dtype == 1)
+    return head_dim == 128 ? (AttnShape<__bf16, 128>::S - 1) * AttnShape<__bf16, 128>::TILE
+                           : (AttnShape<__bf16, 64>::S - 1) * AttnShape<__bf16, 64>::TILE;
+  return head_dim == 128 ? (AttnShape<float, 128>::S - 1) * AttnShape<float, 128>::TILE
+                         : (AttnShape<float, 64>::S - 1) * AttnShape<float, 64>::TILE;
 }
 
 int attn_key_tile(int dtype, int head_dim) {

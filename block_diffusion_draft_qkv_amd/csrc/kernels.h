@@ -235,6 +235,9 @@ hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_
 // and the keys per attention tile.
 int attn_wgs_per_cu(int dtype, int head_dim);
 int attn_key_tile(int dtype, int head_dim);
+// Bytes of K and V tiles one attention work-group keeps in flight (its ring
+// minus the stage being consumed).
+int attn_kv_in_flight(int dtype, int head_dim);
 
 // Pairs that the attention split over several work-group ranges (at most
 // G - 1: each contains a range boundary), merged by HK4.
