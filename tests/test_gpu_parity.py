@@ -102,6 +102,19 @@ def test_sliding_window_bands(window):
     run_and_check(make_case(cfg, seed=window))
 
 
+@pytest.mark.parametrize("edge", [-1, 0, 1])
+@pytest.mark.parametrize("window", [15, 16, 17, 64, 100])
+def test_window_band_edge_tiles(window, edge):
+    """The band mask runs only on key tiles that start before T_b - W (or on
+    every tile when W < block_size): T_b - W one key before, on and one key
+    after the 64-key tile boundary at 128, with windows below, at and above
+    the block size of 16."""
+    T = window + 128 + edge
+    cfg = small(batch=1, sliding_window=window, cached_len=T - 3 - 16, new_ctx=3,
+                config_id=300 + 3 * window + edge)
+    run_and_check(make_case(cfg, seed=window + edge))
+
+
 def test_capacity_exactly_full():
     """T_b equal to the capacity for one sequence (last tile full, no slack)."""
     cfg = small(batch=2, cached_len=(100, 200), new_ctx=(5, 5), config_id=18)
