@@ -44,6 +44,49 @@ __device__ inline float head_sum(float v) {
 // Row slots per wave: a key/query work-group takes 4 * kNormSlots * (128 / D)
 // rows, all of whose loads go out before any is used.
 constexpr int kNormSlots = 4;
+// k slices the host splits a small-M projection into (at most): their loads
+// are all issued before the first add.
+constexpr int kSliceLoads = 4;
+
+// x = sum over the k slices of rows src[r][t] and src[r][t + half] (slice sl
+// at sl * stride[r]): every load of the first kSliceLoads slices goes out
+// before any add, then the slices are added in order (the rounding of a
+// running sum); slices past kSliceLoads, which the host never plans, are
+// added one at a time afterwards.
+template <int N>
+__device__ inline void sum_slices(const float* const (&src)[N], const int64_t (&stride)[N], int kslices, int t,
+                                  int half, float (&x1)[N], float (&x2)[N]) {
+  float l1[kSliceLoads][N], l2[kSliceLoads][N];
+#pragma unroll
+  for (int sl = 0; sl < kSliceLoads; ++sl)
+    if (sl < kslices) {
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        l1[sl][r] = src[r][sl * stride[r] + t];
+        l2[sl][r] = src[r][sl * stride[r] + t + half];
+      }
+    }
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    x1[r] = l1[0][r];
+    x2[r] = l2[0][r];
+  }
+#pragma unroll
+  for (int sl = 1; sl < kSliceLoads; ++sl)
+    if (sl < kslices) {
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        x1[r] += l1[sl][r];
+        x2[r] += l2[sl][r];
+      }
+    }
+  for (int sl = kSliceLoads; sl < kslices; ++sl)
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      x1[r] += src[r][sl * stride[r] + t];
+      x2[r] += src[r][sl * stride[r] + t + half];
+    }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, int yv) {
@@ -101,25 +144,16 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
         pidx[s] = pos_off + n + i;  // queries sit at the window's suffix
       }
     }
-    // Every slot's first k slice goes out before any is used; further slices
-    // (small-M projections split k) are added afterwards.
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      x1[s] = src[s][t];
-      x2[s] = src[s][t + HALF];
-    }
-    for (int sl = 1; sl < a.kslices; ++sl) {
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        x1[s] += src[s][sl * stride[s] + t];
-        x2[s] += src[s][sl * stride[s] + t + HALF];
-      }
-    }
+    // The positions, then every k slice of every slot, all in flight together
+    // (the cos/sin rows wait only for the positions).
     int p[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
+    for (int s = 0; s < SLOTS; ++s)
       // no position array: contiguous positions from the cached length
       p[s] = a.positions ? a.positions[pidx[s]] : L + (pidx[s] - pos_off);
+    sum_slices<SLOTS>(src, stride, a.kslices, t, HALF, x1, x2);
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
       if (p[s] < 0 || p[s] >= a.max_pos) {
         if (kind[s] != 0 && t == 0) atomicOr(a.err, 1);
         p[s] = p[s] < 0 ? 0 : a.max_pos - 1;
@@ -184,18 +218,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       }
     }
   }
-#pragma unroll
-  for (int k = 0; k < VROWS; ++k) {
-    v1[k] = vsrc[k][t];
-    v2[k] = vsrc[k][t + HALF];
-  }
-  for (int sl = 1; sl < a.kslices; ++sl) {
-#pragma unroll
-    for (int k = 0; k < VROWS; ++k) {
-      v1[k] += vsrc[k][sl * vstride[k] + t];
-      v2[k] += vsrc[k][sl * vstride[k] + t + HALF];
-    }
-  }
+  sum_slices<VROWS>(vsrc, vstride, a.kslices, t, HALF, v1, v2);
 #pragma unroll
   for (int k = 0; k < VROWS; ++k) {
     const int rb = wave * RPW + sub + k * 4 * RPW;
