@@ -730,11 +730,17 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   const int nt64 = ((Mq + 63) / 64) * (Nqkv / d) + (int)((Mc + 63) / 64) * (Nkv / d);
   const int nt128 = ((Mq + 127) / 128) * (Nqkv / d) + (int)((Mc + 127) / 128) * (Nkv / d);
   const int target = L->num_cus * 3 / 4;
-  // AUTO fuses at every size: with few rows the separate path's k split and
-  // its norm / RoPE / append launch cost more than the fused tiles save (one
-  // sequence: 0.0484 against 0.0470 ms; C1 0.0392 against 0.0362 ms).
-  const bool fused = L->mx || L->append_mode != DFLASH_APPEND_SEPARATE;
-  const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, nt128 >= target ? nt128 : nt64, 1}
+  const int fused_tiles = nt128 >= target ? nt128 : nt64;
+  // AUTO fuses unless the fused tiles (full k each) would fill at most half
+  // the CUs with a deep k: then the separate path's k split or smaller tiles
+  // cover the CUs, which saves more than its norm / RoPE / append launch costs.
+  // Measured at H = 4096, 32 / 8 heads, bf16: one sequence 0.0427 against
+  // 0.0505 ms fused, 4 sequences 0.0473 against 0.0543, 8 sequences (128 fused
+  // tiles) 0.0537 against 0.0578, 12 sequences (192 fused tiles) 0.0705
+  // against 0.0649; at H = 256 the launch dominates (C1 0.0306 against 0.0287).
+  const bool fused = L->mx || L->append_mode == DFLASH_APPEND_FUSED ||
+                     (L->append_mode == DFLASH_APPEND_AUTO && (fused_tiles > L->num_cus / 2 || H < 2048));
+  const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, fused_tiles, 1}
                               : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
   const int G = (int)attn_groups(L, n_tiles, (int64_t)B * nkv);
   // o_proj: too few rows for the CUs (a small batch) and a weight large enough

@@ -361,8 +361,11 @@ int dflash_layer_poll_error(dflash_layer* layer, void* stream);
 /* Where a step normalises and rotates q and k, packs the queries and appends
  * the new rows to the cache (NeMo page "draft_qwen3": q_norm/k_norm and
  * apply_rotary_pos_emb; "DFlash源码导读（二）" sections 1-4: cache update):
- *   DFLASH_APPEND_AUTO      (default) as FUSED: measured faster at every
- *                           size, also with few rows;
+ *   DFLASH_APPEND_AUTO      (default) as FUSED, except with few rows and a
+ *                           deep k (the fused launch, one tile per head of
+ *                           64 or 128 rows, would fill at most half the
+ *                           CUs, and hidden >= 2048): then as SEPARATE,
+ *                           whose projection splits k over the CUs;
  *   DFLASH_APPEND_FUSED     always in the projection's epilogue (never split k);
  *   DFLASH_APPEND_SEPARATE  always in the separate kernel.
  * The results agree up to the order of the fp32 sums of the projection. With
