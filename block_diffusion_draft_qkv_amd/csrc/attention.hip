@@ -12,9 +12,11 @@
 // tile of up to 64 rows; consumer wave w (0-3) of the work-group owns rows
 // 16w .. 16w+15. Every (sequence b, KV head j) pair owns the key tiles
 // [lo_b, hi_b) (lo_b > 0 only under a sliding window); all tiles of all pairs
-// are flattened head-major (j, then b, then tile) and cut into G equal ranges,
-// one per work-group, so every work-group streams the same number of key
-// tiles whatever the ragged lengths. With G a multiple of nkv every head's
+// are flattened head-major (j, then b, then tile) and cut into G ranges, one
+// per work-group, of about equal cost whatever the ragged lengths: a range's
+// tiles plus about a tile for every pair that starts inside it (the host's
+// attn_bounds; a pair start stalls the stream while the previous segment's
+// output is stored and the next queries are loaded). With G a multiple of nkv every head's
 // tiles split at the same places, and the host deals the ranges so that the
 // nkv work-groups covering the same tiles of all heads run on one XCD: they
 // read neighbouring pieces of the same cache blocks together (measured at C3:
@@ -109,8 +111,6 @@ __device__ inline void seq_tiles(const AttnArgs& a, int b, int kt, int& lo, int&
   cnt = (T + kt - 1) / kt - lo;
 }
 
-__device__ inline int64_t bound_of(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
-__device__ inline int64_t owner_of(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
 
 
 // Which key each lane's S^T accumulator row stands for (see the file comment).
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_splitkv_kernel(AttnArgs 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkv = a.nkv, R = a.R;
-  const int64_t N = a.total_tiles, G = a.G, w = a.range_of[blockIdx.x];
-  const int total = (int)(bound_of(w + 1, N, G) - bound_of(w, N, G));
+  const int w = a.range_of[blockIdx.x];
+  const int total = a.count[blockIdx.x];
   const uint32_t lds0 = lds_base(lds);
   const uint32_t qlds0 = lds0 + S * TILE;
 

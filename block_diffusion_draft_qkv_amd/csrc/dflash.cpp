@@ -150,7 +150,43 @@ int64_t attn_groups(const dflash_layer* L, int64_t n_tiles, int64_t n_pairs) {
 
 }  // namespace
 
-void dflash::attn_range_map(int G, int nkv, uint16_t* range_of) {
+void dflash::attn_bounds(int G, int nkv, int B, const int32_t* tile_cnt, int64_t* bnd) {
+  // One list of pairs is cut: a single head's B pairs when G is a multiple of
+  // nkv (every head then splits at the same places), else all nkv B pairs.
+  const bool by_head = nkv > 1 && G % nkv == 0;
+  const int ranges = by_head ? G / nkv : G, copies = by_head ? 1 : nkv;
+  int64_t per_head = 0;
+  for (int b = 0; b < B; ++b) per_head += tile_cnt[b];
+  const int64_t tiles = per_head * copies;
+  // Costs in quarter tiles: a pair's start, then its tiles.
+  const int64_t total = 4 * tiles + (int64_t)kPairStartQuarters * copies * B;
+  int64_t cut[kMaxGroups + 1];
+  cut[0] = 0;
+  int r = 1;
+  int64_t flat = 0, cost = 0;  // flat tile and cost before the current pair
+  for (int c = 0; c < copies && r < ranges; ++c)
+    for (int b = 0; b < B && r < ranges; ++b) {
+      const int64_t t = tile_cnt[b], first = cost + kPairStartQuarters;  // cost where its tile 0 starts
+      const int64_t end = first + 4 * t;
+      // range r starts at the first tile that begins at or after r total / ranges
+      for (; r < ranges && ((int64_t)r * total + ranges - 1) / ranges <= end - 4; ++r) {
+        const int64_t x = ((int64_t)r * total + ranges - 1) / ranges;
+        cut[r] = flat + (x <= first ? 0 : (x - first + 3) / 4);
+      }
+      flat += t;
+      cost = end;
+    }
+  for (; r < ranges; ++r) cut[r] = tiles;
+  cut[ranges] = tiles;
+  // at least one tile a range: push starts forward, then pull back from the end
+  for (int i = 1; i < ranges; ++i) cut[i] = std::max(cut[i], cut[i - 1] + 1);
+  for (int i = ranges - 1; i >= 1; --i) cut[i] = std::min(cut[i], cut[i + 1] - 1);
+  for (int j = 0; j < (by_head ? nkv : 1); ++j)
+    for (int i = 0; i < ranges; ++i) bnd[j * ranges + i] = j * per_head + cut[i];
+  bnd[G] = per_head * nkv;
+}
+
+void dflash::attn_range_map(int G, int nkv, uint8_t* range_of) {
   // The ranges in the order the XCDs take them: (i, j) when every head has
   // G / nkv ranges, else plain order.
   int order[kMaxGroups];
@@ -167,7 +203,7 @@ void dflash::attn_range_map(int G, int nkv, uint16_t* range_of) {
   constexpr int kXcds = 8;  // MI355X
   int next = 0;
   for (int x = 0; x < kXcds; ++x)
-    for (int bid = x; bid < G; bid += kXcds) range_of[bid] = (uint16_t)order[next++];
+    for (int bid = x; bid < G; bid += kXcds) range_of[bid] = (uint8_t)order[next++];
 }
 
 namespace {
@@ -743,6 +779,11 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   const TileChoice tq = fused ? TileChoice{nt128 >= target ? 128 : 64, d, fused_tiles, 1}
                               : choose_tiles(L, Mq, Nqkv, (int)Mc, Nkv, true);
   const int G = (int)attn_groups(L, n_tiles, (int64_t)B * nkv);
+  // the attention's ranges (their tile counts ride in 16 bits)
+  int64_t bnd[kMaxGroups + 1];
+  attn_bounds(G, nkv, B, tile_cnt, bnd);
+  for (int w = 0; w < G; ++w)
+    if (bnd[w + 1] - bnd[w] > 0xffff) return DFLASH_ERR_UNSUPPORTED;
   // o_proj: too few rows for the CUs (a small batch) and a weight large enough
   // that streaming it dominates (>= 4 MB; below that the extra launch costs
   // more): k split over fp32 slices in the q|k|v region of the scratch (its
@@ -867,6 +908,10 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   aa.map = cache_map(cache, nkv);
   aa.seq = seq;
   attn_range_map(aa.G, nkv, aa.range_of);
+  for (int bid = 0; bid < aa.G; ++bid) {
+    const int w = aa.range_of[bid];
+    aa.count[bid] = (uint16_t)(bnd[w + 1] - bnd[w]);
+  }
   // Each work-group's first (pair, tile): walk the pairs in flat order.
   {
     int64_t f = 0;
@@ -874,8 +919,8 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
     for (int j = 0; j < nkv && w < aa.G; ++j)
       for (int b = 0; b < B && w < aa.G; ++b) {
         const int64_t end = f + tile_cnt[b];
-        for (int64_t fw; w < aa.G && (fw = part_bound(w, n_tiles, aa.G)) < end; ++w)
-          aa.start[w] = (uint32_t)(b * nkv + j) | ((uint32_t)(tile_lo[b] + (fw - f)) << 16);
+        for (; w < aa.G && bnd[w] < end; ++w)
+          aa.start[w] = (uint32_t)(b * nkv + j) | ((uint32_t)(tile_lo[b] + (bnd[w] - f)) << 16);
         f = end;
       }
   }
@@ -894,14 +939,19 @@ static int attn_step_impl(dflash_layer* L, const void* hidden_states, const void
   ma.nq = nq; ma.nkv = nkv; ma.bs = bs; ma.R = R;
   ma.n_split = 0;
   {
+    // owner of flat tile x: the last range starting at or before it (pairs
+    // come in flat order, so the owner only moves forward)
+    int w0 = 0;
     int64_t f = 0;
     for (int j = 0; j < nkv; ++j)
       for (int b = 0; b < B; ++b) {
         const int64_t e = f + tile_cnt[b];
-        const int64_t w0 = part_owner(f, n_tiles, aa.G), w1 = part_owner(e - 1, n_tiles, aa.G);
+        while (w0 + 1 < aa.G && bnd[w0 + 1] <= f) ++w0;
+        int w1 = w0;
+        while (w1 + 1 < aa.G && bnd[w1 + 1] <= e - 1) ++w1;
         if (w0 != w1) {
           ma.pair[ma.n_split] = b * nkv + j;
-          ma.first_slot[ma.n_split] = (int16_t)(2 * w0 + (f != part_bound(w0, n_tiles, aa.G) ? 1 : 0));
+          ma.first_slot[ma.n_split] = (int16_t)(2 * w0 + (f != bnd[w0] ? 1 : 0));
           ma.nparts[ma.n_split] = (int16_t)(w1 - w0 + 1);
           ++ma.n_split;
         }

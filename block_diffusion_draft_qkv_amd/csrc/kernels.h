@@ -204,10 +204,11 @@ struct MxOut {
 
 // Flattened work: pairs (b, j) in head-major order (j outer, b inner), each
 // owning the 64-key tiles [lo_b, hi_b) of sequence b (lo_b > 0 only under a
-// sliding window). Range w takes flat tiles [floor(w N / G), floor((w+1) N / G)).
-// With G a multiple of nkv, ranges w = j (G / nkv) + i of every head j cover
-// the same sequences and tiles, so the nkv work-groups of one i read the nkv
-// neighbouring 16 KB pieces of the same cache blocks at about the same time.
+// sliding window). Range w = range_of[bid] takes the count[bid] flat tiles
+// from the one at start[w]; the host cuts the ranges (attn_bounds). With G a multiple of nkv,
+// ranges w = j (G / nkv) + i of every head j cover the same sequences and
+// tiles, so the nkv work-groups of one i read the nkv neighbouring 16 KB
+// pieces of the same cache blocks at about the same time.
 struct AttnArgs {
   const void* q;           // qpack
   const void* kc;
@@ -223,13 +224,26 @@ struct AttnArgs {
   // Start of range w: pair b * nkv + j in bits 0..15, absolute key tile in
   // bits 16..31 (filled by the host, which knows every length).
   uint32_t start[kMaxGroups];
+  // Key tiles of the range that work-group bid runs (at least one). Indexed
+  // by work-group, not by range: a 16-bit array read at w beside start[w]
+  // let the compiler build start[w]'s scalar load from an SGPR base of
+  // args + 2 w plus an offset of 2 w, and the scalar unit drops a base's low
+  // two bits, so odd ranges read their neighbour's start.
+  uint16_t count[kMaxGroups];
   // Range of work-group `bid` (a permutation of [0, G)); see attn_range_map.
-  uint16_t range_of[kMaxGroups];
+  uint8_t range_of[kMaxGroups];
 };
 // Deals the G ranges to work-groups. Work-groups go to the 8 XCDs round-robin
 // (bid % 8); each XCD gets a contiguous run of the ranges in (i, j) order, so
 // the nkv heads of one i share an XCD and its L2.
-void attn_range_map(int G, int nkv, uint16_t* range_of);
+void attn_range_map(int G, int nkv, uint8_t* range_of);
+// Cuts the flat tiles of B sequences (tile_cnt[b] key tiles each, for each of
+// nkv heads) into G ranges: bnd[w] is the first flat tile of range w, bnd[G]
+// the total. The ranges are about equal in tiles plus kPairStartQuarters / 4
+// tiles for each pair that starts inside them, every range holds at least one
+// tile, and with G a multiple of nkv every head is cut at the same places.
+constexpr int kPairStartQuarters = 4;  // a pair start's cost, in quarter tiles
+void attn_bounds(int G, int nkv, int B, const int32_t* tile_cnt, int64_t* bnd);
 hipError_t launch_attn(int dtype, int head_dim, const AttnArgs& args, hipStream_t stream);
 // Attention work-groups one CU holds at once (bounded by the kernel's LDS ring)
 // and the keys per attention tile.
@@ -255,8 +269,5 @@ struct MergeArgs {
 static_assert(sizeof(AttnArgs) <= 4096 && sizeof(MergeArgs) <= 4096, "kernel arguments exceed 4 KB");
 hipError_t launch_merge(int dtype, int head_dim, const MergeArgs& args, hipStream_t stream);
 
-// Host-side mirror of the kernels' partition (used to size and skip launches).
-inline int64_t part_bound(int64_t w, int64_t n, int64_t g) { return (w * n) / g; }
-inline int64_t part_owner(int64_t f, int64_t n, int64_t g) { return ((f + 1) * g + n - 1) / n - 1; }
 
 }  // namespace dflash

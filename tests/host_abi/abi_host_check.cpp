@@ -27,11 +27,15 @@
 
 extern "C" int hipMalloc(void** p, size_t bytes);
 extern "C" int hipFree(void* p);
+// plan_check.cpp: the attention plan in the captured argument blocks
+extern "C" int plan_check(const void* attn_bytes, size_t attn_size, const void* merge_bytes, size_t merge_size,
+                          int key_tile, char* msg, size_t msg_size);
+extern "C" size_t plan_arg_size(int which);
 
 namespace {
 
 int g_failures = 0, g_checks = 0;
-size_t g_launches_checked = 0;
+size_t g_launches_checked = 0, g_plans_checked = 0;
 
 #define CHECK(cond, ...)                                                  \
   do {                                                                    \
@@ -68,9 +72,23 @@ void* dev_zero(size_t bytes) {
   return p;
 }
 
-// Every launch since the last clear: a sane shape.
-void check_launches(const char* what) {
+// Every launch since the last clear: a sane shape; with key_tile > 0 also the
+// plan of every attention launch and of the merge launch that follows it.
+void check_launches(const char* what, int key_tile = 0) {
   const size_t n = stub_launch_count();
+  if (key_tile > 0) {
+    std::vector<unsigned char> attn(plan_arg_size(0)), merge(plan_arg_size(1));
+    for (size_t i = 0; i < n; ++i) {
+      if (!std::strstr(stub_launch(i).name, "attn_splitkv_kernel")) continue;
+      const size_t na = stub_launch_first_arg(i, attn.data(), attn.size());
+      const bool merged = i + 1 < n && std::strstr(stub_launch(i + 1).name, "attn_merge_kernel");
+      const size_t nm = merged ? stub_launch_first_arg(i + 1, merge.data(), merge.size()) : 0;
+      char msg[256] = "";
+      const int rc = plan_check(attn.data(), na, merged ? merge.data() : nullptr, nm, key_tile, msg, sizeof(msg));
+      CHECK(rc == 0, "%s: attention plan of launch %zu: %s", what, i, msg);
+      ++g_plans_checked;
+    }
+  }
   for (size_t i = 0; i < n; ++i) {
     const StubLaunch l = stub_launch(i);
     const uint64_t threads = (uint64_t)l.block[0] * l.block[1] * l.block[2];
@@ -257,7 +275,7 @@ int run_step(dflash_layer* L, const dflash_config& c, Cache& cache, const std::v
     CHECK(stub_launch_count() == 0, "%s: rejected step launched %zu kernels", what, stub_launch_count());
     CHECK(cache.len == before, "%s: rejected step changed a length", what);
   }
-  check_launches(what);
+  check_launches(what, c.dtype == DFLASH_F32 && c.head_dim == 128 ? 32 : 64);
   return st;
 }
 
@@ -864,6 +882,8 @@ void test_free_functions() {
 
 int main(int argc, char** argv) {
   const int random_cases = argc > 1 ? std::atoi(argv[1]) : 200;
+  stub_capture_first_arg("attn_splitkv_kernel", plan_arg_size(0));
+  stub_capture_first_arg("attn_merge_kernel", plan_arg_size(1));
   const size_t live0 = stub_live_allocations();
   test_status_strings();
   test_layer_create_rejections();
@@ -877,7 +897,7 @@ int main(int argc, char** argv) {
   test_contiguous_positions();
   test_free_functions();
   CHECK(stub_live_allocations() == live0, "%zu device allocations left at exit", stub_live_allocations() - live0);
-  std::printf("host ABI check: %d checks, %zu launches checked, %d failures\n", g_checks, g_launches_checked,
-              g_failures);
+  std::printf("host ABI check: %d checks, %zu launches checked, %zu attention plans checked, %d failures\n", g_checks,
+              g_launches_checked, g_plans_checked, g_failures);
   return g_failures ? 1 : 0;
 }

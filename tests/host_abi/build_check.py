@@ -28,7 +28,8 @@ def _sources():
     srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES]
     srcs += [os.path.join(b.CSRC, f) for f in sorted(os.listdir(b.CSRC)) if f.endswith(".h")]
     srcs += [os.path.join(b.INCLUDE, f) for f in sorted(os.listdir(b.INCLUDE))]
-    srcs += [os.path.join(HERE, f) for f in ("hip_stub.cpp", "hip_stub.h", "abi_host_check.cpp", "build_check.py")]
+    srcs += [os.path.join(HERE, f) for f in ("hip_stub.cpp", "hip_stub.h", "abi_host_check.cpp", "plan_check.cpp",
+                                             "build_check.py")]
     srcs.append(os.path.abspath(b.__file__))
     return b, srcs
 
@@ -56,6 +57,14 @@ def build_check(force: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
         objs.append(obj)
+    # the plan checker reads the library's kernel argument structs: HIP host code
+    obj = os.path.join(OUT, "plan_check.o")
+    cmd = [b.hipcc(), "-xhip", "--cuda-host-only", "-std=c++17", "-O1", "-g", *b.SANITIZE_FLAGS, "-I", b.CSRC,
+           "-I", b.INCLUDE, "-c", os.path.join(HERE, "plan_check.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling plan_check.cpp failed:\n{r.stdout}\n{r.stderr}")
+    objs.append(obj)
     cmd = [CLANG, *SAN, *objs, lib, "-o", EXE + ".tmp", "-lpthread", "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

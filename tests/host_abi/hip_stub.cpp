@@ -26,6 +26,8 @@ std::mutex g_mu;
 std::map<const void*, std::string> g_kernels;   // host stub -> kernel name
 std::map<void*, size_t> g_allocs;               // live device allocations
 std::vector<StubLaunch> g_launches;
+std::vector<std::vector<unsigned char>> g_first_args;  // per launch: the kept copy
+std::vector<std::pair<std::string, size_t>> g_capture;  // name part, bytes
 int g_fail_malloc_after = -1;                   // fail the n-th next hipMalloc
 struct CallConfig {
   dim3 grid, block;
@@ -63,15 +65,24 @@ hipError_t __hipPopCallConfiguration(dim3* grid, dim3* block, size_t* shmem, hip
   return hipSuccess;
 }
 
-hipError_t hipLaunchKernel(const void* f, dim3 grid, dim3 block, void**, size_t shmem, hipStream_t) {
+hipError_t hipLaunchKernel(const void* f, dim3 grid, dim3 block, void** args, size_t shmem, hipStream_t) {
   std::lock_guard<std::mutex> lk(g_mu);
   StubLaunch l;
   auto it = g_kernels.find(f);
-  std::snprintf(l.name, sizeof(l.name), "%s", it == g_kernels.end() ? "<unregistered>" : it->second.c_str());
+  const std::string name = it == g_kernels.end() ? "<unregistered>" : it->second;
+  std::snprintf(l.name, sizeof(l.name), "%s", name.c_str());
   l.grid[0] = grid.x; l.grid[1] = grid.y; l.grid[2] = grid.z;
   l.block[0] = block.x; l.block[1] = block.y; l.block[2] = block.z;
   l.shmem = shmem;
   g_launches.push_back(l);
+  std::vector<unsigned char> kept;
+  for (const auto& c : g_capture)
+    if (args && args[0] && name.find(c.first) != std::string::npos) {
+      const unsigned char* p = static_cast<const unsigned char*>(args[0]);
+      kept.assign(p, p + c.second);
+      break;
+    }
+  g_first_args.push_back(std::move(kept));
   return hipSuccess;
 }
 
@@ -163,10 +174,21 @@ StubLaunch stub_launch(size_t i) {
 void stub_clear_launches(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_launches.clear();
+  g_first_args.clear();
 }
 void stub_fail_malloc_after(int n) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_fail_malloc_after = n;
+}
+void stub_capture_first_arg(const char* name_part, size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_capture.size() < 4) g_capture.emplace_back(name_part, bytes);
+}
+size_t stub_launch_first_arg(size_t i, void* out, size_t max) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const std::vector<unsigned char>& k = g_first_args.at(i);
+  if (out && max >= k.size() && !k.empty()) std::memcpy(out, k.data(), k.size());
+  return k.size();
 }
 
 }  // extern "C"
