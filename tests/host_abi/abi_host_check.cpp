@@ -703,7 +703,7 @@ void test_decoder() {
       CHECK(dflash_decoder_step(D, x, th, offs.data(), static_cast<int32_t*>(pos), &cache.c, out, ws, need,
                                 nullptr) == DFLASH_OK,
             "decoder step B=%d", B);
-      check_launches("decoder step");
+      check_launches("decoder step", 64);  // bf16, head_dim 128: 64-key tiles
       CHECK(cache.len[0] == 9 + 16, "decoder step length");
       CHECK(dflash_decoder_step(D, x, th, offs.data(), static_cast<int32_t*>(pos), &cache.c, out, ws, need - 1,
                                 nullptr) == DFLASH_ERR_WORKSPACE && stub_launch_count() == 0,
@@ -847,7 +847,7 @@ void test_contiguous_positions() {
   CHECK(dflash_attn_step(L, io.hs, io.th, offs.data(), nullptr, &cache.c, io.out, io.ws, io.ws_bytes, nullptr) ==
             DFLASH_OK,
         "step without positions");
-  check_launches("contiguous positions");
+  check_launches("contiguous positions", 64);  // bf16, head_dim 128: 64-key tiles
   cache.len = {10, 200, 261};
   CHECK(dflash_attn_step(L, io.hs, io.th, offs.data(), nullptr, &cache.c, io.out, io.ws, io.ws_bytes, nullptr) ==
                 DFLASH_ERR_RANGE &&
