@@ -271,7 +271,8 @@ int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
  * 2 * B * block_size * n_q_heads * d elements of the dtype (queries and
  * attention output) plus at most 2 * 256 * 64 * (d * es + 8) bytes of partials
  * (es: the dtype's size; 8.6 MB for bf16 at d = 128), and fp32 slices when
- * o_proj splits k for few rows or the append mode is DFLASH_APPEND_SEPARATE.
+ * o_proj splits k for few rows or the step appends in the separate kernel
+ * (DFLASH_APPEND_SEPARATE, or DFLASH_APPEND_AUTO with few rows).
  * Arguments, effects and errors are those of dflash_attn_step, plus:
  * DFLASH_ERR_WORKSPACE (nothing launched, nothing changed) when the step needs
  * more than DFLASH_NOALLOC_SCRATCH_BYTES; DFLASH_ERR_HIP when the buffer's
