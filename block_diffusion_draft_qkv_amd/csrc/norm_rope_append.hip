@@ -49,16 +49,18 @@ constexpr int kNormSlots = 4;
 constexpr int kSliceLoads = 4;
 
 // x = sum over the k slices of rows src[r][t] and src[r][t + half] (slice sl
-// at sl * stride[r]): every load of the first kSliceLoads slices goes out
-// before any add, then the slices are added in order (the rounding of a
-// running sum); slices past kSliceLoads, which the host never plans, are
-// added one at a time afterwards.
-template <int N>
+// at sl * stride[r]): every load of the first SL slices goes out before any
+// add, then the slices are added in order (the rounding of a running sum);
+// slices past SL are added one at a time afterwards. The host launches
+// SL = kSliceLoads for split projections (few rows: the loads' latency
+// matters) and SL = 1 otherwise, whose registers leave room for twice the
+// waves (104 against 200 VGPRs at d = 128).
+template <int N, int SL>
 __device__ inline void sum_slices(const float* const (&src)[N], const int64_t (&stride)[N], int kslices, int t,
                                   int half, float (&x1)[N], float (&x2)[N]) {
-  float l1[kSliceLoads][N], l2[kSliceLoads][N];
+  float l1[SL][N], l2[SL][N];
 #pragma unroll
-  for (int sl = 0; sl < kSliceLoads; ++sl)
+  for (int sl = 0; sl < SL; ++sl)
     if (sl < kslices) {
 #pragma unroll
       for (int r = 0; r < N; ++r) {
@@ -72,7 +74,7 @@ __device__ inline void sum_slices(const float* const (&src)[N], const int64_t (&
     x2[r] = l2[0][r];
   }
 #pragma unroll
-  for (int sl = 1; sl < kSliceLoads; ++sl)
+  for (int sl = 1; sl < SL; ++sl)
     if (sl < kslices) {
 #pragma unroll
       for (int r = 0; r < N; ++r) {
@@ -80,7 +82,7 @@ __device__ inline void sum_slices(const float* const (&src)[N], const int64_t (&
         x2[r] += l2[sl][r];
       }
     }
-  for (int sl = kSliceLoads; sl < kslices; ++sl)
+  for (int sl = SL; sl < kslices; ++sl)
 #pragma unroll
     for (int r = 0; r < N; ++r) {
       x1[r] += src[r][sl * stride[r] + t];
@@ -88,7 +90,7 @@ __device__ inline void sum_slices(const float* const (&src)[N], const int64_t (&
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, int SL>
 __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, int yv) {
   constexpr int HALF = D / 2;            // lanes per row
   constexpr int RPW = 64 / HALF;         // rows per wave slot
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
     for (int s = 0; s < SLOTS; ++s)
       // no position array: contiguous positions from the cached length
       p[s] = a.positions ? a.positions[pidx[s]] : L + (pidx[s] - pos_off);
-    sum_slices<SLOTS>(src, stride, a.kslices, t, HALF, x1, x2);
+    sum_slices<SLOTS, SL>(src, stride, a.kslices, t, HALF, x1, x2);
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       if (p[s] < 0 || p[s] >= a.max_pos) {
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
       }
     }
   }
-  sum_slices<VROWS>(vsrc, vstride, a.kslices, t, HALF, v1, v2);
+  sum_slices<VROWS, SL>(vsrc, vstride, a.kslices, t, HALF, v1, v2);
 #pragma unroll
   for (int k = 0; k < VROWS; ++k) {
     const int rb = wave * RPW + sub + k * 4 * RPW;
@@ -239,6 +241,14 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs a, i
   }
 }
 
+template <typename T, int D>
+void launch_nr(const NormRopeArgs& args, int yv, dim3 g, dim3 blk, hipStream_t stream) {
+  if (args.kslices > 1)
+    hipLaunchKernelGGL((norm_rope_append_kernel<T, D, kSliceLoads>), g, blk, 0, stream, args, yv);
+  else
+    hipLaunchKernelGGL((norm_rope_append_kernel<T, D, 1>), g, blk, 0, stream, args, yv);
+}
+
 }  // namespace
 
 hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, int grid,
@@ -251,14 +261,14 @@ hipError_t launch_norm_rope(int dtype, int head_dim, const NormRopeArgs& args, i
   const dim3 g(grid, yv + yk, layers), blk(256);
   if (dtype == 1) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 128>), g, blk, 0, stream, args, yv);
+      launch_nr<__bf16, 128>(args, yv, g, blk, stream);
     else
-      hipLaunchKernelGGL((norm_rope_append_kernel<__bf16, 64>), g, blk, 0, stream, args, yv);
+      launch_nr<__bf16, 64>(args, yv, g, blk, stream);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), g, blk, 0, stream, args, yv);
+      launch_nr<float, 128>(args, yv, g, blk, stream);
     else
-      hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), g, blk, 0, stream, args, yv);
+      launch_nr<float, 64>(args, yv, g, blk, stream);
   }
   return hipGetLastError();
 }
