@@ -128,13 +128,14 @@ int64_t attn_groups(const dflash_layer* L, int64_t n_tiles, int64_t n_pairs) {
   int64_t cap = (int64_t)L->num_cus * attn_wgs_per_cu(L->cfg.dtype, L->cfg.head_dim);
   cap = std::min<int64_t>(cap, kMaxGroups);
   // A work-group with 64 KB of K and V in flight streams ~32 GB/s, so about
-  // 190 of them saturate HBM and more only add contention. Measured with
-  // bf16, head_dim 128 (attention + merge, 256 -> 192 work-groups): C3
-  // 99.9 -> 97.8 us, C5 (window 4096) 53.4 -> 51.0, 32 sequences of
-  // 256-4096 keys 58.1 -> 57.1, 8 of 16384 keys 92.2 -> 86.3. Below that the
-  // work-groups' own rate bounds it (C3's attention: 92.6 us with 192, 97.8
-  // with 176). Kernel shapes with less in flight keep every work-group.
-  if (attn_kv_in_flight(L->cfg.dtype, L->cfg.head_dim) >= 64 * 1024) cap = cap * 3 / 4;
+  // 200 of them saturate HBM and more only add contention. Measured with
+  // bf16, head_dim 128, attention alone, 192 / 208 / 224 work-groups (two
+  // alternations on one box): C3 92.3-93.2 / 90.1-90.3 / 90.6-90.8 us, C4
+  // 87.0-87.1 / 82.0-82.7 / 84.1-84.4, C5 (window 4096) 48.5 / 47.4-47.8 /
+  // 46.9-47.1; all 256 had been slower still (C3 attention + merge 99.9
+  // against 97.8 us at 192 with an earlier kernel). Kernel shapes with less
+  // in flight keep every work-group.
+  if (attn_kv_in_flight(L->cfg.dtype, L->cfg.head_dim) >= 64 * 1024) cap = cap * 13 / 16;
   // At least 4 tiles a range: a range of one or two tiles is mostly its own
   // ramp, and every range a pair is cut into is one more part for the merge
   // (one sequence at 2080 keys: step 0.0524 ms with 1 tile a range, 0.0476 with

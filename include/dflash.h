@@ -248,7 +248,7 @@ int dflash_workspace_offset(const dflash_layer* layer, int32_t batch, int64_t to
  * negative len, capacity not a multiple of 64 or above 2^21), DFLASH_ERR_CAPACITY (some
  * T_b > capacity), DFLASH_ERR_WORKSPACE, DFLASH_ERR_UNSUPPORTED (one attention
  * work-group would get more than 65535 key tiles: more keys per step than an
- * MI355X can hold at 192 work-groups), DFLASH_ERR_HIP (launch failure;
+ * MI355X can hold at 208 work-groups), DFLASH_ERR_HIP (launch failure;
  * lengths are then left unchanged). */
 int dflash_attn_step(dflash_layer* layer, const void* hidden_states,
                      const void* target_hidden, const int32_t* ctx_offsets,
