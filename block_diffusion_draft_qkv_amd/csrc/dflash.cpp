@@ -132,10 +132,14 @@ int64_t attn_groups(const dflash_layer* L, int64_t n_tiles, int64_t n_pairs) {
   // bf16, head_dim 128, attention alone, 192 / 208 / 224 work-groups (two
   // alternations on one box): C3 92.3-93.2 / 90.1-90.3 / 90.6-90.8 us, C4
   // 87.0-87.1 / 82.0-82.7 / 84.1-84.4, C5 (window 4096) 48.5 / 47.4-47.8 /
-  // 46.9-47.1; all 256 had been slower still (C3 attention + merge 99.9
-  // against 97.8 us at 192 with an earlier kernel). Kernel shapes with less
-  // in flight keep every work-group.
-  if (attn_kv_in_flight(L->cfg.dtype, L->cfg.head_dim) >= 64 * 1024) cap = cap * 13 / 16;
+  // 46.9-47.1; on another box 208 / 224: C3 90.0-90.3 / 90.6-90.7, C4
+  // 81.0-81.6 / 83.7-84.8, C5 47.9-48.0 / 46.8. All 256 had been slower still
+  // (C3 attention + merge 99.9 against 97.8 us at 192 with an earlier
+  // kernel). So 13/16 of the CUs, and 7/8 when the ranges would be short
+  // (under 48 tiles at 13/16, C5's ~40), where the ramp weighs more. Kernel
+  // shapes with less in flight keep every work-group.
+  if (attn_kv_in_flight(L->cfg.dtype, L->cfg.head_dim) >= 64 * 1024)
+    cap = n_tiles < 48 * (cap * 13 / 16) ? cap * 7 / 8 : cap * 13 / 16;
   // At least 4 tiles a range: a range of one or two tiles is mostly its own
   // ramp, and every range a pair is cut into is one more part for the merge
   // (one sequence at 2080 keys: step 0.0524 ms with 1 tile a range, 0.0476 with
