@@ -31,6 +31,9 @@ extern "C" int hipFree(void* p);
 extern "C" int plan_check(const void* attn_bytes, size_t attn_size, const void* merge_bytes, size_t merge_size,
                           int key_tile, char* msg, size_t msg_size);
 extern "C" size_t plan_arg_size(int which);
+namespace dflash {
+void attn_bounds(int G, int nkv, int B, const int32_t* tile_cnt, int64_t* bnd);
+}
 
 namespace {
 
@@ -880,12 +883,41 @@ void test_free_functions() {
 
 }  // namespace
 
+// The attention's range cut on its own, over shapes the steps rarely reach:
+// as many ranges as tiles (every range one tile), one long pair among many
+// short ones, heads that cannot share the cut (G not a multiple of nkv).
+void test_attn_bounds() {
+  Rng rng(11);
+  for (int it = 0; it < 2000; ++it) {
+    const int B = rng.range(1, 64), nkv = rng.range(1, 8);
+    std::vector<int32_t> tc(B);
+    for (int b = 0; b < B; ++b) tc[b] = rng.range(0, 9) == 0 ? rng.range(50, 400) : rng.range(1, 6);
+    int64_t per_head = 0;
+    for (int b = 0; b < B; ++b) per_head += tc[b];
+    const int64_t n = per_head * nkv;
+    // 1 <= G <= the tiles, as attn_groups guarantees
+    const int G = (int)std::min<int64_t>(std::min<int64_t>(256, n), rng.range(0, 3) == 0 ? n : rng.range(1, 256));
+    std::vector<int64_t> bnd(G + 1, -1);
+    dflash::attn_bounds(G, nkv, B, tc.data(), bnd.data());
+    bool ok = bnd[0] == 0 && bnd[G] == n;
+    for (int w = 0; w < G && ok; ++w) ok = bnd[w + 1] > bnd[w];
+    if (ok && nkv > 1 && G % nkv == 0) {
+      const int per = G / nkv;
+      for (int j = 1; j < nkv && ok; ++j)
+        for (int i = 0; i < per && ok; ++i) ok = bnd[j * per + i] == j * per_head + bnd[i];
+    }
+    CHECK(ok, "attn_bounds G=%d nkv=%d B=%d tiles=%lld: not %d non-empty, ordered, per-head ranges", G, nkv, B,
+          (long long)n, G);
+  }
+}
+
 int main(int argc, char** argv) {
   const int random_cases = argc > 1 ? std::atoi(argv[1]) : 200;
   stub_capture_first_arg("attn_splitkv_kernel", plan_arg_size(0));
   stub_capture_first_arg("attn_merge_kernel", plan_arg_size(1));
   const size_t live0 = stub_live_allocations();
   test_status_strings();
+  test_attn_bounds();
   test_layer_create_rejections();
   test_create_allocation_failures();
   test_layer_steps_fixed();
